@@ -1,0 +1,113 @@
+"""Seeded synthetic MoE-layer workloads.
+
+The five full-size layers follow the model shapes the pages quote (128
+experts / top-8 like Qwen3-30B-A3B, 256 / top-8 like DeepSeek-R1, 896 /
+top-16 like Kimi K3 at decode scale, and a latent-dispatch layer) plus a
+tiny fp32 layer.  The small ``PARITY_CONFIGS`` are cut-down layers the CPU
+oracle finishes in seconds while still spanning several GEMM tiles, ragged
+tails, empty experts and the degenerate routings (k = 1, k = E, E = 1,
+T = 1, every token on the same experts).
+
+Nothing here computes any step of the layer: a config is a bag of sizes,
+seeds and value distributions.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from typing import Optional
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int                 # tokens in the step
+    H: int                 # model hidden width
+    E: int                 # routed experts
+    k: int                 # experts selected per token
+    I: int                 # expert FFN intermediate width
+    L: int = 0             # latent dispatch width (0 = dispatch at H)
+    dtype: str = "bf16"    # "bf16" (fp32 accumulate, fp32 router) or "f32"
+    seed: int = 0
+    x_std: float = 1.0     # activations ~ N(0, x_std^2)
+    w_std: float = 0.02    # expert / projection weights ~ N(0, w_std^2)
+    gate: str = "computed"  # "computed": logits = X.Wg (+bias); "drawn": logits ~ N(0,1) given
+    gate_std: Optional[float] = 0.02   # Wg ~ N(0, gate_std^2); None means 1/sqrt(H)
+    zipf_s: Optional[float] = None     # per-expert bias -alpha*s*ln(rank) when set
+    zipf_alpha: float = 0.0
+    const_logits: bool = False         # every router logit equal (all-tie routing)
+
+    @property
+    def D(self) -> int:
+        """Width of the dispatched rows (latent width when L > 0)."""
+        return self.L if self.L else self.H
+
+    @property
+    def R(self) -> int:
+        """Routed rows: every token yields exactly k assignments."""
+        return self.T * self.k
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def has_bias(self) -> bool:
+        return self.zipf_s is not None
+
+    def with_(self, **kw) -> "MoEConfig":
+        return replace(self, **kw)
+
+
+# Scale of the log-Zipf expert bias.  The literal prior -s*ln(rank) makes the
+# p95 max/mean expert-load ratio about 24 on the DeepSeek-R1-shaped layer; the
+# workload asks for about 4.  The value below was chosen by
+# workloads/calibrate_zipf.py (which runs the oracle's router on the seeded
+# layer) and is frozen here; it only shapes the workload.
+ZIPF_ALPHA = 0.25
+
+TINY_F32 = MoEConfig(
+    name="tiny_f32", T=64, H=128, E=8, k=2, I=256, dtype="f32", seed=101,
+    x_std=1.0, w_std=0.05, gate="drawn", gate_std=None)
+
+QWEN3_30B_A3B_SHAPED = MoEConfig(
+    name="qwen3_30b_a3b_shaped", T=4096, H=2048, E=128, k=8, I=768, seed=202,
+    gate="computed", gate_std=0.02)
+
+DEEPSEEK_R1_SHAPED = MoEConfig(
+    name="deepseek_r1_shaped", T=8192, H=7168, E=256, k=8, I=2048, seed=303,
+    gate="computed", gate_std=0.02, zipf_s=1.1, zipf_alpha=ZIPF_ALPHA)
+
+K3_SHAPED_DECODE = MoEConfig(
+    name="k3_shaped_decode", T=128, H=4096, E=896, k=16, I=1024, seed=404,
+    gate="drawn", gate_std=None, zipf_s=1.2, zipf_alpha=ZIPF_ALPHA)
+
+LATENT_MOE = MoEConfig(
+    name="latent_moe", T=4096, H=7168, L=2048, E=256, k=8, I=4096, seed=505,
+    gate="computed", gate_std=None)
+
+FULL_CONFIGS = {c.name: c for c in (TINY_F32, QWEN3_30B_A3B_SHAPED, DEEPSEEK_R1_SHAPED,
+                                    K3_SHAPED_DECODE, LATENT_MOE)}
+
+# Cut-down layers for element-by-element parity (oracle runs in seconds).
+PARITY_CONFIGS = {c.name: c for c in (
+    TINY_F32,
+    # several m-tiles for hot experts, ragged tails, empty experts
+    MoEConfig(name="small_bf16_zipf", T=300, H=256, E=16, k=4, I=192, seed=11,
+              gate="computed", gate_std=0.0625, zipf_s=1.1, zipf_alpha=1.0),
+    MoEConfig(name="small_bf16_uniform", T=517, H=384, E=32, k=8, I=256, seed=12,
+              gate="computed", gate_std=0.05),
+    # decode-like: most experts get 0-3 rows
+    MoEConfig(name="small_bf16_decode", T=24, H=512, E=96, k=6, I=128, seed=13,
+              gate="drawn", gate_std=None, zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
+    MoEConfig(name="small_latent", T=200, H=320, L=128, E=16, k=4, I=256, seed=14,
+              gate="computed", gate_std=None),
+    # degenerate routings
+    MoEConfig(name="one_expert", T=130, H=128, E=1, k=1, I=128, seed=15, gate="drawn"),
+    MoEConfig(name="k_equals_e", T=70, H=128, E=8, k=8, I=64, seed=16, gate="drawn"),
+    MoEConfig(name="single_token", T=1, H=192, E=12, k=3, I=64, seed=17, gate="drawn"),
+    MoEConfig(name="all_ties", T=150, H=128, E=16, k=2, I=128, seed=18, gate="drawn",
+              const_logits=True),
+    MoEConfig(name="many_empty", T=5, H=128, E=64, k=2, I=64, seed=19, gate="drawn"),
+    MoEConfig(name="small_f32_computed", T=97, H=96, E=6, k=3, I=80, dtype="f32",
+              seed=20, w_std=0.05, gate="computed", gate_std=0.1),
+)}
