@@ -1,0 +1,258 @@
+/*
+ * moe.h -- C ABI of libmoe: one GPU's share of a routed-expert MoE layer forward
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the pipeline of the WideEP explainer page (Kimi K3), section
+ * "The router writes a network schedule": the source computes gating scores and
+ * top-k expert ids; a dispatcher counts destinations, allocates slots, permutes
+ * token activations into destination-contiguous rows and attaches routing
+ * metadata; the receiver groups rows by expert and runs the expert matrix
+ * multiplies; the combine reverses the route and the source unpermutes and
+ * applies the routing weights.  On one GPU every assignment is local, so the
+ * "transfer" is the permutation itself (same page, table of communication
+ * paths, row "Same GPU": no fabric hop, still permute and HBM traffic).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller, dense and
+ *   row-major, 16-byte aligned.  The library allocates nothing and keeps no
+ *   state between calls; all scratch comes from the caller's workspace `ws`
+ *   of `ws_bytes` bytes (size it with moe_workspace_bytes; NULL allowed when
+ *   that size is 0).
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  They never read device memory on the host and never
+ *   synchronise: static grids, GPU-resident counts and offsets (same page,
+ *   table row "CPU control path": static shapes, GPU-resident metadata).
+ *   Calls are re-entrant across distinct workspaces; two calls that share a
+ *   workspace or outputs must be ordered by the caller.
+ * - Element types: activations, expert weights, projections and the permuted
+ *   rows are MOE_BF16 or MOE_F32 as `moe_shape.dtype` says.  Router weights,
+ *   bias, logits and routing weights are always fp32; ids, counts, offsets
+ *   and metadata are int32.  bf16 math accumulates in fp32.
+ * - Weight orientation (output-major, like a linear layer's weight, so every
+ *   contraction reads both operands along contiguous K):
+ *     gate_w [E x H]   logits = X gate_w^T
+ *     w1, w3 [E x I x D], w2 [E x D x I]
+ *                      expert e: Y = (SiLU(X w1[e]^T) * (X w3[e]^T)) w2[e]^T
+ *     wd [L x H], wu [H x L]   Z = X wd^T,  out = out_L wu^T
+ *   D is the dispatched width: L for latent layers (L > 0), else H.
+ * - Errors: every call validates its arguments on the host before touching
+ *   the GPU and returns MOE_ERR_INVALID_ARG (bad shape, NULL or misaligned
+ *   pointer), MOE_ERR_UNSUPPORTED (shape outside the kernels' limits, listed
+ *   per call), MOE_ERR_WORKSPACE (ws_bytes too small) or MOE_ERR_HIP (a kernel
+ *   launch failed; no device status is read).  Nothing throws or aborts.
+ * - Preconditions not checked (they would need a device read): logits are
+ *   finite or -inf; caller-supplied topk_ids are in [0, E) and distinct per
+ *   token; offsets are the exclusive prefix sum of the per-expert counts.
+ *
+ * Limits: 1 <= k <= E <= 1024; T*k < 2^31; bf16 layers need D % 64 == 0,
+ * I % 64 == 0 and (for latent layers) H % 64 == 0; fp32 layers need D % 4 == 0
+ * and H % 4 == 0.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which call a workspace size is asked for. */
+typedef enum moe_call {
+  MOE_CALL_ROUTE = 0,
+  MOE_CALL_DISPATCH = 1,
+  MOE_CALL_FFN = 2,
+  MOE_CALL_COMBINE = 3,
+  MOE_CALL_LAYER = 4
+} moe_call;
+
+/* moe_combine flags. */
+#define MOE_COMBINE_FUSED 0   /* one kernel: gather k rows, weight, sum (production) */
+#define MOE_COMBINE_UNFUSED 1 /* two kernels: unpermute to token order, then weighted reduce */
+
+/* Stage events recorded by moe_layer_forward when `stage_events` is non-NULL. */
+#define MOE_NUM_STAGE_EVENTS 9
+/* [0] start  [1] after latent down-projection  [2] after gate  [3] after top-k+count+scan
+ * [4] after permute  [5] after expert gate/up GEMM  [6] after expert down GEMM
+ * [7] after combine  [8] after latent up-projection.  Stages that do not run leave
+ * two consecutive events back to back. */
+
+typedef struct moe_shape {
+  int64_t T;      /* tokens */
+  int64_t H;      /* model width */
+  int64_t E;      /* routed experts */
+  int64_t k;      /* experts per token */
+  int64_t I;      /* expert intermediate width */
+  int64_t L;      /* latent dispatch width, 0 = none */
+  int32_t dtype;  /* moe_dtype */
+  int32_t reserved;  /* must be 0 */
+} moe_shape;
+
+/* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
+size_t moe_workspace_bytes(const moe_shape* s, int call);
+
+/* Static string for a status code. */
+const char* moe_status_string(int status);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+/*
+ * Gate scores + top-k selection + per-expert counts and offsets (steps a1-a3).
+ *
+ * Passage: WideEP explainer, "The router writes a network schedule" (the source
+ * computes gating scores and top-k expert ids; the dispatcher counts
+ * destinations and allocates slots) and "Sparse compute. Dense availability."
+ * (k of E experts per token).
+ *
+ * x        [T x H] activations (dtype); read only when gate_w != NULL.
+ * gate_w   [E x H] fp32 router weight, or NULL when `logits` is given.
+ * gate_bias[E] fp32 per-expert bias, nullable.  With gate_w the bias is added
+ *          into the written logits; without it the score is the fp32 sum
+ *          logits + bias, formed on the fly (logits are not modified).
+ * logits   [T x E] fp32: output when gate_w != NULL, input otherwise.
+ * topk_ids [T x k] int32 out: per token the k experts with the largest scores,
+ *          listed by descending score; equal scores go to the lower expert
+ *          index; -0.0 ranks equal to +0.0.
+ * topk_w   [T x k] fp32 out: softmax over all E scores gathered at topk_ids and
+ *          renormalised over the k (equal to exp(s_j - s_max) / sum_i exp(s_i - s_max)
+ *          over the selected i).  A token whose scores are all -inf gets NaN.
+ * counts   [E] int32 out: assignments per expert (sum = T*k).
+ * offsets  [E+1] int32 out: exclusive prefix sum of counts, offsets[E] = T*k.
+ */
+moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
+                          float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                          int32_t* offsets, const moe_shape* s, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * Permutation into expert-contiguous rows + routing metadata (step a4).
+ *
+ * Passage: WideEP explainer, "The router writes a network schedule" (permute
+ * activations into destination-contiguous buffers and attach routing
+ * metadata; the receiver groups tokens by expert).  The buffer holds exactly
+ * T*k*D*elem bytes, the dispatch payload of "Top-k multiplies traffic.
+ * Locality subtracts it." (no padding, every assignment local).
+ *
+ * x         [T x D] rows to dispatch (dtype): the activations, or Z for latent layers.
+ * topk_ids  [T x k] int32, offsets [E+1] int32 (as written by moe_route_topk).
+ * x_perm    [T*k x D] out: expert e's rows occupy [offsets[e], offsets[e+1]),
+ *           holding, in ascending token order, a bitwise copy of every token
+ *           that picked e.
+ * row_token [T*k] int32 out: source token of each row.
+ * token_row [T x k] int32 out: row holding token t's j-th assignment.
+ */
+moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
+                                void* x_perm, int32_t* row_token, int32_t* token_row,
+                                const moe_shape* s, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped SwiGLU expert FFN over ragged row counts (step a5).
+ *
+ * Passage: WideEP explainer, "The router writes a network schedule" (expert
+ * matrix multiplies on the grouped rows) and "Sparse compute. Dense
+ * availability." (fewer, fatter grouped GEMMs); "Three Parameter Counts...",
+ * table of "Which optimizations need a task-level gate" (a grouped GEMM runs
+ * several expert matrices in one launch with differing row counts and creates
+ * no work for an expert that received no token).
+ *
+ * x_perm [T*k x D] (dtype), offsets [E+1] int32.
+ * w1, w3 [E x I x D], w2 [E x D x I] (dtype).  Weights of experts with no rows
+ *        are never read.
+ * y_perm [T*k x D] out (dtype): row r of expert e holds
+ *        (SiLU(x w1[e]^T) * (x w3[e]^T)) w2[e]^T, with the intermediate rounded
+ *        to dtype; unweighted (weights apply in the combine).
+ */
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
+                           const void* w3, const void* w2, void* y_perm, const moe_shape* s,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine: unpermute and apply routing weights (step a6).
+ *
+ * Passage: WideEP explainer, "The router writes a network schedule" (the
+ * combine reverses the route; the source unpermutes and applies routing
+ * weights) and "Top-k multiplies traffic..." (combine moves about the same
+ * volume as dispatch).
+ *
+ * y_perm    [T*k x D] (dtype), token_row [T x k] int32, topk_w [T x k] fp32.
+ * out       [T x D] out, element type out_dtype (MOE_F32 or MOE_BF16):
+ *           out[t] = sum_{j=0..k-1} topk_w[t,j] * y_perm[token_row[t,j]], fp32
+ *           accumulation in ascending j, one rounding to out_dtype.  The bf16
+ *           result is the round-to-nearest-even of the fp32 result.
+ * flags     MOE_COMBINE_FUSED (one kernel) or MOE_COMBINE_UNFUSED (unpermute to
+ *           token order in the workspace, then the weighted reduce: the separate
+ *           "unpermutation" and "combine" timers of "Three Parameter Counts...",
+ *           "What the utilization dashboard smooths away").  Same result bits.
+ */
+moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
+                       void* out, int out_dtype, int flags, const moe_shape* s, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Weights of one layer for moe_layer_forward (device pointers, layouts as above). */
+typedef struct moe_layer_weights {
+  const float* gate_w;     /* [E x H] fp32, or NULL: router logits are given */
+  const float* gate_bias;  /* [E] fp32, nullable */
+  const void* w1;          /* [E x I x D] */
+  const void* w3;          /* [E x I x D] */
+  const void* w2;          /* [E x D x I] */
+  const void* wd;          /* [L x H], latent layers only */
+  const void* wu;          /* [H x L], latent layers only */
+} moe_layer_weights;
+
+/* Optional caller buffers that expose the intermediate results (each nullable;
+ * NULL fields live in the workspace). */
+typedef struct moe_layer_aux {
+  int32_t* topk_ids;   /* [T x k] */
+  float* topk_w;       /* [T x k] */
+  int32_t* counts;     /* [E] */
+  int32_t* offsets;    /* [E+1] */
+  int32_t* row_token;  /* [T*k] */
+  int32_t* token_row;  /* [T x k] */
+  void* x_perm;        /* [T*k x D] dtype */
+  void* y_perm;        /* [T*k x D] dtype */
+  void* z;             /* [T x L] dtype, latent layers */
+  void* out_latent;    /* [T x L] dtype, latent layers: combine output before up-projection */
+} moe_layer_aux;
+
+/*
+ * The whole layer forward in one call (steps a1-a7), the execution-only fusion
+ * of "Three Parameter Counts...", table of "Which optimizations need a
+ * task-level gate": routing ids, counts, offsets and the permutation are
+ * bit-identical to the separate calls on the same logits.
+ *
+ * Latent layers (s->L > 0) follow "Latent MoE" (Definition; Current Synthesis):
+ * the router scores the full-width X, the rows dispatched are Z = X wd^T, and the
+ * combined latent output (rounded to dtype) is projected back: out = out_L wu^T.
+ *
+ * x       [T x H] (dtype).
+ * logits  [T x E] fp32: input when w->gate_w == NULL, else output (nullable: then
+ *         kept in the workspace).
+ * out     [T x H] out, element type out_dtype (MOE_F32 or MOE_BF16).
+ * aux     nullable, see moe_layer_aux.
+ * stage_events  NULL or an array of MOE_NUM_STAGE_EVENTS hipEvent_t created by
+ *         the caller; each is recorded on `stream` at its stage boundary.
+ */
+moe_status moe_layer_forward(const moe_layer_weights* w, const void* x, float* logits, void* out,
+                             int out_dtype, const moe_shape* s, moe_layer_aux* aux,
+                             void** stage_events, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,182 @@
+// Combine: unpermute the expert outputs and apply the routing weights (step a6).
+//
+// The combine reverses the route and the source unpermutes and applies the
+// routing weights (WideEP explainer (Kimi K3), "The router writes a network
+// schedule"); it moves about the same volume as the dispatch ("Top-k
+// multiplies traffic. Locality subtracts it.").
+//
+// out[t] = sum_j w[t,j] * Y[token_row[t,j]] with one fp32 fma per term in
+// ascending j and one rounding to the output type.  The fused kernel gathers
+// the k rows directly; the unfused pair first unpermutes into token order and
+// then reduces, with the same fma sequence, so both give the same bits.
+#include "moe_kernels.h"
+
+namespace moe {
+
+template <typename IT>
+struct Vec16;  // 16 bytes of input elements
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int n = 8;
+  __device__ static void unpack(uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int n = 4;
+  __device__ static void unpack(uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void store_out(void* out, size_t elem0, const float* acc, bool f32) {
+  if (f32) {
+    float* o = static_cast<float*>(out) + elem0;
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<float4*>(o + i) = make_float4(acc[i], acc[i + 1], acc[i + 2], acc[i + 3]);
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(out) + elem0;
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+    if constexpr (N == 8) {
+      *reinterpret_cast<uint4*>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      *reinterpret_cast<uint2*>(o) = make_uint2(w[0], w[1]);
+    }
+  }
+}
+
+constexpr int kCombTokPerWg = 4;  // one wave per token
+
+// Fused: one wave per token, each lane owns 16-byte column chunks of the row.
+template <typename IT>
+__global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, int row16,
+                                                 const int32_t* __restrict__ token_row,
+                                                 const float* __restrict__ topk_w, int T, int k,
+                                                 void* __restrict__ out, int out_f32) {
+  constexpr int NV = Vec16<IT>::n;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kCombTokPerWg + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int my_row = 0;
+  float my_w = 0.f;
+  if (lane < k) {
+    my_row = token_row[(size_t)t * k + lane];
+    my_w = topk_w[(size_t)t * k + lane];
+  }
+  for (int c = lane; c < row16; c += kWave) {
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {
+      uint4 v[4];
+      float wj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = __shfl(my_row, j + u, kWave);
+        wj[u] = __shfl(my_w, j + u, kWave);
+        v[u] = y[(size_t)r * row16 + c];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float f[NV];
+        Vec16<IT>::unpack(v[u], f);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj[u], f[i], acc[i]);
+      }
+    }
+    for (; j < k; ++j) {
+      const int r = __shfl(my_row, j, kWave);
+      const float wj = __shfl(my_w, j, kWave);
+      float f[NV];
+      Vec16<IT>::unpack(y[(size_t)r * row16 + c], f);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+    }
+    store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
+  }
+}
+
+// Unfused step 1: y_tok[t*k + j] = Y[token_row[t, j]] (one wave per assignment).
+__global__ __launch_bounds__(256) void k_unpermute(const uint4* __restrict__ y, int row16,
+                                                   const int32_t* __restrict__ token_row, int R,
+                                                   uint4* __restrict__ y_tok) {
+  const int lane = threadIdx.x & 63;
+  const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (a >= R) return;
+  const int r = token_row[a];
+  const uint4* src = y + (size_t)r * row16;
+  uint4* dst = y_tok + (size_t)a * row16;
+  for (int c = lane; c < row16; c += kWave) dst[c] = src[c];
+}
+
+// Unfused step 2: out[t] = sum_j w[t, j] * y_tok[t*k + j], same fma order as k_combine.
+template <typename IT>
+__global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict__ y_tok, int row16,
+                                                         const float* __restrict__ topk_w, int T,
+                                                         int k, void* __restrict__ out,
+                                                         int out_f32) {
+  constexpr int NV = Vec16<IT>::n;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kCombTokPerWg + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int c = lane; c < row16; c += kWave) {
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float wj = topk_w[(size_t)t * k + j];
+      float f[NV];
+      Vec16<IT>::unpack(y_tok[((size_t)t * k + j) * row16 + c], f);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+    }
+    store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
+  }
+}
+
+hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
+                          const float* w, int T, int k, void* out, bool out_f32, hipStream_t st) {
+  const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
+  if (in_bf16)
+    hipLaunchKernelGGL(k_combine<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y), row16,
+                       token_row, w, T, k, out, (int)out_f32);
+  else
+    hipLaunchKernelGGL(k_combine<float>, g, b, 0, st, static_cast<const uint4*>(y), row16,
+                       token_row, w, T, k, out, (int)out_f32);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_unpermute, dim3(ceil_div(R, 4)), dim3(256), 0, st,
+                     static_cast<const uint4*>(y), row16, token_row, R, static_cast<uint4*>(y_tok));
+  return hipGetLastError();
+}
+
+hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
+                                  int T, int k, void* out, bool out_f32, hipStream_t st) {
+  const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
+  if (in_bf16)
+    hipLaunchKernelGGL(k_weighted_reduce<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y_tok),
+                       row16, w, T, k, out, (int)out_f32);
+  else
+    hipLaunchKernelGGL(k_weighted_reduce<float>, g, b, 0, st, static_cast<const uint4*>(y_tok),
+                       row16, w, T, k, out, (int)out_f32);
+  return hipGetLastError();
+}
+
+}  // namespace moe

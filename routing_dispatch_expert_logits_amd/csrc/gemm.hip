@@ -1,0 +1,447 @@
+// Grouped expert GEMMs (step a5) and the dense projections built on them
+// (gate scores, step a1; latent down/up projections, step a7).
+//
+// Expert e owns rows [offsets[e], offsets[e+1]) of the permuted buffer; one
+// launch covers every expert with its own row count, and an expert with no
+// rows contributes no tile ("Three Parameter Counts...", table of "Which
+// optimizations need a task-level gate").  The tile table is on the device:
+// mtile_start[e] = sum_{e' < e} ceil(rows_e' / BM), so a workgroup finds its
+// (expert, m-tile, n-tile) with a binary search and the grid is sized from
+// host-known bounds only.
+//
+// Tile order: expert-major, then n-tile, then m-tile, so the tiles that share an
+// expert's weights and rows run together; logical tiles are dealt to the 8 XCDs
+// in contiguous chunks (workgroup i runs on XCD i % 8), keeping each expert's
+// working set in one XCD's L2.
+//
+// bf16 path: v_mfma_f32_16x16x32_bf16, fp32 accumulate.  Lane l of a 16x16x32
+// MFMA supplies A[l % 16][8*(l/16) .. +8] and B[8*(l/16) .. +8][l % 16] and
+// receives D[4*(l/16) .. +4][l % 16].  Because every weight is stored
+// output-major (K contiguous), both operands are 16-byte K-runs.
+#include "moe_kernels.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ tile decode
+
+struct TileCoord {
+  int e, row0, rows, n0;
+};
+
+// Returns false when this workgroup has no tile.
+template <int BM, int BN>
+__device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
+                                            const int32_t* __restrict__ mtile_start, int E, int M,
+                                            int N, TileCoord& tc) {
+  const int NT = ceil_div(N, BN);
+  const int total_mt = offsets ? mtile_start[E] : ceil_div(M, BM);
+  const int total = total_mt * NT;
+  const int per_xcd = ceil_div(total, 8);
+  const int slot = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+  if (slot >= per_xcd) return false;
+  const int L = xcd * per_xcd + slot;
+  if (L >= total) return false;
+  if (offsets) {
+    const int e = upper_index(mtile_start, E, L / NT);
+    const int mt0 = mtile_start[e];
+    const int mte = mtile_start[e + 1] - mt0;
+    const int local = L - mt0 * NT;
+    const int n_idx = local / mte, m_idx = local - n_idx * mte;
+    tc.e = e;
+    tc.row0 = offsets[e] + m_idx * BM;
+    tc.rows = min(BM, offsets[e + 1] - tc.row0);
+    tc.n0 = n_idx * BN;
+  } else {
+    const int n_idx = L / total_mt, m_idx = L - n_idx * total_mt;
+    tc.e = 0;
+    tc.row0 = m_idx * BM;
+    tc.rows = min(BM, M - tc.row0);
+    tc.n0 = n_idx * BN;
+  }
+  return true;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+
+template <int EPI>
+__device__ __forceinline__ void epi_store(void* C, size_t idx, float v0, float v1, const float* bias,
+                                          int col) {
+  if constexpr (EPI == EPI_BF16) {
+    static_cast<uint16_t*>(C)[idx] = f32_to_bf16(v0);
+  } else if constexpr (EPI == EPI_SWIGLU_BF16) {
+    static_cast<uint16_t*>(C)[idx] = f32_to_bf16(silu_mul(v0, v1));
+  } else if constexpr (EPI == EPI_F32) {
+    static_cast<float*>(C)[idx] = v0;
+  } else if constexpr (EPI == EPI_SWIGLU_F32) {
+    static_cast<float*>(C)[idx] = silu_mul(v0, v1);
+  } else {  // EPI_F32_BIAS
+    static_cast<float*>(C)[idx] = bias ? v0 + bias[col] : v0;
+  }
+}
+
+// ------------------------------------------------------------------ bf16 prefill kernel
+// Workgroup tile BM x BN (x NB weight matrices sharing the A tile), 4 waves in
+// 2 x 2, K-step 64 staged through LDS (rows padded to 72 elements so the 16
+// rows one MFMA operand read touches fall in distinct banks), next step's
+// global loads in flight during the current step's MFMAs.
+
+constexpr int kPBK = 64;
+constexpr int kPLD = kPBK + 8;
+
+template <int BM, int BN, int NB, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_prefill(
+    const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+  constexpr int TM = BM / 2, TN = BN / 2;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int A_PER = BM * 8 / 256, B_PER = BN * 8 / 256;
+  static_assert(A_PER >= 1 && B_PER >= 1, "tile too small");
+  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * kPLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[NB][BN * kPLD];
+
+  TileCoord tc;
+  if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const uint16_t* B0e = B0 + (size_t)tc.e * N * K;
+  const uint16_t* B1e = NB > 1 ? B1 + (size_t)tc.e * N * K : B0e;
+
+  // loader mapping: chunk i of this thread is row (tid / 8) + 32 i, K-offset 8 * (tid % 8);
+  // source rows are clamped into the tile so no load leaves its expert's segment
+  const int lrow = tid >> 3, lk = (tid & 7) * 8;
+  uint32_t aoff[A_PER], boff[B_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i)
+    aoff[i] = (uint32_t)(tc.row0 + min(lrow + 32 * i, tc.rows - 1));
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) boff[i] = (uint32_t)min(tc.n0 + lrow + 32 * i, N - 1);
+  const int lds0 = lrow * kPLD + lk;
+  auto a_src = [&](int i, int k0) {
+    return reinterpret_cast<const u32x4*>(A + (size_t)aoff[i] * K + lk + k0);
+  };
+  auto b_src = [&](int nb, int i, int k0) {
+    return reinterpret_cast<const u32x4*>((nb == 0 ? B0e : B1e) + (size_t)boff[i] * K + lk + k0);
+  };
+
+  f32x4 acc[NB][FM][FN];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[nb][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[A_PER], rb[NB][B_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) ra[i] = *a_src(i, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) rb[nb][i] = *b_src(nb, i, 0);
+
+  const int arow = wm * TM + (lane & 15);
+  const int brow = wn * TN + (lane & 15);
+  const int kofs = (lane >> 4) * 8;
+
+  for (int k0 = 0; k0 < K; k0 += kPBK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) *reinterpret_cast<u32x4*>(&sA[lds0 + 32 * i * kPLD]) = ra[i];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) *reinterpret_cast<u32x4*>(&sB[nb][lds0 + 32 * i * kPLD]) = rb[nb][i];
+    __syncthreads();
+    {  // next step's loads (the last step re-reads its own slice, keeping the loop branch-free)
+      const int kn = min(k0 + kPBK, K - kPBK);
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) ra[i] = *a_src(i, kn);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < B_PER; ++i) rb[nb][i] = *b_src(nb, i, kn);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kPBK; ks += 32) {
+      bf16x8 af[FM];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sA[(arow + fm * 16) * kPLD + ks + kofs]));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const bf16x8 bf =
+              as_bf16x8(*reinterpret_cast<const u32x4*>(&sB[nb][(brow + fn * 16) * kPLD + ks + kofs]));
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            acc[nb][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf, acc[nb][fm][fn], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 fragment
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+        const int c = tc.n0 + wn * TN + fn * 16 + (lane & 15);
+        if (r < tc.rows && c < N)
+          epi_store<EPI>(C, (size_t)(tc.row0 + r) * N + c, acc[0][fm][fn][i],
+                         NB > 1 ? acc[NB - 1][fm][fn][i] : 0.f, nullptr, c);
+      }
+}
+
+// ------------------------------------------------------------------ bf16 decode kernel
+// For experts with a handful of rows: 16-row m-tiles, no LDS, every wave
+// streams its own 16*FN weight rows straight from HBM with two K-steps of loads
+// in flight.  Within a 64-wide K-step lane l carries k = 16*(l/16) .. +16 of
+// both operands (two 8-element MFMA halves); the same permutation of k on A and
+// B leaves the sum unchanged and makes each weight row's 128 bytes one
+// contiguous read by 4 lanes.
+
+template <int NB, int FN>
+struct DecodeRegs {
+  uint4 a[2];
+  uint4 b[NB][FN][2];
+};
+
+template <int NB, int FN>
+__device__ __forceinline__ void decode_load(DecodeRegs<NB, FN>& r, const uint16_t* pa,
+                                            const uint16_t* const (&pb)[NB][FN], int k0) {
+  r.a[0] = *reinterpret_cast<const uint4*>(pa + k0);
+  r.a[1] = *reinterpret_cast<const uint4*>(pa + k0 + 8);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      r.b[nb][fn][0] = *reinterpret_cast<const uint4*>(pb[nb][fn] + k0);
+      r.b[nb][fn][1] = *reinterpret_cast<const uint4*>(pb[nb][fn] + k0 + 8);
+    }
+}
+
+template <int NB, int FN>
+__device__ __forceinline__ void decode_mma(f32x4 (&acc)[NB][FN], const DecodeRegs<NB, FN>& r) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x8 a = as_bf16x8(r.a[h]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[nb][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(r.b[nb][fn][h]),
+                                                               acc[nb][fn], 0, 0, 0);
+  }
+}
+
+template <int NB, int FN, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_decode(
+    const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+  constexpr int BM = 16, BN = 4 * 16 * FN;
+  TileCoord tc;
+  if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kl = (lane >> 4) * 16;
+  const uint16_t* pa = A + (size_t)(tc.row0 + min(lane & 15, tc.rows - 1)) * K + kl;
+  const uint16_t* pb[NB][FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int gn = min(tc.n0 + wave * 16 * FN + fn * 16 + (lane & 15), N - 1);
+    pb[0][fn] = B0 + ((size_t)tc.e * N + gn) * K + kl;
+    if constexpr (NB > 1) pb[NB - 1][fn] = B1 + ((size_t)tc.e * N + gn) * K + kl;
+  }
+  f32x4 acc[NB][FN];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[nb][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  DecodeRegs<NB, FN> r0, r1;
+  const int steps = K / 64;
+  decode_load<NB, FN>(r0, pa, pb, 0);
+  if (steps > 1) decode_load<NB, FN>(r1, pa, pb, 64);
+  for (int s = 0; s < steps; s += 2) {
+    decode_mma<NB, FN>(acc, r0);
+    if (s + 2 < steps) decode_load<NB, FN>(r0, pa, pb, (s + 2) * 64);
+    if (s + 1 < steps) {
+      decode_mma<NB, FN>(acc, r1);
+      if (s + 3 < steps) decode_load<NB, FN>(r1, pa, pb, (s + 3) * 64);
+    }
+  }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (lane >> 4) * 4 + i;
+      const int c = tc.n0 + wave * 16 * FN + fn * 16 + (lane & 15);
+      if (r < tc.rows && c < N)
+        epi_store<EPI>(C, (size_t)(tc.row0 + r) * N + c, acc[0][fn][i],
+                       NB > 1 ? acc[NB - 1][fn][i] : 0.f, nullptr, c);
+    }
+}
+
+// ------------------------------------------------------------------ fp32 SIMT kernel
+// fp32 layers and the exact-input fp32 gate: 64x64 tile, 16x16 threads with
+// 4x4 outputs each, K chunks of 16 through LDS; each output is one fma chain
+// over ascending k.  A is fp32 or bf16 (widened exactly), B is fp32.
+
+constexpr int kSBK = 16;
+
+template <typename AT>
+__device__ __forceinline__ float load_as_f32(const AT* p);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename AT, int NB, int EPI>
+__global__ __launch_bounds__(256) void k_gemm_simt(const AT* __restrict__ A, int M,
+                                                   const float* __restrict__ B0,
+                                                   const float* __restrict__ B1,
+                                                   void* __restrict__ C,
+                                                   const int32_t* __restrict__ offsets,
+                                                   const int32_t* __restrict__ mtile_start, int E,
+                                                   int N, int K, const float* __restrict__ bias) {
+  constexpr int BM = 64, BN = 64;
+  __shared__ float sA[kSBK][BM + 4];
+  __shared__ float sB[NB][kSBK][BN + 4];
+  TileCoord tc;
+  if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const float* Bm[2] = {B0 + (size_t)tc.e * N * K, NB > 1 ? B1 + (size_t)tc.e * N * K : nullptr};
+  float acc[NB][4][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[nb][i][j] = 0.f;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row lr, k lk .. lk+3
+  for (int k0 = 0; k0 < K; k0 += kSBK) {
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kk = k0 + lk + q;
+      float va = 0.f;
+      if (lr < tc.rows && kk < K) va = load_as_f32<AT>(A + (size_t)(tc.row0 + lr) * K + kk);
+      sA[lk + q][lr] = va;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float vb = 0.f;
+        if (tc.n0 + lr < N && kk < K) vb = Bm[nb][(size_t)(tc.n0 + lr) * K + kk];
+        sB[nb][lk + q][lr] = vb;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kSBK; ++kk) {
+      float a[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sA[kk][ty + 16 * i];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float b = sB[nb][kk][tx + 16 * j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nb][i][j] = fmaf(a[i], b, acc[nb][i][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = ty + 16 * i, c = tc.n0 + tx + 16 * j;
+      if (r < tc.rows && c < N)
+        epi_store<EPI>(C, (size_t)(tc.row0 + r) * N + c, acc[0][i][j],
+                       NB > 1 ? acc[NB - 1][i][j] : 0.f, bias, c);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+static inline int grid_for(int max_mtiles, int N, int BN) {
+  const long tiles = (long)max_mtiles * ceil_div(N, BN);
+  return (int)(ceil_div((int)tiles, 8) * 8);
+}
+
+int gemm_bm(GemmKind kind) {
+  switch (kind) {
+    case GEMM_PREFILL: return 128;
+    case GEMM_DECODE: return 16;
+    default: return 64;
+  }
+}
+
+int max_mtiles(int M, int E, int bm) {
+  // sum_e ceil(n_e / bm) <= floor(M / bm) + (number of non-empty experts)
+  return M / bm + (E < M ? E : M) + 1;
+}
+
+#define MOE_LAUNCH(kern, grid) \
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K)
+
+hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
+                            const uint16_t* B1, void* C, const int32_t* offsets,
+                            const int32_t* mtile_start, int E, int N, int K, hipStream_t st) {
+  const int bm = gemm_bm(kind);
+  const int mt = offsets ? max_mtiles(M, E, bm) : ceil_div(M, bm);
+  if (kind == GEMM_PREFILL) {
+    const int g = grid_for(mt, N, 128);
+    switch (epi) {
+      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_BF16>), g); break;
+      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_F32>), g); break;
+      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16>), g); break;
+      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32>), g); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const int g = grid_for(mt, N, 4 * 16 * 2);
+    switch (epi) {
+      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), g); break;
+      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_F32>), g); break;
+      case EPI_BF16: MOE_LAUNCH((k_gemm_decode<1, 2, EPI_BF16>), g); break;
+      case EPI_F32: MOE_LAUNCH((k_gemm_decode<1, 2, EPI_F32>), g); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_simt(bool a_bf16, int epi, const void* A, int M, const float* B0,
+                            const float* B1, void* C, const int32_t* offsets,
+                            const int32_t* mtile_start, int E, int N, int K, const float* bias,
+                            hipStream_t st) {
+  const int mt = offsets ? max_mtiles(M, E, 64) : ceil_div(M, 64);
+  const int g = grid_for(mt, N, 64);
+#define MOE_SIMT(AT, NB, EP)                                                                   \
+  hipLaunchKernelGGL((k_gemm_simt<AT, NB, EP>), dim3(g), dim3(256), 0, st,                     \
+                     static_cast<const AT*>(A), M, B0, B1, C, offsets, mtile_start, E, N, K, bias)
+  if (a_bf16) {
+    switch (epi) {
+      case EPI_F32_BIAS: MOE_SIMT(uint16_t, 1, EPI_F32_BIAS); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (epi) {
+      case EPI_F32_BIAS: MOE_SIMT(float, 1, EPI_F32_BIAS); break;
+      case EPI_F32: MOE_SIMT(float, 1, EPI_F32); break;
+      case EPI_SWIGLU_F32: MOE_SIMT(float, 2, EPI_SWIGLU_F32); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef MOE_SIMT
+  return hipGetLastError();
+}
+
+}  // namespace moe

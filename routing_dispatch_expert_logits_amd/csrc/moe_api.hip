@@ -1,0 +1,380 @@
+// Host side of the libmoe C ABI: argument validation, workspace carve-up,
+// kernel selection by shape, and the launch sequence of each call.  No call
+// allocates, synchronises or reads device memory.
+#include <climits>
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Carve {
+  size_t cur = 0;
+  size_t take(size_t bytes) {
+    const size_t o = cur;
+    cur = align_up(cur + bytes);
+    return o;
+  }
+};
+
+bool al16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al16_or_null(const void* p) { return !p || al16(p); }
+
+struct Dims {
+  int T, H, E, k, I, L, D, R, nb, es;
+  bool bf16;
+};
+
+moe_status check_shape(const moe_shape* s, Dims& d) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->L < 0 || s->reserved != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->k > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->E > kMaxE || s->k > kWave) return MOE_ERR_UNSUPPORTED;
+  if (s->T > INT_MAX || s->H > INT_MAX || s->I > INT_MAX || s->L > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (s->T * s->k > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  d.T = (int)s->T; d.H = (int)s->H; d.E = (int)s->E; d.k = (int)s->k; d.I = (int)s->I;
+  d.L = (int)s->L; d.D = d.L ? d.L : d.H; d.R = d.T * d.k;
+  d.nb = ceil_div(d.T, kBlockTok);
+  d.bf16 = s->dtype == MOE_BF16;
+  d.es = d.bf16 ? 2 : 4;
+  if (d.bf16) {
+    if (d.D % 64 || d.I % 64 || (d.L && d.H % 64)) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (d.D % 4 || d.H % 4) return MOE_ERR_UNSUPPORTED;
+  }
+  // element counts addressed with int inside some kernels
+  if ((long long)d.R * d.D / 8 > INT_MAX || (long long)d.T * d.E > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+GemmKind expert_kind(const Dims& d) {
+  if (!d.bf16) return GEMM_SIMT;
+  // mean rows per expert decides between one weight pass with 128-row tiles and
+  // 16-row tiles that stream weights once per handful of rows
+  return (d.R >= 48 * d.E) ? GEMM_PREFILL : GEMM_DECODE;
+}
+
+struct RouteWs { size_t bc, total; };
+RouteWs route_ws(const Dims& d) {
+  Carve c; RouteWs w;
+  w.bc = c.take((size_t)d.nb * d.E * 4);
+  w.total = c.cur;
+  return w;
+}
+
+struct FfnWs { size_t mtile, act, total; };
+FfnWs ffn_ws(const Dims& d) {
+  Carve c; FfnWs w;
+  w.mtile = c.take((size_t)(d.E + 1) * 4);
+  w.act = c.take((size_t)d.R * d.I * d.es);
+  w.total = c.cur;
+  return w;
+}
+
+struct CombWs { size_t ytok, total; };
+CombWs comb_ws(const Dims& d) {
+  Carve c; CombWs w;
+  w.ytok = c.take((size_t)d.R * d.D * d.es);
+  w.total = c.cur;
+  return w;
+}
+
+struct LayerWs {
+  size_t logits, ids, w, counts, offsets, row_token, token_row, bc, mtile, z, xperm, act, outl, total;
+};
+LayerWs layer_ws(const Dims& d) {
+  Carve c; LayerWs w;
+  w.logits = c.take((size_t)d.T * d.E * 4);
+  w.ids = c.take((size_t)d.R * 4);
+  w.w = c.take((size_t)d.R * 4);
+  w.counts = c.take((size_t)d.E * 4);
+  w.offsets = c.take((size_t)(d.E + 1) * 4);
+  w.row_token = c.take((size_t)d.R * 4);
+  w.token_row = c.take((size_t)d.R * 4);
+  w.bc = c.take((size_t)d.nb * d.E * 4);
+  w.mtile = c.take((size_t)(d.E + 1) * 4);
+  w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
+  w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
+  w.act = c.take((size_t)d.R * d.I * d.es);
+  w.outl = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
+  w.total = c.cur;
+  return w;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+#define MOE_HIP(call)                          \
+  do {                                         \
+    if ((call) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status gate_scores(const Dims& d, const void* x, const float* gate_w, const float* bias,
+                       float* logits, hipStream_t st) {
+  MOE_HIP(launch_gemm_simt(d.bf16, EPI_F32_BIAS, x, d.T, gate_w, nullptr, logits, nullptr, nullptr,
+                           1, d.E, d.H, bias, st));
+  return MOE_OK;
+}
+
+moe_status expert_ffn(const Dims& d, const void* x_perm, const int32_t* offsets,
+                      const int32_t* mtile, const void* w1, const void* w3, const void* w2,
+                      void* act, void* y_perm, hipStream_t st) {
+  const GemmKind kind = expert_kind(d);
+  if (kind == GEMM_SIMT) {
+    MOE_HIP(launch_gemm_simt(false, EPI_SWIGLU_F32, x_perm, d.R, static_cast<const float*>(w1),
+                             static_cast<const float*>(w3), act, offsets, mtile, d.E, d.I, d.D,
+                             nullptr, st));
+    MOE_HIP(launch_gemm_simt(false, EPI_F32, act, d.R, static_cast<const float*>(w2), nullptr,
+                             y_perm, offsets, mtile, d.E, d.D, d.I, nullptr, st));
+  } else {
+    MOE_HIP(launch_gemm_bf16(kind, EPI_SWIGLU_BF16, static_cast<const uint16_t*>(x_perm), d.R,
+                             static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
+                             act, offsets, mtile, d.E, d.I, d.D, st));
+    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                             static_cast<const uint16_t*>(w2), nullptr, y_perm, offsets, mtile,
+                             d.E, d.D, d.I, st));
+  }
+  return MOE_OK;
+}
+
+// Dense projection C[M x N] = A[M x K] W^T for the latent layers (W stored [N x K]).
+moe_status dense_proj(const Dims& d, const void* A, const void* W, void* C, int M, int N, int K,
+                      bool out_f32, hipStream_t st) {
+  if (d.bf16) {
+    MOE_HIP(launch_gemm_bf16(GEMM_PREFILL, out_f32 ? EPI_F32 : EPI_BF16,
+                             static_cast<const uint16_t*>(A), M, static_cast<const uint16_t*>(W),
+                             nullptr, C, nullptr, nullptr, 1, N, K, st));
+  } else {
+    if (!out_f32) return MOE_ERR_UNSUPPORTED;
+    MOE_HIP(launch_gemm_simt(false, EPI_F32, A, M, static_cast<const float*>(W), nullptr, C,
+                             nullptr, nullptr, 1, N, K, nullptr, st));
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: bad shape or pointer";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside the kernels' limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    default: return "unknown moe_status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int call) {
+  Dims d;
+  if (check_shape(s, d) != MOE_OK) return 0;
+  switch (call) {
+    case MOE_CALL_ROUTE: return route_ws(d).total;
+    case MOE_CALL_DISPATCH: return route_ws(d).total;
+    case MOE_CALL_FFN: return ffn_ws(d).total;
+    case MOE_CALL_COMBINE: return comb_ws(d).total;
+    case MOE_CALL_LAYER: return layer_ws(d).total;
+    default: return 0;
+  }
+}
+
+moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
+                          float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                          int32_t* offsets, const moe_shape* s, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!al16(logits) || !al16(topk_ids) || !al16(topk_w) || !al16(counts) || !al16(offsets) ||
+      !al16_or_null(gate_w) || !al16_or_null(gate_bias))
+    return MOE_ERR_INVALID_ARG;
+  if (gate_w && !al16(x)) return MOE_ERR_INVALID_ARG;
+  const RouteWs w = route_ws(d);
+  if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (gate_w) {
+    rc = gate_scores(d, x, gate_w, gate_bias, logits, st);
+    if (rc != MOE_OK) return rc;
+  }
+  int32_t* bc = at<int32_t>(ws, w.bc);
+  MOE_HIP(launch_topk(logits, gate_w ? nullptr : gate_bias, d.T, d.E, d.k, topk_ids, topk_w, bc, st));
+  MOE_HIP(launch_scan(bc, d.nb, d.E, nullptr, counts, offsets, 0, nullptr, st));
+  return MOE_OK;
+}
+
+moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
+                                void* x_perm, int32_t* row_token, int32_t* token_row,
+                                const moe_shape* s, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!al16(x) || !al16(topk_ids) || !al16(offsets) || !al16(x_perm) || !al16(row_token) ||
+      !al16(token_row))
+    return MOE_ERR_INVALID_ARG;
+  const RouteWs w = route_ws(d);
+  if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* bc = at<int32_t>(ws, w.bc);
+  MOE_HIP(launch_block_counts(topk_ids, d.T, d.E, d.k, bc, st));
+  MOE_HIP(launch_scan(bc, d.nb, d.E, offsets, nullptr, nullptr, 0, nullptr, st));
+  MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, bc, x_perm, row_token,
+                         token_row, st));
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
+                           const void* w3, const void* w2, void* y_perm, const moe_shape* s,
+                           void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!al16(x_perm) || !al16(offsets) || !al16(w1) || !al16(w3) || !al16(w2) || !al16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  const FfnWs w = ffn_ws(d);
+  if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* mtile = at<int32_t>(ws, w.mtile);
+  MOE_HIP(launch_mtiles(offsets, d.E, gemm_bm(expert_kind(d)), mtile, st));
+  return expert_ffn(d, x_perm, offsets, mtile, w1, w3, w2, at<void>(ws, w.act), y_perm, st);
+}
+
+moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
+                       void* out, int out_dtype, int flags, const moe_shape* s, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!al16(y_perm) || !al16(token_row) || !al16(topk_w) || !al16(out)) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (flags != MOE_COMBINE_FUSED && flags != MOE_COMBINE_UNFUSED) return MOE_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int row16 = d.D * d.es / 16;
+  const bool of32 = out_dtype == MOE_F32;
+  if (flags == MOE_COMBINE_FUSED) {
+    MOE_HIP(launch_combine(y_perm, row16, d.bf16, token_row, topk_w, d.T, d.k, out, of32, st));
+    return MOE_OK;
+  }
+  const CombWs w = comb_ws(d);
+  if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
+  void* ytok = at<void>(ws, w.ytok);
+  MOE_HIP(launch_unpermute(y_perm, row16, token_row, d.R, ytok, st));
+  MOE_HIP(launch_weighted_reduce(ytok, row16, d.bf16, topk_w, d.T, d.k, out, of32, st));
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* logits, void* out,
+                             int out_dtype, const moe_shape* s, moe_layer_aux* aux,
+                             void** stage_events, void* ws, size_t ws_bytes, void* stream) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!wt || !al16(x) || !al16(out) || !al16(wt->w1) || !al16(wt->w3) || !al16(wt->w2))
+    return MOE_ERR_INVALID_ARG;
+  if (!al16_or_null(wt->gate_w) || !al16_or_null(wt->gate_bias) || !al16_or_null(logits))
+    return MOE_ERR_INVALID_ARG;
+  if (!wt->gate_w && !logits) return MOE_ERR_INVALID_ARG;  // given logits are required
+  if (d.L && (!al16(wt->wd) || !al16(wt->wu))) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!d.bf16 && d.L && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  moe_layer_aux none = {};
+  moe_layer_aux& ax = aux ? *aux : none;
+  const void* auxp[] = {ax.topk_ids, ax.topk_w, ax.counts, ax.offsets, ax.row_token,
+                        ax.token_row, ax.x_perm, ax.y_perm, ax.z, ax.out_latent};
+  for (const void* p : auxp)
+    if (!al16_or_null(p)) return MOE_ERR_INVALID_ARG;
+  const LayerWs w = layer_ws(d);
+  if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto pick = [&](void* user, size_t off) { return user ? user : at<void>(ws, off); };
+  float* lg = static_cast<float*>(logits ? logits : at<void>(ws, w.logits));
+  int32_t* ids = static_cast<int32_t*>(pick(ax.topk_ids, w.ids));
+  float* tw = static_cast<float*>(pick(ax.topk_w, w.w));
+  int32_t* counts = static_cast<int32_t*>(pick(ax.counts, w.counts));
+  int32_t* offs = static_cast<int32_t*>(pick(ax.offsets, w.offsets));
+  int32_t* rtok = static_cast<int32_t*>(pick(ax.row_token, w.row_token));
+  int32_t* trow = static_cast<int32_t*>(pick(ax.token_row, w.token_row));
+  int32_t* bc = at<int32_t>(ws, w.bc);
+  int32_t* mtile = at<int32_t>(ws, w.mtile);
+  void* z = d.L ? pick(ax.z, w.z) : nullptr;
+  void* xperm = pick(ax.x_perm, w.xperm);
+  // y_perm: caller's buffer, else the workspace x_perm region (free once the gate/up GEMM has read it)
+  void* yperm = ax.y_perm ? ax.y_perm : at<void>(ws, w.xperm);
+  void* act = at<void>(ws, w.act);
+  void* outl = d.L ? pick(ax.out_latent, w.outl) : nullptr;
+
+  auto ev = [&](int i) -> bool {
+    return !stage_events || hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
+  };
+  const GemmKind kind = expert_kind(d);
+
+  if (!ev(0)) return MOE_ERR_HIP;
+  if (d.L) {  // a7: Z = X wd^T (rounded to the layer dtype)
+    rc = dense_proj(d, x, wt->wd, z, d.T, d.L, d.H, !d.bf16, st);
+    if (rc != MOE_OK) return rc;
+  }
+  if (!ev(1)) return MOE_ERR_HIP;
+  if (wt->gate_w) {  // a1: router logits on the full-width state
+    rc = gate_scores(d, x, wt->gate_w, wt->gate_bias, lg, st);
+    if (rc != MOE_OK) return rc;
+  }
+  if (!ev(2)) return MOE_ERR_HIP;
+  // a2 + a3
+  MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
+  MOE_HIP(launch_scan(bc, d.nb, d.E, nullptr, counts, offs, gemm_bm(kind), mtile, st));
+  if (!ev(3)) return MOE_ERR_HIP;
+  // a4
+  MOE_HIP(launch_permute(d.L ? z : x, d.D * d.es / 16, ids, d.T, d.E, d.k, bc, xperm, rtok, trow, st));
+  if (!ev(4)) return MOE_ERR_HIP;
+  // a5
+  if (kind == GEMM_SIMT) {
+    MOE_HIP(launch_gemm_simt(false, EPI_SWIGLU_F32, xperm, d.R, static_cast<const float*>(wt->w1),
+                             static_cast<const float*>(wt->w3), act, offs, mtile, d.E, d.I, d.D,
+                             nullptr, st));
+    if (!ev(5)) return MOE_ERR_HIP;
+    MOE_HIP(launch_gemm_simt(false, EPI_F32, act, d.R, static_cast<const float*>(wt->w2), nullptr,
+                             yperm, offs, mtile, d.E, d.D, d.I, nullptr, st));
+  } else {
+    MOE_HIP(launch_gemm_bf16(kind, EPI_SWIGLU_BF16, static_cast<const uint16_t*>(xperm), d.R,
+                             static_cast<const uint16_t*>(wt->w1),
+                             static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I, d.D,
+                             st));
+    if (!ev(5)) return MOE_ERR_HIP;
+    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
+                             d.E, d.D, d.I, st));
+  }
+  if (!ev(6)) return MOE_ERR_HIP;
+  // a6
+  const int row16 = d.D * d.es / 16;
+  if (d.L) {
+    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, d.T, d.k, outl, !d.bf16, st));
+  } else {
+    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, d.T, d.k, out, out_dtype == MOE_F32, st));
+  }
+  if (!ev(7)) return MOE_ERR_HIP;
+  if (d.L) {  // a7: out = out_L wu^T
+    rc = dense_proj(d, outl, wt->wu, out, d.T, d.H, d.L, out_dtype == MOE_F32, st);
+    if (rc != MOE_OK) return rc;
+  }
+  if (!ev(8)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

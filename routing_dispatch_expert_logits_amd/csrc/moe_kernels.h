@@ -1,0 +1,52 @@
+// Internal launchers of the libmoe kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_device.h"
+
+namespace moe {
+
+enum Epi {
+  EPI_BF16 = 0,         // C = bf16(acc)
+  EPI_SWIGLU_BF16 = 1,  // C = bf16(SiLU(acc0) * acc1)
+  EPI_F32 = 2,          // C = acc
+  EPI_SWIGLU_F32 = 3,   // C = SiLU(acc0) * acc1
+  EPI_F32_BIAS = 4      // C = acc + bias[col]
+};
+
+enum GemmKind { GEMM_PREFILL = 0, GEMM_DECODE = 1, GEMM_SIMT = 2 };
+
+int gemm_bm(GemmKind kind);
+int max_mtiles(int M, int E, int bm);
+
+hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
+                       float* w, int32_t* block_counts, hipStream_t st);
+hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t* block_counts,
+                               hipStream_t st);
+hipError_t launch_scan(int32_t* block_counts, int nb, int E, const int32_t* offsets_in,
+                       int32_t* counts_out, int32_t* offsets_out, int bm, int32_t* mtile_start,
+                       hipStream_t st);
+hipError_t launch_mtiles(const int32_t* offsets, int E, int bm, int32_t* mtile_start,
+                         hipStream_t st);
+hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
+                          const int32_t* bases, void* x_perm, int32_t* row_token,
+                          int32_t* token_row, hipStream_t st);
+hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
+                          const float* w, int T, int k, void* out, bool out_f32, hipStream_t st);
+hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
+                            hipStream_t st);
+hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
+                                  int T, int k, void* out, bool out_f32, hipStream_t st);
+// bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.
+hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
+                            const uint16_t* B1, void* C, const int32_t* offsets,
+                            const int32_t* mtile_start, int E, int N, int K, hipStream_t st);
+// fp32 SIMT GEMM (A fp32 or bf16, B fp32).
+hipError_t launch_gemm_simt(bool a_bf16, int epi, const void* A, int M, const float* B0,
+                            const float* B1, void* C, const int32_t* offsets,
+                            const int32_t* mtile_start, int E, int N, int K, const float* bias,
+                            hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,136 @@
+"""The C-ABI library on the host: it loads, exports every declared call, sizes
+workspaces, and rejects bad arguments before any GPU work (CPU only).
+
+The calls below all fail host-side validation, so they return before any HIP
+call; the fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from routing_dispatch_expert_logits_amd import binding as B
+from workloads import FULL_CONFIGS, PARITY_CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_route_topk", "moe_dispatch_permute", "moe_grouped_ffn", "moe_combine",
+                 "moe_layer_forward", "moe_workspace_bytes", "moe_status_string", "moe_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(B.lib, name)
+
+
+def test_abi_version_and_status_strings():
+    assert B.lib.moe_abi_version() == B.ABI_VERSION
+    for code in range(5):
+        assert B.status_string(code).startswith("MOE_")
+    assert "unknown" in B.status_string(99)
+
+
+def _bytes(cfg, call):
+    return B.workspace_bytes(B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype), call)
+
+
+@pytest.mark.parametrize("cfg", list(FULL_CONFIGS.values()) + list(PARITY_CONFIGS.values()),
+                         ids=lambda c: c.name)
+def test_workspace_sizes(cfg):
+    R, D, es = cfg.R, cfg.D, cfg.elem_bytes
+    route = _bytes(cfg, B.MOE_CALL_ROUTE)
+    assert route >= ((cfg.T + 63) // 64) * cfg.E * 4
+    assert _bytes(cfg, B.MOE_CALL_FFN) >= R * cfg.I * es
+    assert _bytes(cfg, B.MOE_CALL_COMBINE) >= R * D * es
+    layer = _bytes(cfg, B.MOE_CALL_LAYER)
+    assert layer >= R * D * es + R * cfg.I * es
+    # one permuted-row buffer serves both x_perm and y_perm
+    assert layer < 2 * R * D * es + R * cfg.I * es + 2 * cfg.T * max(cfg.L, 1) * es + 64 * 1024 * 1024
+
+
+def test_invalid_shapes_have_no_workspace():
+    bad = [B.shape(0, 128, 8, 2, 256), B.shape(4, 128, 8, 9, 256), B.shape(4, 128, 0, 1, 256),
+           B.shape(4, 128, 2048, 2, 256), B.shape(4, 100, 8, 2, 256),   # bf16 needs D % 64
+           B.shape(4, 128, 8, 2, 100), B.shape(4, 128, 128, 65, 256)]
+    for s in bad:
+        assert B.workspace_bytes(s, B.MOE_CALL_LAYER) == 0
+
+
+def _route(s, ws_bytes=1 << 20, **over):
+    args = dict(x=FAKE, gate_w=None, bias=None, logits=FAKE, ids=FAKE, w=FAKE, counts=FAKE,
+                offsets=FAKE, ws=FAKE)
+    args.update(over)
+    return B.lib.moe_route_topk(args["x"], args["gate_w"], args["bias"], args["logits"], args["ids"],
+                                args["w"], args["counts"], args["offsets"], ctypes.byref(s),
+                                args["ws"], ws_bytes, None)
+
+
+def test_route_rejects_bad_arguments_on_host():
+    s = B.shape(64, 128, 8, 2, 256)
+    assert _route(B.shape(0, 128, 8, 2, 256)) == B.MOE_ERR_INVALID_ARG
+    assert _route(B.shape(64, 128, 8, 9, 256)) == B.MOE_ERR_INVALID_ARG       # k > E
+    assert _route(B.shape(64, 128, 2000, 2, 256)) == B.MOE_ERR_UNSUPPORTED    # E > 1024
+    assert _route(B.shape(64, 128, 200, 65, 256)) == B.MOE_ERR_UNSUPPORTED    # k > 64
+    assert _route(s, logits=None) == B.MOE_ERR_INVALID_ARG
+    assert _route(s, ids=FAKE + 4) == B.MOE_ERR_INVALID_ARG                   # misaligned
+    assert _route(s, ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert _route(s, ws=None) == B.MOE_ERR_WORKSPACE
+    bad = B.shape(64, 128, 8, 2, 256)
+    bad.reserved = 1
+    assert _route(bad) == B.MOE_ERR_INVALID_ARG
+    bad = B.shape(64, 128, 8, 2, 256)
+    bad.dtype = 7
+    assert _route(bad) == B.MOE_ERR_INVALID_ARG
+
+
+def test_other_calls_reject_bad_arguments_on_host():
+    s = B.shape(64, 128, 8, 2, 256)
+    L = B.lib
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(s), FAKE, 1 << 20,
+                                  None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 0,
+                                  None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.byref(s), FAKE, 1 << 30,
+                             None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 8,
+                             None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 5, 0, ctypes.byref(s), FAKE, 1 << 30,
+                         None) == B.MOE_ERR_INVALID_ARG                     # out dtype
+    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 0, 3, ctypes.byref(s), FAKE, 1 << 30,
+                         None) == B.MOE_ERR_INVALID_ARG                     # flags
+    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 0, B.MOE_COMBINE_UNFUSED, ctypes.byref(s), FAKE, 8,
+                         None) == B.MOE_ERR_WORKSPACE
+    w = B.MoeLayerWeights(None, None, FAKE, FAKE, FAKE, None, None)
+    aux = B.MoeLayerAux()
+    # no gate weight and no given logits
+    assert L.moe_layer_forward(ctypes.byref(w), FAKE, None, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
+                               None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    # latent layer without projections
+    sl = B.shape(64, 128, 8, 2, 256, L=64)
+    assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(sl), ctypes.byref(aux),
+                               None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    aux.x_perm = FAKE + 8
+    assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
+                               None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    aux.x_perm = None
+    assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
+                               None, FAKE, 1024, None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_layer_forward(None, FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
+                               None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG

@@ -1,0 +1,292 @@
+"""GPU parity of every stage against the CPU oracle on small seeded layers.
+
+Each test feeds the same seeded inputs (workloads/) to the HIP path through the
+C ABI and to the oracle, then compares element by element:
+
+* integers (ids, counts, offsets, row_token, token_row) and the permuted rows:
+  bit-exact;
+* routing weights: |dw| <= 1e-6;
+* gate logits: max |d| <= 1e-5 x RMS(logits);
+* expert outputs Y: within one bf16 ulp of the oracle plus 5e-3 x RMS(Y), and
+  at most 1e-4 of the elements beyond one ulp plus 1e-3 x RMS(Y) (the oracle
+  rounds A and Y at the same points; a different fp32 summation order can move
+  an A element one ulp, see _check_y), max |d| <= 2e-2 x RMS overall; fp32
+  layers 1e-5 x RMS;
+* layer output (fp32 result): max |d| <= 2e-2 x RMS(out) for bf16 layers,
+  1e-5 x RMS(out) for fp32 layers; the bf16 output is bitwise the
+  round-to-nearest-even of the fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import PARITY_CONFIGS, generator as gen
+from routing_dispatch_expert_logits_amd import binding as B
+from tests.gpu_util import (dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits, rel_err,
+                            check_permutation_valid)
+
+pytestmark = pytest.mark.gpu
+
+CFGS = list(PARITY_CONFIGS.values())
+IDS = [c.name for c in CFGS]
+
+
+def _scores_input(cfg, step=0):
+    """Seeded fp32 router logits given to moe_route_topk (and the bias, if any)."""
+    lg = gen.drawn_logits(cfg, step)
+    return lg, gen.zipf_bias(cfg)
+
+
+def _route_gpu(cfg, logits, bias):
+    s = shape_of(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    ids, w = empty((T, k), "i32"), empty((T, k), "f32")
+    counts, offs = empty((E,), "i32"), empty((E + 1,), "i32")
+    B.route_topk(None, None, None if bias is None else dev(bias), dev(logits), ids, w, counts, offs,
+                 s, ws(s, B.MOE_CALL_ROUTE))
+    torch.cuda.synchronize()
+    return host(ids), host(w), host(counts), host(offs)
+
+
+def _check_route(cfg, logits, bias):
+    ids, w, counts, offs = _route_gpu(cfg, logits, bias)
+    ref = oracle.route(oracle.router_scores(logits, bias), cfg.k, cfg.E)
+    np.testing.assert_array_equal(ids, ref["ids"])
+    np.testing.assert_array_equal(counts, ref["counts"])
+    np.testing.assert_array_equal(offs, ref["offsets"])
+    assert np.max(np.abs(w - ref["weights"])) <= 1e-6
+    return ref
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=IDS)
+def test_route_topk_bit_exact(cfg):
+    lg, bias = _scores_input(cfg)
+    _check_route(cfg, lg, bias)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 8), (100, 7), (256, 8), (896, 16), (1024, 64), (5, 5)])
+def test_route_ties_and_signed_zeros(E, k):
+    """Integer-valued scores (heavy ties), -0.0 next to +0.0, and -inf entries."""
+    T = 203
+    r = np.random.default_rng(E * 1000 + k)
+    lg = r.integers(-2, 3, size=(T, E)).astype(np.float32)
+    lg[lg == 0] = np.where(r.random(int((lg == 0).sum())) < 0.5, -0.0, 0.0).astype(np.float32)
+    lg[5, :] = 0.0
+    lg[6, :] = -0.0
+    lg[7, : E // 2] = -np.inf
+    cfg = PARITY_CONFIGS["all_ties"].with_(T=T, E=E, k=k)
+    _check_route(cfg, lg, None)
+
+
+@pytest.mark.parametrize("cfg", [c for c in CFGS if c.gate == "computed"],
+                         ids=[c.name for c in CFGS if c.gate == "computed"])
+def test_gate_logits(cfg):
+    inp = gen.layer_inputs(cfg, with_experts=False)
+    s = shape_of(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    logits = empty((T, E), "f32")
+    ids, w = empty((T, k), "i32"), empty((T, k), "f32")
+    counts, offs = empty((E,), "i32"), empty((E + 1,), "i32")
+    bias = inp.get("bias")
+    B.route_topk(dev(inp["x"]), dev(inp["gate_w"]), None if bias is None else dev(bias), logits,
+                 ids, w, counts, offs, s, ws(s, B.MOE_CALL_ROUTE))
+    torch.cuda.synchronize()
+    ref = oracle.gate_logits(inp["x"], inp["gate_w"], bias)
+    assert rel_err(host(logits), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=IDS)
+def test_dispatch_permute_bit_exact(cfg):
+    lg, bias = _scores_input(cfg)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
+    rt, tr = oracle.permutation(ref["ids"], cfg.E)
+    x = gen.activations(cfg)
+    s = shape_of(cfg)
+    R, D = cfg.R, cfg.H
+    sc = s if not cfg.L else B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, 0, cfg.dtype)
+    x_perm = empty((R, D), act_kind(cfg))
+    row_token, token_row = empty((R,), "i32"), empty((cfg.T, cfg.k), "i32")
+    B.dispatch_permute(dev(x), dev(ref["ids"].astype(np.int32)), dev(ref["offsets"].astype(np.int32)),
+                       x_perm, row_token, token_row, sc, ws(sc, B.MOE_CALL_DISPATCH))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(row_token), rt)
+    np.testing.assert_array_equal(host(token_row), tr)
+    xp = host(x_perm, bf16=cfg.dtype == "bf16")
+    np.testing.assert_array_equal(xp, oracle.gather_rows(x, rt))
+    assert xp.nbytes == oracle.dispatch_bytes(cfg.T, cfg.k, D, cfg.elem_bytes)
+
+
+def _ffn_inputs(cfg):
+    lg, bias = _scores_input(cfg)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
+    rt, _ = oracle.permutation(ref["ids"], cfg.E)
+    x = gen.draw(cfg, gen.TAG_X, 0, (cfg.T, cfg.D), cfg.x_std)
+    return ref, oracle.gather_rows(x, rt)
+
+
+def _check_y(cfg, got, ref_y):
+    """Expert outputs: both sides round A and Y to bf16 at the same points, but the
+    fp32 sums run in different orders, so an A element near a rounding midpoint
+    can land one ulp apart; that moves Y by ulp(a) * |w2| (about 1e-3 x RMS(Y) for
+    |a| ~ 5 x RMS(a) at I = 256).  Bound: every element within one bf16 ulp of Y
+    plus 5e-3 x RMS(Y); at most 1e-4 of them beyond one ulp plus 1e-3 x RMS(Y)."""
+    if cfg.dtype == "bf16":
+        y = oracle.decode(got)
+        rms = float(np.sqrt(np.mean(ref_y ** 2)))
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref_y), 1e-30))) - 7)
+        err = np.abs(y - ref_y)
+        worst = float(np.max((err - ulp) / rms))
+        assert not (err > ulp + 5e-3 * rms).any(), f"worst excess over 1 ulp: {worst:.2e} x RMS"
+        frac = float(np.mean(err > ulp + 1e-3 * rms))
+        assert frac <= 1e-4, f"{frac:.2e} of elements beyond 1 ulp + 1e-3 RMS (worst {worst:.2e})"
+        assert rel_err(y, ref_y) <= 2e-2
+    else:
+        assert rel_err(got, ref_y) <= 1e-5
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=IDS)
+def test_grouped_ffn(cfg):
+    ref, xp = _ffn_inputs(cfg)
+    wts = gen.expert_weights(cfg)
+    s = shape_of(cfg)
+    y = empty((cfg.R, cfg.D), act_kind(cfg))
+    B.grouped_ffn(dev(xp), dev(ref["offsets"].astype(np.int32)), dev(wts["w1"]), dev(wts["w3"]),
+                  dev(wts["w2"]), y, s, ws(s, B.MOE_CALL_FFN))
+    torch.cuda.synchronize()
+    ref_y = oracle.grouped_expert_ffn(xp, ref["offsets"], wts["w1"], wts["w3"], wts["w2"],
+                                      bf16=cfg.dtype == "bf16")
+    _check_y(cfg, host(y, bf16=cfg.dtype == "bf16"), ref_y)
+
+
+def test_grouped_ffn_never_reads_empty_experts():
+    """Weights of experts with no rows are NaN: outputs stay finite and unchanged."""
+    cfg = PARITY_CONFIGS["many_empty"]
+    ref, xp = _ffn_inputs(cfg)
+    wts = gen.expert_weights(cfg)
+    s = shape_of(cfg)
+    offs = dev(ref["offsets"].astype(np.int32))
+    y0, y1 = empty((cfg.R, cfg.D), "bf16"), empty((cfg.R, cfg.D), "bf16")
+    B.grouped_ffn(dev(xp), offs, dev(wts["w1"]), dev(wts["w3"]), dev(wts["w2"]), y0, s,
+                  ws(s, B.MOE_CALL_FFN))
+    empty_e = np.nonzero(ref["counts"] == 0)[0]
+    assert len(empty_e) > cfg.E // 2
+    nan = np.uint16(0x7FC0)
+    for name in ("w1", "w3", "w2"):
+        wts[name][empty_e] = nan
+    B.grouped_ffn(dev(xp), offs, dev(wts["w1"]), dev(wts["w3"]), dev(wts["w2"]), y1, s,
+                  ws(s, B.MOE_CALL_FFN))
+    torch.cuda.synchronize()
+    a, b = host(y0, True), host(y1, True)
+    assert np.isfinite(oracle.decode(b)).all()
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=IDS)
+def test_combine(cfg):
+    lg, bias = _scores_input(cfg)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
+    _, tr = oracle.permutation(ref["ids"], cfg.E)
+    w32 = ref["weights"].astype(np.float32)
+    y = gen.stage_rows(cfg, cfg.R, cfg.D)
+    s = shape_of(cfg)
+    outs = {}
+    for flags in (B.MOE_COMBINE_FUSED, B.MOE_COMBINE_UNFUSED):
+        for od in (B.MOE_F32, B.MOE_BF16):
+            o = empty((cfg.T, cfg.D), "f32" if od == B.MOE_F32 else "bf16")
+            B.combine(dev(y), dev(tr.astype(np.int32)), dev(w32), o, od, flags, s,
+                      ws(s, B.MOE_CALL_COMBINE))
+            outs[(flags, od)] = o
+    torch.cuda.synchronize()
+    f32 = host(outs[(B.MOE_COMBINE_FUSED, B.MOE_F32)])
+    ref_out = oracle.combine(y, tr, w32.astype(np.float64))
+    assert rel_err(f32, ref_out) <= 1e-5
+    np.testing.assert_array_equal(host(outs[(B.MOE_COMBINE_UNFUSED, B.MOE_F32)]), f32)
+    bf = host(outs[(B.MOE_COMBINE_FUSED, B.MOE_BF16)], True)
+    np.testing.assert_array_equal(bf, rne_bf16_bits(f32))
+    np.testing.assert_array_equal(host(outs[(B.MOE_COMBINE_UNFUSED, B.MOE_BF16)], True), bf)
+
+
+# ------------------------------------------------------------------ whole layer
+
+def run_layer(cfg, inp, out_dtype=B.MOE_F32, with_aux=True):
+    """moe_layer_forward on uploaded inputs; returns host copies of out and the aux buffers."""
+    s = shape_of(cfg)
+    T, E, k, R, D = cfg.T, cfg.E, cfg.k, cfg.R, cfg.D
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu") if n in inp}
+    if "bias" in inp:
+        w["gate_bias"] = dev(inp["bias"])
+    logits = dev(inp["logits"]) if "logits" in inp else empty((T, E), "f32")
+    aux = {}
+    if with_aux:
+        aux = {"topk_ids": empty((T, k), "i32"), "topk_w": empty((T, k), "f32"),
+               "counts": empty((E,), "i32"), "offsets": empty((E + 1,), "i32"),
+               "row_token": empty((R,), "i32"), "token_row": empty((T, k), "i32"),
+               "x_perm": empty((R, D), act_kind(cfg)), "y_perm": empty((R, D), act_kind(cfg))}
+        if cfg.L:
+            aux["z"] = empty((T, cfg.L), act_kind(cfg))
+            aux["out_latent"] = empty((T, cfg.L), act_kind(cfg))
+    out = empty((T, cfg.H), "f32" if out_dtype == B.MOE_F32 else "bf16")
+    B.layer_forward(w, dev(inp["x"]), logits, out, out_dtype, s, ws(s, B.MOE_CALL_LAYER), aux)
+    torch.cuda.synchronize()
+    res = {"out": host(out, out_dtype == B.MOE_BF16), "logits": host(logits)}
+    bf = cfg.dtype == "bf16"
+    for n, t in aux.items():
+        res[n] = host(t, bf and n in ("x_perm", "y_perm", "z", "out_latent"))
+    return res
+
+
+def unambiguous_tokens(scores_ref: np.ndarray, k: int, tol: float) -> np.ndarray:
+    """Tokens whose top-k set cannot change under score perturbations below tol."""
+    if k == scores_ref.shape[1]:
+        return np.ones(scores_ref.shape[0], dtype=bool)
+    srt = -np.sort(-scores_ref, axis=1)
+    return (srt[:, k - 1] - srt[:, k]) > 2 * tol
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=IDS)
+def test_layer_forward(cfg):
+    inp = gen.layer_inputs(cfg)
+    bf = cfg.dtype == "bf16"
+    got = run_layer(cfg, inp)
+    ref = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=bf)
+    if "logits" in inp:   # given router output: routing must be bit-exact everywhere
+        keep = np.ones(cfg.T, dtype=bool)
+        np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
+        np.testing.assert_array_equal(got["counts"], ref["counts"])
+        np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+        np.testing.assert_array_equal(got["row_token"], ref["row_token"])
+        np.testing.assert_array_equal(got["token_row"], ref["token_row"])
+    else:                 # computed logits: compare routing where the scores decide it uniquely
+        tol = 1e-5 * float(np.sqrt(np.mean(ref["logits"] ** 2)))
+        assert rel_err(got["logits"], ref["logits"]) <= 1e-5
+        keep = unambiguous_tokens(ref["logits"], cfg.k, tol)
+        assert keep.mean() > 0.99
+        np.testing.assert_array_equal(np.sort(got["topk_ids"][keep], axis=1),
+                                      np.sort(ref["ids"][keep], axis=1))
+        check_permutation_valid(got["topk_ids"], got["offsets"], got["row_token"], got["token_row"])
+        np.testing.assert_array_equal(got["counts"], np.diff(got["offsets"]))
+    tol = 2e-2 if bf else 1e-5
+    assert rel_err(got["out"][keep], ref["out"][keep]) <= tol
+    # bf16 output is the RNE of the fp32 output of the same kernels
+    got16 = run_layer(cfg, inp, out_dtype=B.MOE_BF16, with_aux=False)
+    np.testing.assert_array_equal(got16["out"], rne_bf16_bits(got["out"]))
+
+
+@pytest.mark.parametrize("name", ["small_bf16_zipf", "small_latent", "tiny_f32"])
+def test_layer_matches_separate_calls_and_is_deterministic(name):
+    """Fusion is execution-only: routing, permutation and output bits equal the separate calls."""
+    cfg = PARITY_CONFIGS[name]
+    inp = gen.layer_inputs(cfg)
+    a = run_layer(cfg, inp)
+    b = run_layer(cfg, inp)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    # separate calls on the fused call's own logits
+    lg = a["logits"]
+    bias = None if cfg.gate == "computed" else inp.get("bias")
+    ids, w, counts, offs = _route_gpu(cfg, lg, bias)
+    np.testing.assert_array_equal(ids, a["topk_ids"])
+    np.testing.assert_array_equal(w, a["topk_w"])
+    np.testing.assert_array_equal(counts, a["counts"])
+    np.testing.assert_array_equal(offs, a["offsets"])
