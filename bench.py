@@ -1,0 +1,286 @@
+"""Benchmark one routed-expert MoE layer forward on one MI355X.
+
+A step is one moe_layer_forward over one seeded batch: gate scores, top-k +
+counts + offsets, permutation, grouped SwiGLU expert GEMMs, combine (and the
+latent projections for the latent layer).  Inputs and weights are resident in
+HBM before timing starts.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+The default workload is the Qwen3-30B-A3B-shaped layer (T=4096, H=2048,
+E=128, k=8, I=768, bf16).  Other configs: deepseek_r1_shaped,
+k3_shaped_decode, latent_moe, tiny_f32.
+
+Per-stage times come from HIP events that moe_layer_forward records on the
+stream the kernels run on.  The roofline object describes the dominant kernel
+(the expert gate/up GEMM): algorithmic bytes per launch over its average
+event-timed duration, against MI355X's 8 TB/s HBM peak.  cpu_baseline is the
+CPU oracle (tests' reference implementation) timed on a bounded token sample of
+the same layer on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+F32_PEAK_TFLOPS = 157.3
+GEMM_SRC = os.path.join(ROOT, "routing_dispatch_expert_logits_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{config}.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            assert rc == 0, f"hipEventCreate failed: {rc}"
+            evs.append(h.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        assert rc == 0, f"hipEventElapsedTime failed: {rc}"
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def stage_bytes_flops(cfg, counts):
+    """Algorithmic HBM bytes and FLOPs per stage for one layer forward.
+
+    b = element bytes of activations/weights; touched = experts with >= 1 row.
+    """
+    T, H, E, k, I, L, D, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.D, cfg.R
+    b = cfg.elem_bytes
+    touched = int(sum(1 for c in counts if c > 0))
+    out_b = 2 if cfg.dtype == "bf16" else 4
+    st = {}
+    st["latent_down"] = (T * H * b + L * H * b + T * L * b, 2 * T * H * L) if L else (0, 0)
+    st["gate"] = ((T * H * b + E * H * 4 + T * E * 4, 2 * T * H * E) if cfg.gate == "computed"
+                  else (0, 0))
+    st["route"] = (T * E * 4 + 8 * R + (2 * E + 1) * 4, 0)
+    st["permute"] = (T * D * b + R * D * b + 12 * R, 0)
+    st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
+    st["gemm_down"] = (touched * D * I * b + R * I * b + R * D * b, 2 * R * D * I)
+    st["combine"] = (R * D * b + 8 * R + T * D * (b if L else out_b), 0)
+    st["latent_up"] = (T * L * b + H * L * b + T * H * out_b, 2 * T * L * H) if L else (0, 0)
+    return st, touched
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def cpu_baseline(cfg, inp, target_s):
+    """Time the CPU oracle on the first n tokens of the same layer, growing n until
+    about target_s seconds of work (or the whole layer); report assignments/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = 1
+    n = min(64, cfg.T)
+    while True:
+        sub = dict(inp)
+        sub["x"] = inp["x"][:n]
+        if "logits" in inp:
+            sub["logits"] = inp["logits"][:n]
+        t0 = time.perf_counter()
+        oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16")
+        dt = time.perf_counter() - t0
+        log(f"cpu oracle: {n} tokens in {dt:.2f} s")
+        if dt >= target_s / 3 or n >= cfg.T:
+            break
+        n = min(cfg.T, n * 4)
+    return {"value": n * cfg.k / dt, "unit": "assignments/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same layer (all {cfg.E} experts' "
+                      f"weights), float64 numpy oracle, {dt:.2f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3_30b_a3b_shaped")
+    ap.add_argument("--skew-steps", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's share of the layer only; --gpus {args.gpus} is not "
+              "supported (no collectives between GPUs in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from routing_dispatch_expert_logits_amd import binding as B
+    from workloads import FULL_CONFIGS, generator as gen
+
+    cfg = FULL_CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} L={cfg.L} {cfg.dtype}")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+
+    t0 = time.perf_counter()
+    inp = gen.layer_inputs(cfg)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
+    w = {n: up(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu") if n in inp}
+    if "bias" in inp:
+        w["gate_bias"] = up(inp["bias"])
+    x = up(inp["x"])
+    logits = up(inp["logits"]) if "logits" in inp else torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype)
+    ws = torch.empty(B.workspace_bytes(s, B.MOE_CALL_LAYER), dtype=torch.uint8, device=dev)
+    od = B.MOE_BF16 if args.out_dtype == "bf16" and cfg.dtype == "bf16" else B.MOE_F32
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16 if od == B.MOE_BF16 else torch.float32, device=dev)
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    aux = {"counts": counts}
+    torch.cuda.synchronize()
+    resident = sum(t.numel() * t.element_size() for t in w.values())
+    log(f"uploaded; resident weights {resident / 1e9:.2f} GB, workspace {ws.numel() / 1e9:.2f} GB")
+
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = HipEvents()
+    nev = B.MOE_NUM_STAGE_EVENTS
+    evs = [hip.create(nev) for _ in range(args.steps)]
+
+    for _ in range(args.warmup):
+        B.layer_forward(w, x, logits, out, od, s, ws, aux=aux, stream=stream)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    # timed region: exactly K steps, synchronised on both sides (one GPU: no barrier needed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        B.layer_forward(w, x, logits, out, od, s, ws, aux=aux, stage_events=evs[i], stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step")
+
+    names = B.STAGE_NAMES
+    stage_ms = {n: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    layer_ev_ms = float(np.mean([hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]))
+    for e in evs:
+        hip.destroy(e)
+
+    cnt = counts.cpu().numpy()
+    sb, touched = stage_bytes_flops(cfg, cnt)
+    stages = {}
+    for n in names:
+        byt, flp = sb[n]
+        if byt == 0 and flp == 0:
+            continue
+        t_s = stage_ms[n] * 1e-3
+        stages[n] = {"ms": round(stage_ms[n], 5), "GB/s": round(byt / t_s / 1e9, 1) if t_s > 0 else None}
+        if flp:
+            stages[n]["TFLOP/s"] = round(flp / t_s / 1e12, 2)
+
+    # p95 of the max/mean expert-load ratio over reseeded steps (route only)
+    skews = []
+    if args.skew_steps > 0:
+        ids_b = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+        w_b = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+        offs_b = torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev)
+        lg_b = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+        ws_r = torch.empty(max(B.workspace_bytes(s, B.MOE_CALL_ROUTE), 256), dtype=torch.uint8, device=dev)
+        for step in range(args.skew_steps):
+            if cfg.gate == "computed":
+                B.route_topk(up(gen.activations(cfg, step)), w["gate_w"], w.get("gate_bias"), lg_b,
+                             ids_b, w_b, counts, offs_b, s, ws_r, stream=stream)
+            else:
+                B.route_topk(None, None, w.get("gate_bias"), up(gen.drawn_logits(cfg, step)), ids_b,
+                             w_b, counts, offs_b, s, ws_r, stream=stream)
+            c = counts.cpu().numpy()
+            skews.append(float(c.max()) / (cfg.T * cfg.k / cfg.E))
+        srt = sorted(skews)
+        p95 = srt[int(np.ceil(0.95 * len(srt))) - 1]
+        log(f"p95 skew over {len(skews)} steps: {p95:.3f}")
+    else:
+        p95 = None
+
+    # roofline of the dominant kernel: the expert gate/up GEMM
+    g_bytes, g_flops = sb["gemm_gate_up"]
+    g_s = stage_ms["gemm_gate_up"] * 1e-3
+    achieved = g_bytes / g_s / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "k_gemm_prefill<128,128,2,SwiGLU> (expert gate/up GEMM)" if cfg.dtype == "bf16" and cfg.R >= 48 * cfg.E
+            else "expert gate/up GEMM",
+            "algorithmic_bytes": int(g_bytes), "avg_ms": round(stage_ms["gemm_gate_up"], 5),
+            "mfma_tflops": round(g_flops / g_s / 1e12, 1),
+            "mfma_frac": round(g_flops / g_s / 1e12 / (BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS), 4)}
+    tf = TRAFFIC_FILE.format(config=cfg.name)
+    if os.path.exists(tf):
+        tr = json.load(open(tf))
+        if tr.get("gemm_src_sha256_16") == src_hash(GEMM_SRC):
+            roof["traffic"] = tr.get("hbm_bytes_per_launch")
+
+    gemm_ms = stage_ms["gemm_gate_up"] + stage_ms["gemm_down"]
+    line = {
+        "metric": "routed assignments/s per MoE layer",
+        "value": round(cfg.R / (ms_per_step * 1e-3), 1),
+        "unit": "assignments/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic: seeded numpy PCG64 inputs, random-init weights",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "L": cfg.L, "out_dtype": "bf16" if od == B.MOE_BF16 else "f32"},
+        "grouped_gemm_tflops": round((sb["gemm_gate_up"][1] + sb["gemm_down"][1]) / (gemm_ms * 1e-3) / 1e12, 1),
+        "permute_gbps": stages["permute"]["GB/s"],
+        "combine_gbps": stages["combine"]["GB/s"],
+        "layer_event_ms": round(layer_ev_ms, 5),
+        "stages": stages,
+        "p95_skew": round(p95, 3) if p95 is not None else None,
+        "touched_experts": touched,
+        "dispatch_bytes": cfg.T * cfg.k * cfg.D * cfg.elem_bytes,
+        "dispatch_bytes_full_width": cfg.T * cfg.k * cfg.H * cfg.elem_bytes,
+        "resident_expert_bytes": resident,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,6 +52,10 @@ class MoeLayerAux(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own libamdhip64.so.7; loading torch first makes libmoe bind
+    # to that same HIP runtime instance, so torch's streams, events and
+    # allocations are the library's too
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmoe.so not built at {LIB_PATH}; run "
                           "`python -m routing_dispatch_expert_logits_amd.build`")
