@@ -137,6 +137,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB 3 times "
+                         "(reference kernel of known size for HBM counter scaling)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share of the layer only; --gpus {args.gpus} is not "
@@ -199,6 +202,16 @@ def main(argv=None):
     layer_ev_ms = float(np.mean([hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]))
     for e in evs:
         hip.destroy(e)
+
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src_c = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst_c = torch.empty_like(src_c)
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
+        log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
 
     cnt = counts.cpu().numpy()
     sb, touched = stage_bytes_flops(cfg, cnt)

@@ -45,7 +45,7 @@
  *   finite or -inf; caller-supplied topk_ids are in [0, E) and distinct per
  *   token; offsets are the exclusive prefix sum of the per-expert counts.
  *
- * Limits: 1 <= k <= E <= 1024; T*k < 2^31; bf16 layers need D % 64 == 0,
+ * Limits: 1 <= k <= E, E <= 1024, k <= 64; T*k < 2^31; bf16 layers need D % 64 == 0,
  * I % 64 == 0 and (for latent layers) H % 64 == 0; fp32 layers need D % 4 == 0
  * and H % 4 == 0.
  */
@@ -60,6 +60,10 @@ extern "C" {
 #endif
 
 #define MOE_ABI_VERSION 1
+
+#ifndef MOE_API
+#define MOE_API __attribute__((visibility("default")))
+#endif
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -103,13 +107,13 @@ typedef struct moe_shape {
 } moe_shape;
 
 /* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
-size_t moe_workspace_bytes(const moe_shape* s, int call);
+MOE_API size_t moe_workspace_bytes(const moe_shape* s, int call);
 
 /* Static string for a status code. */
-const char* moe_status_string(int status);
+MOE_API const char* moe_status_string(int status);
 
 /* MOE_ABI_VERSION of the loaded library. */
-int moe_abi_version(void);
+MOE_API int moe_abi_version(void);
 
 /*
  * Gate scores + top-k selection + per-expert counts and offsets (steps a1-a3).
@@ -134,7 +138,7 @@ int moe_abi_version(void);
  * counts   [E] int32 out: assignments per expert (sum = T*k).
  * offsets  [E+1] int32 out: exclusive prefix sum of counts, offsets[E] = T*k.
  */
-moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
+MOE_API moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
                           float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
                           int32_t* offsets, const moe_shape* s, void* ws, size_t ws_bytes,
                           void* stream);
@@ -156,7 +160,7 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
  * row_token [T*k] int32 out: source token of each row.
  * token_row [T x k] int32 out: row holding token t's j-th assignment.
  */
-moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
+MOE_API moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
                                 void* x_perm, int32_t* row_token, int32_t* token_row,
                                 const moe_shape* s, void* ws, size_t ws_bytes, void* stream);
 
@@ -177,7 +181,7 @@ moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const in
  *        (SiLU(x w1[e]^T) * (x w3[e]^T)) w2[e]^T, with the intermediate rounded
  *        to dtype; unweighted (weights apply in the combine).
  */
-moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
+MOE_API moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
                            const void* w3, const void* w2, void* y_perm, const moe_shape* s,
                            void* ws, size_t ws_bytes, void* stream);
 
@@ -199,7 +203,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const voi
  *           "unpermutation" and "combine" timers of "Three Parameter Counts...",
  *           "What the utilization dashboard smooths away").  Same result bits.
  */
-moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
+MOE_API moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
                        void* out, int out_dtype, int flags, const moe_shape* s, void* ws,
                        size_t ws_bytes, void* stream);
 
@@ -247,7 +251,7 @@ typedef struct moe_layer_aux {
  * stage_events  NULL or an array of MOE_NUM_STAGE_EVENTS hipEvent_t created by
  *         the caller; each is recorded on `stream` at its stage boundary.
  */
-moe_status moe_layer_forward(const moe_layer_weights* w, const void* x, float* logits, void* out,
+MOE_API moe_status moe_layer_forward(const moe_layer_weights* w, const void* x, float* logits, void* out,
                              int out_dtype, const moe_shape* s, moe_layer_aux* aux,
                              void** stage_events, void* ws, size_t ws_bytes, void* stream);
 

@@ -370,22 +370,28 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool) -> 
 def token_outputs(inp: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarray,
                   weights: np.ndarray, expert_w: Dict[int, tuple], *, bf16: bool,
                   z: Optional[np.ndarray] = None) -> np.ndarray:
-    """Layer output of selected tokens only, computed token by token.
+    """Layer output of selected tokens only: out[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x_t).
 
-    For full-size layers: token t's output is sum_j w[t, j] * FFN_{ids[t, j]}(x_t),
-    with ``expert_w[e] = (w1e, w3e, w2e)`` supplied for every expert the
-    tokens use.  Same rounding points as ``layer_forward``.
+    For full-size layers.  ``ids`` / ``weights`` are [len(tokens) x k] for the
+    selected tokens, ``expert_w[e] = (w1e, w3e, w2e)`` for every expert they
+    use, ``z`` the latent rows of the selected tokens (latent layers).  Each
+    expert's FFN acts on rows independently, so it is evaluated once on all the
+    selected rows routed to it.  Same rounding points as ``layer_forward``.
     """
-    src = z if z is not None else decode(inp["x"])
-    rows = []
-    for t in tokens.tolist():
-        acc = np.zeros(src.shape[1], dtype=np.float64)
-        for j in range(ids.shape[1]):
-            w1e, w3e, w2e = expert_w[int(ids[t, j])]
-            y = expert_ffn_rows(src[t:t + 1], w1e, w3e, w2e, bf16)[0]
-            acc += weights[t, j] * y
-        rows.append(acc)
-    out = np.stack(rows)
+    tokens = np.asarray(tokens)
+    src = z if z is not None else decode(np.asarray(inp["x"])[tokens])
+    n, k = ids.shape
+    y = {}
+    for e in sorted(set(int(v) for v in ids.ravel())):
+        rows = [i for i in range(n) if e in ids[i]]
+        w1e, w3e, w2e = expert_w[e]
+        ye = expert_ffn_rows(src[rows], w1e, w3e, w2e, bf16)
+        for r, i in enumerate(rows):
+            y[(i, e)] = ye[r]
+    out = np.zeros((n, src.shape[1]), dtype=np.float64)
+    for j in range(k):
+        for i in range(n):
+            out[i] += weights[i, j] * y[(i, int(ids[i, j]))]
     if "wu" in inp:
         out = latent_up(out, inp["wu"], bf16)
     return out

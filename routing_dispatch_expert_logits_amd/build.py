@@ -26,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
 DEVICE_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-Wall", "-Wno-unused-function",
+                "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
                 "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

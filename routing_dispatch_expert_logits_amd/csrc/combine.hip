@@ -70,13 +70,15 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kCombTokPerWg + (threadIdx.x >> 6);
   if (t >= T) return;
+  const int c0 = (int)((long)row16 * blockIdx.y / gridDim.y);
+  const int c1 = (int)((long)row16 * (blockIdx.y + 1) / gridDim.y);
   int my_row = 0;
   float my_w = 0.f;
   if (lane < k) {
     my_row = token_row[(size_t)t * k + lane];
     my_w = topk_w[(size_t)t * k + lane];
   }
-  for (int c = lane; c < row16; c += kWave) {
+  for (int c = c0 + lane; c < c1; c += kWave) {
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
@@ -150,7 +152,11 @@ __global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict
 
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
                           const float* w, int T, int k, void* out, bool out_f32, hipStream_t st) {
-  const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
+  // split columns until ~1024 workgroups (small token counts)
+  const int gx = ceil_div(T, kCombTokPerWg);
+  int cs = 1;
+  while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
+  const dim3 g(gx, cs), b(256);
   if (in_bf16)
     hipLaunchKernelGGL(k_combine<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y), row16,
                        token_row, w, T, k, out, (int)out_f32);

@@ -81,18 +81,20 @@ __device__ __forceinline__ void epi_store(void* C, size_t idx, float v0, float v
 
 // ------------------------------------------------------------------ bf16 prefill kernel
 // Workgroup tile BM x BN (x NB weight matrices sharing the A tile), 4 waves in
-// 2 x 2, K-step 64 staged through LDS (rows padded to 72 elements so the 16
-// rows one MFMA operand read touches fall in distinct banks), next step's
-// global loads in flight during the current step's MFMAs.
+// 2 x 2, K-step 64 staged through LDS (rows padded to 80 elements: 160-byte rows
+// let one MFMA operand read of 16 rows run at full LDS rate on gfx950), next
+// step's global loads in flight during the current step's MFMAs.
 
 constexpr int kPBK = 64;
-constexpr int kPLD = kPBK + 8;
 
-template <int BM, int BN, int NB, int EPI>
-__global__ __launch_bounds__(256) void k_gemm_prefill(
+// MINW: waves per SIMD the register budget must allow (2 -> two workgroups per CU);
+// PAD: LDS row padding in bf16 elements.
+template <int BM, int BN, int NB, int EPI, int MINW = 1, int PAD = 16>
+__global__ __launch_bounds__(256, MINW) void k_gemm_prefill(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+  constexpr int kPLD = kPBK + PAD;
   constexpr int TM = BM / 2, TN = BN / 2;
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr int A_PER = BM * 8 / 256, B_PER = BN * 8 / 256;
@@ -184,6 +186,165 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
   }
 
   // epilogue: lane holds rows 4*(lane/16)+i, column lane%16 of each 16x16 fragment
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+        const int c = tc.n0 + wn * TN + fn * 16 + (lane & 15);
+        if (r < tc.rows && c < N)
+          epi_store<EPI>(C, (size_t)(tc.row0 + r) * N + c, acc[0][fm][fn][i],
+                         NB > 1 ? acc[NB - 1][fm][fn][i] : 0.f, nullptr, c);
+      }
+}
+
+// ------------------------------------------------------------------ bf16 pipelined kernel
+// Wave-specialised variant of the tile kernel: 4 MFMA waves (2 x 2, 64 x 64
+// each) and 2 loader waves per workgroup.  The loader waves copy each K-step's
+// A and B tiles straight from global memory into an S-stage LDS ring with
+// global_load_lds_dwordx4 (no register staging) and run up to two stages
+// ahead; the MFMA waves only read LDS.  One barrier per K-step hands stage s
+// to the MFMA waves and the freed stage back to the loaders.  Because only the
+// loader waves issue the LDS DMA, the MFMA waves' LDS reads never wait for
+// loads of later stages.
+//
+// LDS layout: a tile is rows of 64 bf16 (8 16-byte chunks); chunk c of row r is
+// stored at chunk slot c ^ (r & 7).  Measured on gfx950, ds_read_b128 of 16
+// consecutive rows at one chunk index runs at full LDS rate with this XOR
+// (about 200 B/clk/CU), while unswizzled 128-byte rows run at a quarter and
+// 144-byte padded rows at half of it.  A DMA instruction fills 8 consecutive
+// rows (lane i -> row 8q + i/8, slot i % 8).
+
+__device__ __forceinline__ int swz(int r) { return r & 7; }
+
+// The LDS-DMA builtin takes a global-address-space source and an LDS
+// destination; spelling both casts out keeps the host compilation pass of the
+// kernel valid (it otherwise drops the kernel's host stub).
+typedef const __attribute__((address_space(1))) void* gas_ptr;
+typedef __attribute__((address_space(3))) void* las_ptr;
+
+// s_waitcnt immediate that waits until at most n vector-memory ops are outstanding
+// (vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at "no wait").
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+static_assert(waitcnt_vm(24) == 0x4F78 && waitcnt_vm(0) == 0x0F70, "s_waitcnt encoding");
+
+template <int BM, int BN, int NB, int EPI, int S>
+__global__ __launch_bounds__(384) void k_gemm_ws(
+    const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+  static_assert(BM == 128 && BN == 128, "4 MFMA waves of 64 x 64");
+  static_assert(S == 3 || S == 4, "3- or 4-stage ring");
+  constexpr int TM = 64, TN = 64, FM = 4, FN = 4;
+  constexpr int A_ELEMS = BM * 64, B_ELEMS = BN * 64;
+  constexpr int STAGE = A_ELEMS + NB * B_ELEMS;   // bf16 elements per stage
+  constexpr int NQ = (BM + NB * BN) / 8;          // DMA instructions per stage
+  constexpr int NQP = NQ / 2;                     // per loader wave
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
+
+  TileCoord tc;
+  if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nsteps = K / 64;
+
+  if (wave >= 4) {
+    // ---------------- loader waves
+    const int p = wave - 4;
+    const uint16_t* src[NQP];
+    int ldsoff[NQP];
+#pragma unroll
+    for (int j = 0; j < NQP; ++j) {
+      const int q = p * NQP + j;       // instruction index within the stage
+      const int r = (q % 16) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      if (q < 16) {                    // A tile rows
+        src[j] = A + (size_t)(tc.row0 + min(r, tc.rows - 1)) * K + c * 8;
+        ldsoff[j] = (q % 16) * 512;
+      } else {
+        const uint16_t* Bm = (q < 32) ? B0 : B1;
+        src[j] = Bm + ((size_t)tc.e * N + min(tc.n0 + r, N - 1)) * K + c * 8;
+        ldsoff[j] = A_ELEMS + (q / 16 - 1) * B_ELEMS + (q % 16) * 512;
+      }
+    }
+    auto issue = [&](int st) {
+      const int base = (st % S) * STAGE;
+#pragma unroll
+      for (int j = 0; j < NQP; ++j)
+        __builtin_amdgcn_global_load_lds((gas_ptr)(src[j] + st * 64), (las_ptr)&lds[base + ldsoff[j]],
+                                         16, 0, 0);
+    };
+    // Up to S-1 stages in flight.  wait_behind(n): the oldest outstanding stage has
+    // landed once at most n later stages (n * NQP loads) are still in flight.
+    auto wait_behind = [](int n) {
+      if (n >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NQP));
+      else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQP));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    };
+    const int pre = min(S - 1, nsteps);               // stages issued before the loop
+    for (int st = 0; st < pre; ++st) issue(st);
+    wait_behind(pre - 1);                             // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    for (int s = 0; s < nsteps; ++s) {
+      if (s + S - 1 < nsteps) issue(s + S - 1);       // into the stage freed by step s - 1
+      // stage s+1 must land; later issued stages are s+2 .. min(s+S-1, nsteps-1)
+      wait_behind(max(0, min(s + S - 1, nsteps - 1) - (s + 1)));
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    return;
+  }
+
+  // ---------------- MFMA waves
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x4 acc[NB][FM][FN];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[nb][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // element offsets of this lane's operand chunks inside a stage, per 32-wide substep
+  int aoffs[2][FM], boffs[2][FN];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 4 + (lane >> 4);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = wm * TM + fm * 16 + (lane & 15);
+      aoffs[h][fm] = r * 64 + ((c ^ swz(r)) << 3);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int r = wn * TN + fn * 16 + (lane & 15);
+      boffs[h][fn] = A_ELEMS + r * 64 + ((c ^ swz(r)) << 3);
+    }
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const uint16_t* base = lds + (s % S) * STAGE;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 af[FM];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+        af[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoffs[h][fm]));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[h][fn]));
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            acc[nb][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf, acc[nb][fm][fn], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -398,11 +559,27 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
   const int mt = offsets ? max_mtiles(M, E, bm) : ceil_div(M, bm);
   if (kind == GEMM_PREFILL) {
     const int g = grid_for(mt, N, 128);
+    // Measured on MI355X (expert GEMMs of the Qwen3-30B-A3B- and DeepSeek-R1-shaped
+    // layers): for the gate/up pair with a long K the wave-specialised LDS-DMA kernel
+    // is ~8% faster; otherwise the register-staged tile kernel at two workgroups per
+    // CU wins.
+    const bool pipelined = (epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_F32) && K >= 4096;
+    if (pipelined) {
+      const dim3 gb(g), bb(384);
+      if (epi == EPI_SWIGLU_BF16)
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3>), gb, bb, 0, st, A, M, B0, B1, C,
+                           offsets, mtile_start, E, N, K);
+      else
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3>), gb, bb, 0, st, A, M, B0, B1, C,
+                           offsets, mtile_start, E, N, K);
+      return hipGetLastError();
+    }
     switch (epi) {
-      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_BF16>), g); break;
-      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_F32>), g); break;
-      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16>), g); break;
-      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32>), g); break;
+      // two workgroups per CU: one hides the other's barrier and load waits
+      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_BF16, 2>), g); break;
+      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_F32, 2>), g); break;
+      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16, 2>), g); break;
+      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32, 2>), g); break;
       default: return hipErrorInvalidValue;
     }
   } else {

@@ -44,7 +44,7 @@ moe_status check_shape(const moe_shape* s, Dims& d) {
   if (s->T * s->k > INT_MAX) return MOE_ERR_UNSUPPORTED;
   d.T = (int)s->T; d.H = (int)s->H; d.E = (int)s->E; d.k = (int)s->k; d.I = (int)s->I;
   d.L = (int)s->L; d.D = d.L ? d.L : d.H; d.R = d.T * d.k;
-  d.nb = ceil_div(d.T, kBlockTok);
+  d.nb = ceil_div(d.T, block_tokens(d.T));
   d.bf16 = s->dtype == MOE_BF16;
   d.es = d.bf16 ? 2 : 4;
   if (d.bf16) {
@@ -123,8 +123,12 @@ P* at(void* ws, size_t off) {
 
 moe_status gate_scores(const Dims& d, const void* x, const float* gate_w, const float* bias,
                        float* logits, hipStream_t st) {
-  MOE_HIP(launch_gemm_simt(d.bf16, EPI_F32_BIAS, x, d.T, gate_w, nullptr, logits, nullptr, nullptr,
-                           1, d.E, d.H, bias, st));
+  if (d.bf16) {
+    MOE_HIP(launch_gate_bf16(static_cast<const uint16_t*>(x), gate_w, bias, logits, d.T, d.E, d.H, st));
+  } else {
+    MOE_HIP(launch_gemm_simt(false, EPI_F32_BIAS, x, d.T, gate_w, nullptr, logits, nullptr, nullptr,
+                             1, d.E, d.H, bias, st));
+  }
   return MOE_OK;
 }
 

@@ -7,7 +7,11 @@
 namespace moe {
 
 constexpr int kWave = 64;
-constexpr int kBlockTok = 64;   // tokens per ranking block (one bit per token in a 64-bit mask)
+// Tokens per ranking block (one bit per token in a 64-bit mask): 64, or 16 for
+// small token counts so the top-k kernel runs one token per wave on more CUs.
+constexpr int kBlockTokLarge = 64;
+constexpr int kBlockTokSmall = 16;
+__host__ __device__ __forceinline__ int block_tokens(int T) { return T <= 2048 ? kBlockTokSmall : kBlockTokLarge; }
 constexpr int kMaxE = 1024;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -47,6 +51,37 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+// Wave-wide unsigned max / min with DPP row operations (butterfly inside each row
+// of 16 lanes: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror), then the four row results through readlane.  Every lane must be
+// active.  The result is wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));
+  v = min(v, dpp_u32<0x4E>(v));
+  v = min(v, dpp_u32<0x141>(v));
+  v = min(v, dpp_u32<0x140>(v));
+  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
+  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
+  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
+  return min(min(a, b), min(c, d));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {

@@ -16,33 +16,40 @@
 
 namespace moe {
 
-constexpr int kPermTokPerWg = 16;  // 4 waves x 4 tokens
 constexpr int kCopyUnroll = 4;
 
-// x / x_perm are addressed in 16-byte units; a row is row16 units.
-__global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x, int row16,
+// Workgroup (blockIdx.x, blockIdx.y): 4 waves x tpw tokens starting at
+// blockIdx.x * 4 * tpw, columns [c0, c1) of their rows (16-byte units; the
+// column split lets small token counts still fill the GPU).  Only the
+// blockIdx.y == 0 workgroups write the metadata.  x / x_perm rows are row16
+// 16-byte units long.
+__global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int row16,
                                                  const int32_t* __restrict__ topk_ids, int T,
-                                                 int E, int k,
+                                                 int E, int k, int tpw,
                                                  const int32_t* __restrict__ bases,
-                                                 uint4* __restrict__ x_perm,
+                                                 u32x4* __restrict__ x_perm,
                                                  int32_t* __restrict__ row_token,
                                                  int32_t* __restrict__ token_row) {
   __shared__ unsigned long long mask[kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok0 = blockIdx.x * kPermTokPerWg;
-  const int blk = tok0 / kBlockTok;
-  const int bt0 = blk * kBlockTok;
+  const int tok0 = blockIdx.x * 4 * tpw;
+  const int btok = block_tokens(T);
+  const int blk = tok0 / btok;
+  const int bt0 = blk * btok;
+  const int c0 = (int)((long)row16 * blockIdx.y / gridDim.y);
+  const int c1 = (int)((long)row16 * (blockIdx.y + 1) / gridDim.y);
+  const bool meta = blockIdx.y == 0;
   for (int e = tid; e < E; e += 256) mask[e] = 0ull;
   __syncthreads();
-  const int nblk = min(kBlockTok, T - bt0) * k;
+  const int nblk = min(btok, T - bt0) * k;
   for (int a = tid; a < nblk; a += 256) {
     const int tl = a / k;
     atomicOr(&mask[topk_ids[(size_t)bt0 * k + a]], 1ull << tl);
   }
   __syncthreads();
 
-  for (int i = 0; i < kPermTokPerWg / 4; ++i) {
-    const int t = tok0 + wave * (kPermTokPerWg / 4) + i;
+  for (int i = 0; i < tpw; ++i) {
+    const int t = tok0 + wave * tpw + i;
     if (t >= T) break;
     int row = 0;
     if (lane < k) {
@@ -50,24 +57,26 @@ __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x, in
       const int tl = t - bt0;
       const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
       row = bases[(size_t)blk * E + e] + rank;
-      token_row[(size_t)t * k + lane] = row;
-      row_token[row] = t;
+      if (meta) {
+        token_row[(size_t)t * k + lane] = row;
+        row_token[row] = t;
+      }
     }
-    const uint4* src = x + (size_t)t * row16;
-    for (int c0 = 0; c0 < row16; c0 += kWave * kCopyUnroll) {
-      uint4 v[kCopyUnroll];
+    const u32x4* src = x + (size_t)t * row16;
+    for (int cb = c0; cb < c1; cb += kWave * kCopyUnroll) {
+      u32x4 v[kCopyUnroll];
 #pragma unroll
       for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = c0 + u * kWave + lane;
-        if (c < row16) v[u] = src[c];
+        const int c = cb + u * kWave + lane;
+        if (c < c1) v[u] = src[c];
       }
       for (int j = 0; j < k; ++j) {
         const int r = __shfl(row, j, kWave);
-        uint4* dst = x_perm + (size_t)r * row16;
+        u32x4* dst = x_perm + (size_t)r * row16;
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
-          const int c = c0 + u * kWave + lane;
-          if (c < row16) dst[c] = v[u];
+          const int c = cb + u * kWave + lane;
+          if (c < c1) dst[c] = v[u];
         }
       }
     }
@@ -77,9 +86,14 @@ __global__ __launch_bounds__(256) void k_permute(const uint4* __restrict__ x, in
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
                           const int32_t* bases, void* x_perm, int32_t* row_token,
                           int32_t* token_row, hipStream_t st) {
-  hipLaunchKernelGGL(k_permute, dim3(ceil_div(T, kPermTokPerWg)), dim3(256), 0, st,
-                     static_cast<const uint4*>(x), row16, ids, T, E, k, bases,
-                     static_cast<uint4*>(x_perm), row_token, token_row);
+  // 4 tokens per wave for large T, 1 for small T (a workgroup's tokens always lie
+  // in one ranking block); split columns until ~1024 workgroups
+  const int tpw = T >= 4096 ? 4 : 1;
+  const int gx = ceil_div(T, 4 * tpw);
+  int cs = 1;
+  while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
+  hipLaunchKernelGGL(k_permute, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
+                     ids, T, E, k, tpw, bases, static_cast<u32x4*>(x_perm), row_token, token_row);
   return hipGetLastError();
 }
 

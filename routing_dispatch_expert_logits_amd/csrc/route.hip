@@ -14,11 +14,13 @@
 
 namespace moe {
 
-// One workgroup per 64-token ranking block: 16 waves x 4 tokens.  Each wave
-// holds one token's E scores as 64-bit keys (order_key(score) << 32 | ~expert),
-// so a plain max picks the larger score and, on equal scores, the lower expert
-// index.  k rounds of wave-max extract the top k in order.  Counts per expert
-// for the block are gathered in LDS (order-independent) and written to
+// One workgroup per ranking block of 16 * tpw tokens: 16 waves x tpw tokens
+// (tpw = 4 for 64-token blocks, 1 for 16-token blocks).  A wave holds
+// one token's E scores as order keys (order_key(score): larger score, larger
+// key).  Each of the k rounds takes the wave-wide largest key, then the lowest
+// expert index holding it (so equal scores go to the lower index), and removes
+// that entry; both reductions are DPP row butterflies plus readlane.  Counts per
+// expert for the block are gathered in LDS (order-independent) and written to
 // block_counts[block][e].
 template <int SLOTS>
 __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_in,
@@ -31,44 +33,66 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
 
-  for (int i = 0; i < 4; ++i) {
-    const int t = blockIdx.x * kBlockTok + wave * 4 + i;
-    if (t >= T) break;
-    const float* row = scores_in + (size_t)t * E;
-    uint64_t key[SLOTS];
+  // the scores of G tokens are loaded before their selection work starts
+  constexpr int G = SLOTS >= 16 ? 2 : 4;
+  const int tpw = block_tokens(T) / 16;
+  float bv[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const int e = lane + s * kWave;
-      if (e < E) {
-        float v = row[e];
-        if (bias) v = v + bias[e];
-        key[s] = (static_cast<uint64_t>(order_key(v)) << 32) | (0xffffffffu - static_cast<uint32_t>(e));
-      } else {
-        key[s] = 0;  // below every real key
+  for (int s = 0; s < SLOTS; ++s) {
+    const int e = lane + s * kWave;
+    bv[s] = (bias && e < E) ? bias[e] : 0.f;
+  }
+  for (int g0 = 0; g0 < tpw; g0 += G) {
+    const int tbase = blockIdx.x * 16 * tpw + wave * tpw + g0;
+    float sv[G][SLOTS];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int t = min(tbase + i, T - 1);
+      const float* row = scores_in + (size_t)t * E;
+#pragma unroll
+      for (int s = 0; s < SLOTS; ++s) {
+        const int e = lane + s * kWave;
+        sv[i][s] = e < E ? row[e] : 0.f;
       }
     }
-    int my_e = 0;
-    float my_s = 0.f, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
 #pragma unroll
-      for (int s = 1; s < SLOTS; ++s) best = key[s] > best ? key[s] : best;
-      best = wave_max_u64(best);
-      const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
-      const float sc = key_to_score(static_cast<uint32_t>(best >> 32));
-      if (j == 0) top = sc;
-      if (lane == j) { my_e = e; my_s = sc; }
+    for (int i = 0; i < G; ++i) {
+      const int t = tbase + i;
+      if (t >= T || g0 + i >= tpw) break;
+      uint32_t key[SLOTS];
 #pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        if (lane + s * kWave == e) key[s] = 0;
-    }
-    // Renormalised softmax over the selected k: the full-E denominator cancels.
-    const float ex = lane < k ? expf(my_s - top) : 0.f;
-    const float sum = wave_sum_f32(ex);
-    if (lane < k) {
-      topk_ids[(size_t)t * k + lane] = my_e;
-      topk_w[(size_t)t * k + lane] = ex / sum;
-      atomicAdd(&cnt[my_e], 1);
+      for (int s = 0; s < SLOTS; ++s) {
+        const int e = lane + s * kWave;
+        const float v = bias ? sv[i][s] + bv[s] : sv[i][s];
+        key[s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
+      }
+      int my_e = 0;
+      float my_s = 0.f, top = 0.f;
+      for (int j = 0; j < k; ++j) {
+        uint32_t lm = key[0];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
+        const uint32_t best = wave_max_u32(lm);
+        uint32_t li = 0xffffffffu;
+#pragma unroll
+        for (int s = SLOTS - 1; s >= 0; --s)
+          if (key[s] == best) li = static_cast<uint32_t>(lane + s * kWave);
+        const int e = static_cast<int>(wave_min_u32(li));
+        const float sc = key_to_score(best);
+        if (j == 0) top = sc;
+        if (lane == j) { my_e = e; my_s = sc; }
+#pragma unroll
+        for (int s = 0; s < SLOTS; ++s)
+          if (lane + s * kWave == e) key[s] = 0u;
+      }
+      // Renormalised softmax over the selected k: the full-E denominator cancels.
+      const float ex = lane < k ? expf(my_s - top) : 0.f;
+      const float sum = wave_sum_f32(ex);
+      if (lane < k) {
+        topk_ids[(size_t)t * k + lane] = my_e;
+        topk_w[(size_t)t * k + lane] = ex / sum;
+        atomicAdd(&cnt[my_e], 1);
+      }
     }
   }
   __syncthreads();
@@ -83,8 +107,9 @@ __global__ __launch_bounds__(256) void k_block_counts(const int32_t* __restrict_
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 256) cnt[e] = 0;
   __syncthreads();
-  const int t0 = blockIdx.x * kBlockTok;
-  const int n = min(kBlockTok, T - t0) * k;
+  const int bt = block_tokens(T);
+  const int t0 = blockIdx.x * bt;
+  const int n = min(bt, T - t0) * k;
   for (int a = tid; a < n; a += 256) atomicAdd(&cnt[topk_ids[(size_t)t0 * k + a]], 1);
   __syncthreads();
   for (int e = tid; e < E; e += 256) block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
@@ -115,27 +140,45 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem
 //   offsets_in  non-NULL: use these segment starts (moe_dispatch_permute);
 //               NULL: write counts_out / offsets_out from the block counts.
 //   bm > 0: mtile_start[e] = sum_{e' < e} ceil(count_e' / bm), mtile_start[E] = total.
+// Thread t works on expert t % E and on the P = 1024 / E contiguous block ranges
+// of part t / E, so the column sums and the per-block prefix run P-wide.
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_counts, int nb, int E,
                                                const int32_t* __restrict__ offsets_in,
                                                int32_t* __restrict__ counts_out,
                                                int32_t* __restrict__ offsets_out, int bm,
                                                int32_t* __restrict__ mtile_start) {
   __shared__ int smem[48];
-  const int e = threadIdx.x;
+  __shared__ int psum[1024];
+  __shared__ int off_s[kMaxE];
+  const int t = threadIdx.x;
+  const int P = 1024 / E;
+  const int e = t % E, p = t / E;
+  const bool active = p < P;
+  const int b0 = active ? (int)((long)nb * p / P) : 0;
+  const int b1 = active ? (int)((long)nb * (p + 1) / P) : 0;
+  int part = 0;
+  for (int b = b0; b < b1; ++b) part += block_counts[(size_t)b * E + e];
+  if (active) psum[p * E + e] = part;
+  __syncthreads();
   int c = 0;
-  if (e < E)
-    for (int b = 0; b < nb; ++b) c += block_counts[(size_t)b * E + e];
+  if (t < E)
+    for (int q = 0; q < P; ++q) c += psum[q * E + t];
   int total = 0;
-  int off = block_exclusive_scan(e < E ? c : 0, &total, smem);
-  if (offsets_in && e < E) off = offsets_in[e];
-  if (e < E) {
-    if (counts_out) counts_out[e] = c;
+  int off = block_exclusive_scan(t < E ? c : 0, &total, smem);
+  if (t < E) {
+    if (offsets_in) off = offsets_in[t];
+    off_s[t] = off;
+    if (counts_out) counts_out[t] = c;
     if (offsets_out) {
-      offsets_out[e] = off;
-      if (e == E - 1) offsets_out[E] = off + c;
+      offsets_out[t] = off;
+      if (t == E - 1) offsets_out[E] = off + c;
     }
-    int run = off;
-    for (int b = 0; b < nb; ++b) {
+  }
+  __syncthreads();
+  if (active) {
+    int run = off_s[e];
+    for (int q = 0; q < p; ++q) run += psum[q * E + e];
+    for (int b = b0; b < b1; ++b) {
       const size_t i = (size_t)b * E + e;
       const int v = block_counts[i];
       block_counts[i] = run;
@@ -143,11 +186,11 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
     }
   }
   if (bm > 0) {
-    const int mt = e < E ? ceil_div(c, bm) : 0;
+    const int mt = t < E ? ceil_div(c, bm) : 0;
     int tot = 0;
     const int st = block_exclusive_scan(mt, &tot, smem);
-    if (e < E) mtile_start[e] = st;
-    if (e == E - 1) mtile_start[E] = st + mt;
+    if (t < E) mtile_start[t] = st;
+    if (t == E - 1) mtile_start[E] = st + mt;
   }
 }
 
@@ -167,7 +210,7 @@ __global__ __launch_bounds__(1024) void k_mtiles(const int32_t* __restrict__ off
 
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
                        float* w, int32_t* block_counts, hipStream_t st) {
-  const int nb = ceil_div(T, kBlockTok);
+  const int nb = ceil_div(T, block_tokens(T));
   const int slots = ceil_div(E, kWave);
   dim3 g(nb), b(1024);
   if (slots <= 1) hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
@@ -180,7 +223,7 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
 
 hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t* block_counts,
                                hipStream_t st) {
-  hipLaunchKernelGGL(k_block_counts, dim3(ceil_div(T, kBlockTok)), dim3(256), 0, st, ids, T, E, k,
+  hipLaunchKernelGGL(k_block_counts, dim3(ceil_div(T, block_tokens(T))), dim3(256), 0, st, ids, T, E, k,
                      block_counts);
   return hipGetLastError();
 }

@@ -426,3 +426,16 @@ def test_pins_catch_planted_mistakes():
     s = np.array([[1.0, 1.0, 0.0]], dtype=np.float32)
     assert oracle.topk_ids(s, 1)[0, 0] == 0
     assert np.argsort(-s[0], kind="stable")[0] == 0 and np.argsort(s[0])[::-1][0] != 0
+
+
+def test_token_outputs_match_whole_layer():
+    """The sampled-token evaluation (full-size layers) equals the whole-layer oracle's rows."""
+    for name in ("small_bf16_zipf", "small_latent"):
+        cfg = PARITY_CONFIGS[name]
+        inp = gen.layer_inputs(cfg)
+        ref = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True)
+        tok = np.array([0, 3, 7, 11, cfg.T - 1])
+        ew = {e: (inp["w1"][e], inp["w3"][e], inp["w2"][e]) for e in range(cfg.E)}
+        z = ref["z"][tok] if cfg.L else None
+        got = oracle.token_outputs(inp, tok, ref["ids"][tok], ref["weights"][tok], ew, bf16=True, z=z)
+        np.testing.assert_allclose(got, ref["out"][tok], rtol=1e-12, atol=1e-14)
