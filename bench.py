@@ -127,7 +127,58 @@ def cpu_baseline(cfg, inp, target_s):
                       f"weights), float64 numpy oracle, {dt:.2f} s"}
 
 
+DOMINANT_KERNEL_PATTERNS = ("k_gemm_prefill<128, 128, 2,", "k_gemm_ws<128, 128, 2,", "k_gemm_decode<2, 2,")
+
+
+def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cmd):
+    """HBM bytes per launch of the expert gate/up GEMM from two rocprofv3 --pmc runs.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same
+    counter reads for the 1 GiB calibration copy (a plain device copy of known
+    size in the same run), then averaged over the GEMM's dispatches.
+    """
+    import csv
+
+    def rows(path, counter):
+        out = []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return out
+
+    copy_bytes = copy_mib << 20
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rs = rows(path, counter)
+        copies = [v for n, v in rs if "copyBuffer" in n]
+        big = max(copies)
+        cal = [v for v in copies if v > 0.9 * big]
+        scale = copy_bytes / (1024.0 * sum(cal) / len(cal))
+        gemm = [v for n, v in rs if any(p in n for p in DOMINANT_KERNEL_PATTERNS)]
+        kname = next(n for n, v in rs if any(p in n for p in DOMINANT_KERNEL_PATTERNS))
+        res[counter] = {"kib_per_launch": sum(gemm) / len(gemm), "launches": len(gemm),
+                        "copy_kib": sum(cal) / len(cal), "scale": scale, "kernel": kname.split("(")[0]}
+    hbm = (res["FETCH_SIZE"]["kib_per_launch"] * 1024 * res["FETCH_SIZE"]["scale"] +
+           res["WRITE_SIZE"]["kib_per_launch"] * 1024 * res["WRITE_SIZE"]["scale"])
+    out = {"config": config, "kernel": res["FETCH_SIZE"]["kernel"],
+           "gemm_src_sha256_16": src_hash(GEMM_SRC),
+           "hbm_bytes_per_launch": int(hbm),
+           "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+           "copy_calibration_bytes": copy_bytes,
+           "commands": [fetch_cmd, write_cmd]}
+    path = TRAFFIC_FILE.format(config=config)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
+    if argv is None:
+        argv = sys.argv[1:]
+    if argv and argv[0] == "--traffic-from":
+        # python bench.py --traffic-from FETCH.csv WRITE.csv CONFIG COPY_MIB "fetch cmd" "write cmd"
+        traffic_from_pmc(argv[1], argv[2], argv[3], int(argv[4]), argv[5], argv[6])
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
