@@ -201,8 +201,8 @@ __global__ __launch_bounds__(256, MINW) void k_gemm_prefill(
 }
 
 // ------------------------------------------------------------------ bf16 pipelined kernel
-// Wave-specialised variant of the tile kernel: 4 MFMA waves (2 x 2, 64 x 64
-// each) and 2 loader waves per workgroup.  The loader waves copy each K-step's
+// Wave-specialised variant of the tile kernel: MW MFMA waves (4: 2 x 2 of 64 x 64,
+// or 8: 2 x 4 of 64 x 32, two per SIMD) and 2 loader waves per workgroup.  The loader waves copy each K-step's
 // A and B tiles straight from global memory into an S-stage LDS ring with
 // global_load_lds_dwordx4 (no register staging) and run up to two stages
 // ahead; the MFMA waves only read LDS.  One barrier per K-step hands stage s
@@ -230,14 +230,17 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 static_assert(waitcnt_vm(24) == 0x4F78 && waitcnt_vm(0) == 0x0F70, "s_waitcnt encoding");
 
-template <int BM, int BN, int NB, int EPI, int S>
-__global__ __launch_bounds__(384) void k_gemm_ws(
+template <int BM, int BN, int NB, int EPI, int S, int MW = 4>
+__global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_start, int E, int N, int K) {
-  static_assert(BM == 128 && BN == 128, "4 MFMA waves of 64 x 64");
-  static_assert(S == 3 || S == 4, "3- or 4-stage ring");
-  constexpr int TM = 64, TN = 64, FM = 4, FN = 4;
+  static_assert((BM == 128 || BM == 256) && BN == 128, "tile 128 x 128 or 256 x 128");
+  static_assert(S >= 2 && S <= 4, "2- to 4-stage ring");
+  constexpr int WM = BM / 64;                     // MFMA waves along M (64 rows each)
+  constexpr int WN = MW / WM;                     // MFMA waves along N
+  static_assert(WM * WN == MW && WN >= 1, "wave grid");
+  constexpr int TM = 64, TN = BN / WN, FM = 4, FN = TN / 16;
   constexpr int A_ELEMS = BM * 64, B_ELEMS = BN * 64;
   constexpr int STAGE = A_ELEMS + NB * B_ELEMS;   // bf16 elements per stage
   constexpr int NQ = (BM + NB * BN) / 8;          // DMA instructions per stage
@@ -249,23 +252,27 @@ __global__ __launch_bounds__(384) void k_gemm_ws(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = K / 64;
 
-  if (wave >= 4) {
+  if (wave >= MW) {
     // ---------------- loader waves
-    const int p = wave - 4;
+    const int p = wave - MW;
     const uint16_t* src[NQP];
     int ldsoff[NQP];
+    constexpr int QA = BM / 8, QB = BN / 8;       // DMA instructions per A / B tile
 #pragma unroll
     for (int j = 0; j < NQP; ++j) {
       const int q = p * NQP + j;       // instruction index within the stage
-      const int r = (q % 16) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      if (q < 16) {                    // A tile rows
+      if (q < QA) {                    // A tile rows 8q .. 8q+7
+        const int r = q * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
         src[j] = A + (size_t)(tc.row0 + min(r, tc.rows - 1)) * K + c * 8;
-        ldsoff[j] = (q % 16) * 512;
-      } else {
-        const uint16_t* Bm = (q < 32) ? B0 : B1;
+        ldsoff[j] = q * 512;
+      } else {                         // B tile nb, rows 8qq .. 8qq+7
+        const int nb = (q - QA) / QB, qq = (q - QA) % QB;
+        const int r = qq * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const uint16_t* Bm = nb == 0 ? B0 : B1;
         src[j] = Bm + ((size_t)tc.e * N + min(tc.n0 + r, N - 1)) * K + c * 8;
-        ldsoff[j] = A_ELEMS + (q / 16 - 1) * B_ELEMS + (q % 16) * 512;
+        ldsoff[j] = A_ELEMS + nb * B_ELEMS + qq * 512;
       }
     }
     auto issue = [&](int st) {
@@ -298,7 +305,7 @@ __global__ __launch_bounds__(384) void k_gemm_ws(
   }
 
   // ---------------- MFMA waves
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   f32x4 acc[NB][FM][FN];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -322,8 +329,14 @@ __global__ __launch_bounds__(384) void k_gemm_ws(
       boffs[h][fn] = A_ELEMS + r * 64 + ((c ^ swz(r)) << 3);
     }
   }
+  // a wave whose 64 rows all lie past the tile's valid rows only keeps the barrier cadence
+  const bool active = wm * TM < tc.rows;
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
+    if (!active) {
+      __syncthreads();
+      continue;
+    }
     const uint16_t* base = lds + (s % S) * STAGE;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -555,35 +568,59 @@ int max_mtiles(int M, int E, int bm) {
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st) {
-  const int bm = gemm_bm(kind);
-  const int mt = offsets ? max_mtiles(M, E, bm) : ceil_div(M, bm);
+  const bool swiglu = epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_F32;
   if (kind == GEMM_PREFILL) {
-    const int g = grid_for(mt, N, 128);
-    // Measured on MI355X (expert GEMMs of the Qwen3-30B-A3B- and DeepSeek-R1-shaped
-    // layers): for the gate/up pair with a long K the wave-specialised LDS-DMA kernel
-    // is ~8% faster; otherwise the register-staged tile kernel at two workgroups per
-    // CU wins.
-    const bool pipelined = (epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_F32) && K >= 4096;
-    if (pipelined) {
-      const dim3 gb(g), bb(384);
-      if (epi == EPI_SWIGLU_BF16)
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3>), gb, bb, 0, st, A, M, B0, B1, C,
+    // Kernel per GEMM, measured on MI355X with the real per-expert row counts of the
+    // Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped and latent layers (one box, one run):
+    //  - expert gate/up: wave-specialised LDS-DMA kernel, 128 x 128 tiles, 8 MFMA
+    //    waves (best or within 1 % on all three);
+    //  - expert down: register-staged tile kernel at three waves per SIMD, or (K >= 2048,
+    //    measured in the whole layer) the wave-specialised kernel with 256 x 128 tiles;
+    //  - dense latent projections (one group): wave-specialised kernel with
+    //    256 x 128 tiles (one tile row per 256 tokens fills 256 CUs in one pass).
+    if (!offsets) {
+      const dim3 g(grid_for(ceil_div(M, 256), N, 128)), b(8 * 64 + 128);
+      if (epi == EPI_BF16)
+        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
+                           offsets, mtile_start, E, N, K);
+      else if (epi == EPI_F32)
+        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
                            offsets, mtile_start, E, N, K);
       else
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3>), gb, bb, 0, st, A, M, B0, B1, C,
-                           offsets, mtile_start, E, N, K);
+        return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+    const int g = grid_for(max_mtiles(M, E, 128), N, 128);
+    if (swiglu) {
+      const dim3 gb(g), bb(8 * 64 + 128);
+      if (epi == EPI_SWIGLU_BF16)
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), gb, bb, 0, st, A, M, B0,
+                           B1, C, offsets, mtile_start, E, N, K);
+      else
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), gb, bb, 0, st, A, M, B0,
+                           B1, C, offsets, mtile_start, E, N, K);
+      return hipGetLastError();
+    }
+    if (K >= 2048) {  // down GEMM with a long K: 256-row tiles (second m-tile table)
+      const dim3 gb(grid_for(max_mtiles(M, E, 256), N, 128)), bb(8 * 64 + 128);
+      const int32_t* mt256 = mtile_start + E + 1;
+      if (epi == EPI_BF16)
+        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
+                           offsets, mt256, E, N, K);
+      else if (epi == EPI_F32)
+        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
+                           offsets, mt256, E, N, K);
+      else
+        return hipErrorInvalidValue;
       return hipGetLastError();
     }
     switch (epi) {
-      // two workgroups per CU: one hides the other's barrier and load waits
-      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_BF16, 2>), g); break;
-      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 2, EPI_SWIGLU_F32, 2>), g); break;
-      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16, 2>), g); break;
-      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32, 2>), g); break;
+      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16, 3>), g); break;
+      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32, 3>), g); break;
       default: return hipErrorInvalidValue;
     }
   } else {
-    const int g = grid_for(mt, N, 4 * 16 * 2);
+    const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
     switch (epi) {
       case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), g); break;
       case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_F32>), g); break;

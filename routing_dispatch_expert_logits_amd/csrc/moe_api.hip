@@ -75,7 +75,7 @@ RouteWs route_ws(const Dims& d) {
 struct FfnWs { size_t mtile, act, total; };
 FfnWs ffn_ws(const Dims& d) {
   Carve c; FfnWs w;
-  w.mtile = c.take((size_t)(d.E + 1) * 4);
+  w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
   w.act = c.take((size_t)d.R * d.I * d.es);
   w.total = c.cur;
   return w;
@@ -102,7 +102,7 @@ LayerWs layer_ws(const Dims& d) {
   w.row_token = c.take((size_t)d.R * 4);
   w.token_row = c.take((size_t)d.R * 4);
   w.bc = c.take((size_t)d.nb * d.E * 4);
-  w.mtile = c.take((size_t)(d.E + 1) * 4);
+  w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
   w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
   w.act = c.take((size_t)d.R * d.I * d.es);

@@ -40,6 +40,8 @@ hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, 
 hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
                                   int T, int k, void* out, bool out_f32, hipStream_t st);
 // bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.
+// mtile_start holds the m-tile tables for tile heights gemm_bm(kind) and 2 * gemm_bm(kind)
+// (E + 1 entries each, as written by launch_scan / launch_mtiles).
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st);

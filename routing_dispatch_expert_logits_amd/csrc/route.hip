@@ -139,7 +139,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem
 //                      out: first row of block b's assignments to e.
 //   offsets_in  non-NULL: use these segment starts (moe_dispatch_permute);
 //               NULL: write counts_out / offsets_out from the block counts.
-//   bm > 0: mtile_start[e] = sum_{e' < e} ceil(count_e' / bm), mtile_start[E] = total.
+//   bm > 0: GEMM m-tile tables for two tile heights, bm and 2 bm:
+//           mtile_start[e] = sum_{e' < e} ceil(count_e' / bm), mtile_start[E] = total,
+//           and the same for 2 bm at mtile_start[E + 1 + e].
 // Thread t works on expert t % E and on the P = 1024 / E contiguous block ranges
 // of part t / E, so the column sums and the per-block prefix run P-wide.
 __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_counts, int nb, int E,
@@ -186,24 +188,34 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
     }
   }
   if (bm > 0) {
-    const int mt = t < E ? ceil_div(c, bm) : 0;
-    int tot = 0;
-    const int st = block_exclusive_scan(mt, &tot, smem);
-    if (t < E) mtile_start[t] = st;
-    if (t == E - 1) mtile_start[E] = st + mt;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mt = t < E ? ceil_div(c, bm << h) : 0;
+      int tot = 0;
+      const int st = block_exclusive_scan(mt, &tot, smem);
+      int32_t* tab = mtile_start + h * (E + 1);
+      if (t < E) tab[t] = st;
+      if (t == E - 1) tab[E] = st + mt;
+    }
   }
 }
 
-// m-tile table from given offsets (moe_grouped_ffn on its own).
+// m-tile tables (tile heights bm and 2 bm, as in k_scan) from given offsets
+// (moe_grouped_ffn on its own).
 __global__ __launch_bounds__(1024) void k_mtiles(const int32_t* __restrict__ offsets, int E, int bm,
                                                  int32_t* __restrict__ mtile_start) {
   __shared__ int smem[48];
   const int e = threadIdx.x;
-  const int mt = e < E ? ceil_div(offsets[e + 1] - offsets[e], bm) : 0;
-  int tot = 0;
-  const int st = block_exclusive_scan(mt, &tot, smem);
-  if (e < E) mtile_start[e] = st;
-  if (e == E - 1) mtile_start[E] = st + mt;
+  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int mt = e < E ? ceil_div(c, bm << h) : 0;
+    int tot = 0;
+    const int st = block_exclusive_scan(mt, &tot, smem);
+    int32_t* tab = mtile_start + h * (E + 1);
+    if (e < E) tab[e] = st;
+    if (e == E - 1) tab[E] = st + mt;
+  }
 }
 
 // ------------------------------------------------------------------ launchers
