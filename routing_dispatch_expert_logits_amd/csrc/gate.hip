@@ -27,12 +27,15 @@ __device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uin
   lo = f32_to_bf16(r1 - bf16_to_f32(mid));
 }
 
+// blockIdx.y selects a K slice [y * Hs, (y + 1) * Hs) (split-K).  With one slice the
+// result plus bias goes to logits; with several, slice y writes its fp32 partial to
+// logits + y * T * E and k_gate_reduce adds the slices in a fixed order.
 template <int BM>
 __global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restrict__ X,
                                                        const float* __restrict__ Wg,
                                                        const float* __restrict__ bias,
                                                        float* __restrict__ logits, int T, int E,
-                                                       int H) {
+                                                       int H, int Hs) {
   constexpr int BN = kGBN, TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
   constexpr int A_PER = BM * 8 / 256;   // 16-byte bf16 chunks of the X tile per thread
   constexpr int B_PER = BN * 16 / 256;  // 16-byte fp32 chunks of the Wg tile per thread
@@ -42,6 +45,13 @@ __global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restric
 
   const int NT = ceil_div(E, BN);
   const int m0 = (blockIdx.x / NT) * BM, n0 = (blockIdx.x % NT) * BN;
+  const int kbeg = blockIdx.y * Hs;
+  X += kbeg;
+  Wg += kbeg;
+  if (gridDim.y > 1) {
+    logits += (size_t)blockIdx.y * T * E;
+    bias = nullptr;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -76,7 +86,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restric
   };
   load(0);
   const int ar = wm * TM + (lane & 15), br = wn * TN + (lane & 15), kofs = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < H; k0 += kGBK) {
+  for (int k0 = 0; k0 < Hs; k0 += kGBK) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < A_PER; ++i)
@@ -92,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restric
       *reinterpret_cast<uint2*>(&sB[2][o]) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
     }
     __syncthreads();
-    load(min(k0 + kGBK, H - kGBK));
+    load(min(k0 + kGBK, Hs - kGBK));
 #pragma unroll
     for (int ks = 0; ks < kGBK; ks += 32) {
       bf16x8 af[FM];
@@ -127,17 +137,42 @@ __global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restric
       }
 }
 
-hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
-                            int T, int E, int H, hipStream_t st) {
+// logits[t, e] = sum_{s < S} part[s][t][e] (+ bias[e]), summed in ascending s.
+__global__ __launch_bounds__(256) void k_gate_reduce(const float* __restrict__ part, int S,
+                                                     const float* __restrict__ bias,
+                                                     float* __restrict__ logits, int T, int E) {
+  const size_t n = (size_t)T * E;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = part[i];
+  for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
+  if (bias) v += bias[i % E];
+  logits[i] = v;
+}
+
+int gate_splits(int T, int E, int H) {
   const int NT = ceil_div(E, kGBN);
-  // largest row tile that still gives at least 256 workgroups
-  int bm = 32;
-  if (ceil_div(T, 128) * NT >= 256) bm = 128;
-  else if (ceil_div(T, 64) * NT >= 256) bm = 64;
-  const dim3 g(ceil_div(T, bm) * NT), b(256);
-  if (bm == 128) hipLaunchKernelGGL(k_gate_split<128>, g, b, 0, st, x, gate_w, bias, logits, T, E, H);
-  else if (bm == 64) hipLaunchKernelGGL(k_gate_split<64>, g, b, 0, st, x, gate_w, bias, logits, T, E, H);
-  else hipLaunchKernelGGL(k_gate_split<32>, g, b, 0, st, x, gate_w, bias, logits, T, E, H);
+  const int tiles = ceil_div(T, 64) * NT;
+  int s = 1;
+  while (tiles * s < 1024 && s < 8 && H % (64 * s * 2) == 0) s *= 2;
+  return s;
+}
+
+hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
+                            float* partial, int T, int E, int H, hipStream_t st) {
+  const int NT = ceil_div(E, kGBN);
+  // 64-row tiles; the K range is split until there are ~1024 workgroups (each K slice
+  // a multiple of 64), so every workgroup runs a short K loop
+  const int S = gate_splits(T, E, H);
+  const int Hs = H / S;
+  const dim3 g(ceil_div(T, 64) * NT, S), b(256);
+  hipLaunchKernelGGL(k_gate_split<64>, g, b, 0, st, x, gate_w, bias, S > 1 ? partial : logits, T, E,
+                     H, Hs);
+  if (S > 1) {
+    const size_t n = (size_t)T * E;
+    hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial, S,
+                       bias, logits, T, E);
+  }
   return hipGetLastError();
 }
 

@@ -201,23 +201,28 @@ __global__ __launch_bounds__(256, MINW) void k_gemm_prefill(
 }
 
 // ------------------------------------------------------------------ bf16 pipelined kernel
-// Wave-specialised variant of the tile kernel: MW MFMA waves (4: 2 x 2 of 64 x 64,
-// or 8: 2 x 4 of 64 x 32, two per SIMD) and 2 loader waves per workgroup.  The loader waves copy each K-step's
-// A and B tiles straight from global memory into an S-stage LDS ring with
-// global_load_lds_dwordx4 (no register staging) and run up to two stages
-// ahead; the MFMA waves only read LDS.  One barrier per K-step hands stage s
-// to the MFMA waves and the freed stage back to the loaders.  Because only the
-// loader waves issue the LDS DMA, the MFMA waves' LDS reads never wait for
+// Wave-specialised variant of the tile kernel: MW MFMA waves (64 x TN tiles, two
+// per SIMD when MW = 8) and 2 loader waves per workgroup.  The loader waves copy
+// each K-step's A and B tiles straight from global memory into an S-stage LDS
+// ring with global_load_lds_dwordx4 (no register staging) and run up to S-1
+// stages ahead; the MFMA waves only read LDS.  One barrier per K-step hands a
+// stage to the MFMA waves and the freed stage back to the loaders.  Because only
+// the loader waves issue the LDS DMA, the MFMA waves' LDS reads never wait for
 // loads of later stages.
 //
-// LDS layout: a tile is rows of 64 bf16 (8 16-byte chunks); chunk c of row r is
-// stored at chunk slot c ^ (r & 7).  Measured on gfx950, ds_read_b128 of 16
-// consecutive rows at one chunk index runs at full LDS rate with this XOR
-// (about 200 B/clk/CU), while unswizzled 128-byte rows run at a quarter and
-// 144-byte padded rows at half of it.  A DMA instruction fills 8 consecutive
-// rows (lane i -> row 8q + i/8, slot i % 8).
+// LDS layout: a tile is rows of BK bf16 in 16-byte chunks; chunk c of row r sits
+// at chunk slot c ^ swz(r).  Measured on gfx950 (ds_read_b128 of the 16 rows one
+// MFMA operand touches, at one chunk index): 128-byte rows (BK = 64) run at full
+// LDS rate (~200 B/clk/CU) with swz(r) = r & 7, 64-byte rows (BK = 32) with
+// swz(r) = (r >> 1) & 3; unswizzled rows run at a half or a quarter of that.  A
+// DMA instruction fills 1 KB: 64 / (BK / 8) consecutive rows (lane i -> row
+// i / (BK / 8), slot i % (BK / 8)).
 
-__device__ __forceinline__ int swz(int r) { return r & 7; }
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64) return r & 7;
+  else return (r >> 1) & 3;
+}
 
 // The LDS-DMA builtin takes a global-address-space source and an LDS
 // destination; spelling both casts out keeps the host compilation pass of the
@@ -230,46 +235,49 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 static_assert(waitcnt_vm(24) == 0x4F78 && waitcnt_vm(0) == 0x0F70, "s_waitcnt encoding");
 
-template <int BM, int BN, int NB, int EPI, int S, int MW = 4>
+template <int BM, int BN, int NB, int EPI, int S, int MW = 4, int BK = 64>
 __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_start, int E, int N, int K) {
   static_assert((BM == 128 || BM == 256) && BN == 128, "tile 128 x 128 or 256 x 128");
-  static_assert(S >= 2 && S <= 4, "2- to 4-stage ring");
+  static_assert(BK == 32 || BK == 64, "K-step 32 or 64");
   constexpr int WM = BM / 64;                     // MFMA waves along M (64 rows each)
   constexpr int WN = MW / WM;                     // MFMA waves along N
   static_assert(WM * WN == MW && WN >= 1, "wave grid");
   constexpr int TM = 64, TN = BN / WN, FM = 4, FN = TN / 16;
-  constexpr int A_ELEMS = BM * 64, B_ELEMS = BN * 64;
+  constexpr int CH = BK / 8;                      // 16-byte chunks per LDS row
+  constexpr int RPQ = 64 / CH;                    // rows per DMA instruction
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
   constexpr int STAGE = A_ELEMS + NB * B_ELEMS;   // bf16 elements per stage
-  constexpr int NQ = (BM + NB * BN) / 8;          // DMA instructions per stage
+  constexpr int QA = BM / RPQ, QB = BN / RPQ;     // DMA instructions per A / B tile
+  constexpr int NQ = QA + NB * QB;                // DMA instructions per stage
   constexpr int NQP = NQ / 2;                     // per loader wave
+  static_assert(S >= 2 && S <= 6 && (S - 2) * NQP <= 63, "outstanding loads fit vmcnt");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
 
   TileCoord tc;
   if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nsteps = K / 64;
+  const int nsteps = K / BK;
 
   if (wave >= MW) {
     // ---------------- loader waves
     const int p = wave - MW;
     const uint16_t* src[NQP];
     int ldsoff[NQP];
-    constexpr int QA = BM / 8, QB = BN / 8;       // DMA instructions per A / B tile
 #pragma unroll
     for (int j = 0; j < NQP; ++j) {
       const int q = p * NQP + j;       // instruction index within the stage
-      if (q < QA) {                    // A tile rows 8q .. 8q+7
-        const int r = q * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+      if (q < QA) {                    // A tile rows RPQ*q ..
+        const int r = q * RPQ + lane / CH;
+        const int c = (lane % CH) ^ swz<BK>(r);
         src[j] = A + (size_t)(tc.row0 + min(r, tc.rows - 1)) * K + c * 8;
         ldsoff[j] = q * 512;
-      } else {                         // B tile nb, rows 8qq .. 8qq+7
+      } else {                         // B tile nb, rows RPQ*qq ..
         const int nb = (q - QA) / QB, qq = (q - QA) % QB;
-        const int r = qq * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
+        const int r = qq * RPQ + lane / CH;
+        const int c = (lane % CH) ^ swz<BK>(r);
         const uint16_t* Bm = nb == 0 ? B0 : B1;
         src[j] = Bm + ((size_t)tc.e * N + min(tc.n0 + r, N - 1)) * K + c * 8;
         ldsoff[j] = A_ELEMS + nb * B_ELEMS + qq * 512;
@@ -279,13 +287,15 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
       const int base = (st % S) * STAGE;
 #pragma unroll
       for (int j = 0; j < NQP; ++j)
-        __builtin_amdgcn_global_load_lds((gas_ptr)(src[j] + st * 64), (las_ptr)&lds[base + ldsoff[j]],
+        __builtin_amdgcn_global_load_lds((gas_ptr)(src[j] + st * BK), (las_ptr)&lds[base + ldsoff[j]],
                                          16, 0, 0);
     };
     // Up to S-1 stages in flight.  wait_behind(n): the oldest outstanding stage has
     // landed once at most n later stages (n * NQP loads) are still in flight.
     auto wait_behind = [](int n) {
-      if (n >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NQP));
+      if (n >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NQP < 63 ? 4 * NQP : 63));
+      else if (n == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * NQP < 63 ? 3 * NQP : 63));
+      else if (n == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NQP < 63 ? 2 * NQP : 63));
       else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQP));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
@@ -314,19 +324,20 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) acc[nb][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
   // element offsets of this lane's operand chunks inside a stage, per 32-wide substep
-  int aoffs[2][FM], boffs[2][FN];
+  constexpr int NH = BK / 32;
+  int aoffs[NH][FM], boffs[NH][FN];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < NH; ++h) {
     const int c = h * 4 + (lane >> 4);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int r = wm * TM + fm * 16 + (lane & 15);
-      aoffs[h][fm] = r * 64 + ((c ^ swz(r)) << 3);
+      aoffs[h][fm] = r * BK + ((c ^ swz<BK>(r)) << 3);
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int r = wn * TN + fn * 16 + (lane & 15);
-      boffs[h][fn] = A_ELEMS + r * 64 + ((c ^ swz(r)) << 3);
+      boffs[h][fn] = A_ELEMS + r * BK + ((c ^ swz<BK>(r)) << 3);
     }
   }
   // a wave whose 64 rows all lie past the tile's valid rows only keeps the barrier cadence
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     }
     const uint16_t* base = lds + (s % S) * STAGE;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       bf16x8 af[FM];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)

@@ -64,10 +64,13 @@ GemmKind expert_kind(const Dims& d) {
   return (d.R >= 48 * d.E) ? GEMM_PREFILL : GEMM_DECODE;
 }
 
-struct RouteWs { size_t bc, total; };
-RouteWs route_ws(const Dims& d) {
+size_t gate_partial_bytes(const Dims& d);
+
+struct RouteWs { size_t bc, gpart, total; };
+RouteWs route_ws(const Dims& d, bool with_gate) {
   Carve c; RouteWs w;
   w.bc = c.take((size_t)d.nb * d.E * 4);
+  w.gpart = c.take(with_gate ? gate_partial_bytes(d) : 0);
   w.total = c.cur;
   return w;
 }
@@ -90,7 +93,8 @@ CombWs comb_ws(const Dims& d) {
 }
 
 struct LayerWs {
-  size_t logits, ids, w, counts, offsets, row_token, token_row, bc, mtile, z, xperm, act, outl, total;
+  size_t logits, ids, w, counts, offsets, row_token, token_row, bc, gpart, mtile, z, xperm, act, outl,
+      total;
 };
 LayerWs layer_ws(const Dims& d) {
   Carve c; LayerWs w;
@@ -102,6 +106,7 @@ LayerWs layer_ws(const Dims& d) {
   w.row_token = c.take((size_t)d.R * 4);
   w.token_row = c.take((size_t)d.R * 4);
   w.bc = c.take((size_t)d.nb * d.E * 4);
+  w.gpart = c.take(gate_partial_bytes(d));
   w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
   w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
@@ -121,10 +126,17 @@ P* at(void* ws, size_t off) {
     if ((call) != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
+size_t gate_partial_bytes(const Dims& d) {
+  if (!d.bf16) return 0;
+  const int s = gate_splits(d.T, d.E, d.H);
+  return s > 1 ? (size_t)s * d.T * d.E * 4 : 0;
+}
+
 moe_status gate_scores(const Dims& d, const void* x, const float* gate_w, const float* bias,
-                       float* logits, hipStream_t st) {
+                       float* logits, float* partial, hipStream_t st) {
   if (d.bf16) {
-    MOE_HIP(launch_gate_bf16(static_cast<const uint16_t*>(x), gate_w, bias, logits, d.T, d.E, d.H, st));
+    MOE_HIP(launch_gate_bf16(static_cast<const uint16_t*>(x), gate_w, bias, logits, partial, d.T, d.E,
+                             d.H, st));
   } else {
     MOE_HIP(launch_gemm_simt(false, EPI_F32_BIAS, x, d.T, gate_w, nullptr, logits, nullptr, nullptr,
                              1, d.E, d.H, bias, st));
@@ -189,8 +201,8 @@ size_t moe_workspace_bytes(const moe_shape* s, int call) {
   Dims d;
   if (check_shape(s, d) != MOE_OK) return 0;
   switch (call) {
-    case MOE_CALL_ROUTE: return route_ws(d).total;
-    case MOE_CALL_DISPATCH: return route_ws(d).total;
+    case MOE_CALL_ROUTE: return route_ws(d, true).total;
+    case MOE_CALL_DISPATCH: return route_ws(d, false).total;
     case MOE_CALL_FFN: return ffn_ws(d).total;
     case MOE_CALL_COMBINE: return comb_ws(d).total;
     case MOE_CALL_LAYER: return layer_ws(d).total;
@@ -209,11 +221,11 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
       !al16_or_null(gate_w) || !al16_or_null(gate_bias))
     return MOE_ERR_INVALID_ARG;
   if (gate_w && !al16(x)) return MOE_ERR_INVALID_ARG;
-  const RouteWs w = route_ws(d);
+  const RouteWs w = route_ws(d, gate_w != nullptr);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (gate_w) {
-    rc = gate_scores(d, x, gate_w, gate_bias, logits, st);
+    rc = gate_scores(d, x, gate_w, gate_bias, logits, at<float>(ws, w.gpart), st);
     if (rc != MOE_OK) return rc;
   }
   int32_t* bc = at<int32_t>(ws, w.bc);
@@ -231,7 +243,7 @@ moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const in
   if (!al16(x) || !al16(topk_ids) || !al16(offsets) || !al16(x_perm) || !al16(row_token) ||
       !al16(token_row))
     return MOE_ERR_INVALID_ARG;
-  const RouteWs w = route_ws(d);
+  const RouteWs w = route_ws(d, false);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* bc = at<int32_t>(ws, w.bc);
@@ -335,7 +347,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   }
   if (!ev(1)) return MOE_ERR_HIP;
   if (wt->gate_w) {  // a1: router logits on the full-width state
-    rc = gate_scores(d, x, wt->gate_w, wt->gate_bias, lg, st);
+    rc = gate_scores(d, x, wt->gate_w, wt->gate_bias, lg, at<float>(ws, w.gpart), st);
     if (rc != MOE_OK) return rc;
   }
   if (!ev(2)) return MOE_ERR_HIP;
