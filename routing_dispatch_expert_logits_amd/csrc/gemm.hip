@@ -9,8 +9,8 @@
 // (expert, m-tile, n-tile) with a binary search and the grid is sized from
 // host-known bounds only.
 //
-// Tile order: expert-major, then n-tile, then m-tile, so the tiles that share an
-// expert's weights and rows run together; logical tiles are dealt to the 8 XCDs
+// Tile order: expert-major, then n-tile (or a group of n-tiles), then m-tile, so
+// the tiles that share an expert's weights and rows run together; logical tiles are dealt to the 8 XCDs
 // in contiguous chunks (workgroup i runs on XCD i % 8), keeping each expert's
 // working set in one XCD's L2.
 //
@@ -28,8 +28,11 @@ struct TileCoord {
   int e, row0, rows, n0;
 };
 
-// Returns false when this workgroup has no tile.
-template <int BM, int BN>
+// Returns false when this workgroup has no tile.  Within an expert, tiles run in
+// groups of G consecutive n-tiles; inside a group the m-tile index is outer, so
+// the G tiles reading one m-tile's rows are adjacent and each weight panel is
+// reused G tiles later.
+template <int BM, int BN, int G = 1>
 __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
                                             const int32_t* __restrict__ mtile_start, int E, int M,
                                             int N, TileCoord& tc) {
@@ -46,7 +49,16 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
     const int mt0 = mtile_start[e];
     const int mte = mtile_start[e + 1] - mt0;
     const int local = L - mt0 * NT;
-    const int n_idx = local / mte, m_idx = local - n_idx * mte;
+    int n_idx, m_idx;
+    if constexpr (G == 1) {
+      n_idx = local / mte;
+      m_idx = local - n_idx * mte;
+    } else {
+      const int grp = local / (G * mte), r = local - grp * (G * mte);
+      const int ng = min(G, NT - grp * G);  // n-tiles in this group
+      m_idx = r / ng;
+      n_idx = grp * G + (r - m_idx * ng);
+    }
     tc.e = e;
     tc.row0 = offsets[e] + m_idx * BM;
     tc.rows = min(BM, offsets[e + 1] - tc.row0);
@@ -235,12 +247,12 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 static_assert(waitcnt_vm(24) == 0x4F78 && waitcnt_vm(0) == 0x0F70, "s_waitcnt encoding");
 
-template <int BM, int BN, int NB, int EPI, int S, int MW = 4, int BK = 64>
+template <int BM, int BN, int NB, int EPI, int S, int MW = 4, int BK = 64, int G = 1>
 __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_start, int E, int N, int K) {
-  static_assert((BM == 128 || BM == 256) && BN == 128, "tile 128 x 128 or 256 x 128");
+  static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile 128/256 x 128/256");
   static_assert(BK == 32 || BK == 64, "K-step 32 or 64");
   constexpr int WM = BM / 64;                     // MFMA waves along M (64 rows each)
   constexpr int WN = MW / WM;                     // MFMA waves along N
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
 
   TileCoord tc;
-  if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
+  if (!decode_tile<BM, BN, G>(offsets, mtile_start, E, M, N, tc)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nsteps = K / BK;
 
@@ -316,6 +328,12 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 
   // ---------------- MFMA waves
   const int wm = wave / WN, wn = wave % WN;
+  // a wave whose 64 rows all lie past the tile's valid rows only keeps the barrier
+  // cadence (one barrier before the loop, one per K-step)
+  if (wm * TM >= tc.rows) {
+    for (int s = 0; s <= nsteps; ++s) __syncthreads();
+    return;
+  }
   f32x4 acc[NB][FM][FN];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -340,33 +358,85 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
       boffs[h][fn] = A_ELEMS + r * BK + ((c ^ swz<BK>(r)) << 3);
     }
   }
-  // a wave whose 64 rows all lie past the tile's valid rows only keeps the barrier cadence
-  const bool active = wm * TM < tc.rows;
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    if (!active) {
-      __syncthreads();
-      continue;
+  // Operands are double-buffered in registers: the LDS reads of the next 32-wide
+  // substep are issued between the MFMAs of the current one, and the first reads of
+  // stage s+1 go out right after the barrier that releases it, ahead of stage s's
+  // last MFMAs.  So LDS reads overlap the MFMA pipe instead of preceding it.
+  struct Ops {
+    bf16x8 a[FM];
+    bf16x8 b[NB][FN];
+  };
+  constexpr int NR = FM + NB * FN, NM = NB * FN * FM;   // reads and MFMAs per substep
+  auto rd = [&](Ops& o, const uint16_t* base, int h) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) o.a[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoffs[h][fm]));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        o.b[nb][fn] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[h][fn]));
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          acc[nb][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[fm], o.b[nb][fn], acc[nb][fm][fn], 0, 0, 0);
+  };
+  // one MFMA, one LDS read, alternating while reads remain, then the other MFMAs
+  auto interleave = [] {
+#pragma unroll
+    for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    const uint16_t* base = lds + (s % S) * STAGE;
+    if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  };
+  static_assert(NH == 1 || NH == 2, "one or two substeps per K-step");
+  // Double-buffering needs a second operand set in registers; tiles whose
+  // accumulators leave no room for it (VGPRs per wave: 512 / waves per SIMD) read
+  // each substep's operands just before its MFMAs instead.
+  constexpr int kWavesPerSimd = (MW + 2 + 3) / 4;
+  constexpr int kVgprBudget = (512 / kWavesPerSimd) & ~7;
+  constexpr bool kDoubleBuffer = NM * 4 + 2 * NR * 4 + 40 <= kVgprBudget;
+  if constexpr (!kDoubleBuffer) {
+    __syncthreads();  // stage 0 has landed
+    for (int s = 0; s < nsteps; ++s) {
+      const uint16_t* base = lds + (s % S) * STAGE;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      bf16x8 af[FM];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoffs[h][fm]));
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[h][fn]));
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            acc[nb][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bf, acc[nb][fm][fn], 0, 0, 0);
-        }
+      for (int h = 0; h < NH; ++h) {
+        Ops o;
+        rd(o, base, h);
+        mma(o);
+      }
+      __syncthreads();  // every MFMA wave has read stage s; stage s+1 has landed
+    }
+  } else {
+    Ops o0, o1;
+    __syncthreads();  // stage 0 has landed
+    rd(o0, lds, 0);
+    for (int s = 0; s < nsteps; ++s) {
+      // the reads after the barrier fetch stage s+1; on the last step they read a
+      // stale (in-bounds) stage that no MFMA consumes
+      const uint16_t* nxt = lds + ((s + 1) % S) * STAGE;
+      if constexpr (NH == 2) {
+        rd(o1, lds + (s % S) * STAGE, 1);
+        mma(o0);
+        interleave();
+        __syncthreads();  // every MFMA wave has read stage s; stage s+1 has landed
+        rd(o0, nxt, 0);
+        mma(o1);
+        interleave();
+      } else {
+        __syncthreads();
+        rd(o1, nxt, 0);
+        mma(o0);
+        interleave();
+        o0 = o1;
       }
     }
-    __syncthreads();
   }
 
 #pragma unroll
@@ -603,13 +673,26 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
     }
     const int g = grid_for(max_mtiles(M, E, 128), N, 128);
     if (swiglu) {
+      // with 16 or more n-tiles per expert, n-tiles run in pairs so the two tiles
+      // reading one m-tile's rows are adjacent (DeepSeek-R1- and latent-shaped
+      // layers); with fewer, plain n-major order measured faster (Qwen3-shaped)
       const dim3 gb(g), bb(8 * 64 + 128);
-      if (epi == EPI_SWIGLU_BF16)
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), gb, bb, 0, st, A, M, B0,
-                           B1, C, offsets, mtile_start, E, N, K);
-      else
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), gb, bb, 0, st, A, M, B0,
-                           B1, C, offsets, mtile_start, E, N, K);
+      const bool pairs = ceil_div(N, 128) >= 16;
+      if (epi == EPI_SWIGLU_BF16) {
+        if (pairs)
+          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
+                             B0, B1, C, offsets, mtile_start, E, N, K);
+        else
+          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), gb, bb, 0, st, A, M, B0,
+                             B1, C, offsets, mtile_start, E, N, K);
+      } else {
+        if (pairs)
+          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
+                             B0, B1, C, offsets, mtile_start, E, N, K);
+        else
+          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), gb, bb, 0, st, A, M, B0,
+                             B1, C, offsets, mtile_start, E, N, K);
+      }
       return hipGetLastError();
     }
     if (K >= 2048) {  // down GEMM with a long K: 256-row tiles (second m-tile table)

@@ -113,4 +113,8 @@ PARITY_CONFIGS = {c.name: c for c in (
     # more than 2048 tokens: 64-token ranking blocks, 4 tokens per wave
     MoEConfig(name="many_tokens", T=2600, H=128, E=40, k=3, I=128, seed=21, gate="drawn",
               zipf_s=1.1, zipf_alpha=0.5),
+    # wide experts: 16 n-tiles of 128 in the gate/up GEMM and K = 2048 in the down
+    # GEMM (the large-layer kernel choices), skewed counts spanning several m-tiles
+    MoEConfig(name="wide_experts", T=400, H=256, E=4, k=2, I=2048, seed=22, gate="drawn",
+              zipf_s=1.1, zipf_alpha=1.0),
 )}
