@@ -11,124 +11,114 @@
 // cover fp32's 24).  Every bf16 x bf16 product is exact in fp32, so
 // X Wg^T = X hi^T + X mid^T + X lo^T evaluated with three fp32-accumulating MFMA
 // chains has the accuracy of an fp32 GEMM, at bf16 MFMA rate.  The split is done
-// while staging the weight tile into LDS; nothing is written back.
+// in registers on the weight fragments as they arrive; nothing is written back.
 #include "moe_kernels.h"
 
 namespace moe {
 
-constexpr int kGBK = 64;
-constexpr int kGLD = kGBK + 8;
-constexpr int kGBN = 64;
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ void split3(float w, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-  hi = f32_to_bf16(w);
-  const float r1 = w - bf16_to_f32(hi);
-  mid = f32_to_bf16(r1);
-  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+// Exact three-way bf16 split of 8 fp32 weights: w = hi + mid + lo.
+__device__ __forceinline__ void split3(f32x8 w, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
+  hi = __builtin_convertvector(w, bf16x8);
+  const f32x8 r1 = w - __builtin_convertvector(hi, f32x8);
+  mid = __builtin_convertvector(r1, bf16x8);
+  lo = __builtin_convertvector(r1 - __builtin_convertvector(mid, f32x8), bf16x8);
 }
 
-// blockIdx.y selects a K slice [y * Hs, (y + 1) * Hs) (split-K).  With one slice the
-// result plus bias goes to logits; with several, slice y writes its fp32 partial to
-// logits + y * T * E and k_gate_reduce adds the slices in a fixed order.
-template <int BM>
-__global__ __launch_bounds__(256, 2) void k_gate_split(const uint16_t* __restrict__ X,
-                                                       const float* __restrict__ Wg,
-                                                       const float* __restrict__ bias,
-                                                       float* __restrict__ logits, int T, int E,
-                                                       int H, int Hs) {
-  constexpr int BN = kGBN, TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16;
-  constexpr int A_PER = BM * 8 / 256;   // 16-byte bf16 chunks of the X tile per thread
-  constexpr int B_PER = BN * 16 / 256;  // 16-byte fp32 chunks of the Wg tile per thread
-  static_assert(A_PER >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * kGLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[3][BN * kGLD];
+// Workgroup: 4 waves as 2 (tokens) x 2 (experts); a wave owns a 64 x 32 block of
+// logits, a workgroup 128 x 64.  No LDS: every lane loads its own MFMA operand
+// fragments (8 consecutive k of one X row, 8 consecutive k of one Wg row), two
+// 32-wide K-steps ahead of their use; the waves of a workgroup that share rows or
+// experts read the same lines at about the same time, so the repeats hit in L1.
+constexpr int kGTM = 64, kGTN = 32, kGBM = 2 * kGTM, kGBN = 2 * kGTN;
 
-  const int NT = ceil_div(E, BN);
-  const int m0 = (blockIdx.x / NT) * BM, n0 = (blockIdx.x % NT) * BN;
+struct GateFrag {
+  u32x4 a[4];      // X rows m0 + 16 fm + l % 16
+  f32x4 b[2][2];   // Wg rows n0 + 16 fn + l % 16, two halves of 4 k
+};
+
+// blockIdx.y selects a K slice [y * Hs, (y + 1) * Hs), Hs a multiple of 64
+// (split-K).  With one slice the result plus bias goes to logits; with several,
+// slice y writes its fp32 partial to logits + y * T * E and k_gate_reduce adds
+// the slices in a fixed order.
+__global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
+                                              const float* __restrict__ Wg,
+                                              const float* __restrict__ bias,
+                                              float* __restrict__ logits, int T, int E, int H,
+                                              int Hs) {
+  const int NT = ceil_div(E, kGBN);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m0 = (blockIdx.x / NT) * kGBM + (wave >> 1) * kGTM;
+  const int n0 = (blockIdx.x % NT) * kGBN + (wave & 1) * kGTN;
+  if (m0 >= T || n0 >= E) return;  // no barriers or LDS: a wave with no logits leaves
   const int kbeg = blockIdx.y * Hs;
-  X += kbeg;
-  Wg += kbeg;
   if (gridDim.y > 1) {
     logits += (size_t)blockIdx.y * T * E;
     bias = nullptr;
   }
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // X tile loader: row (tid / 8) + 32 i, bf16 k-offset 8 * (tid % 8)
-  const int arow = tid >> 3, ak = (tid & 7) * 8;
-  uint32_t aoff[A_PER];
+  const int kl = (lane >> 4) * 8;
+  const uint16_t* pa[4];
+  const float* pb[2];
 #pragma unroll
-  for (int i = 0; i < A_PER; ++i) aoff[i] = (uint32_t)min(m0 + arow + 32 * i, T - 1);
-  // Wg tile loader: row (tid / 16) + 16 i, fp32 k-offset 4 * (tid % 16)
-  const int brow = tid >> 4, bk = (tid & 15) * 4;
-  uint32_t boff[B_PER];
+  for (int fm = 0; fm < 4; ++fm) pa[fm] = X + (size_t)min(m0 + fm * 16 + (lane & 15), T - 1) * H + kbeg + kl;
 #pragma unroll
-  for (int i = 0; i < B_PER; ++i) boff[i] = (uint32_t)min(n0 + brow + 16 * i, E - 1);
+  for (int fn = 0; fn < 2; ++fn) pb[fn] = Wg + (size_t)min(n0 + fn * 16 + (lane & 15), E - 1) * H + kbeg + kl;
 
-  f32x4 acc[3][FM][FN];
+  auto load = [&](GateFrag& f, int k) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) f.a[fm] = *reinterpret_cast<const u32x4*>(pa[fm] + k);
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      f.b[fn][0] = *reinterpret_cast<const f32x4*>(pb[fn] + k);
+      f.b[fn][1] = *reinterpret_cast<const f32x4*>(pb[fn] + k + 4);
+    }
+  };
+  f32x4 acc[3][4][2];
 #pragma unroll
   for (int j = 0; j < 3; ++j)
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[j][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[A_PER];
-  f32x4 rb[B_PER];
-  auto load = [&](int k0) {
+      for (int fn = 0; fn < 2; ++fn) acc[j][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const GateFrag& f) {
+    bf16x8 bh[2], bm[2], bl[2];
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      ra[i] = *reinterpret_cast<const u32x4*>(X + (size_t)aoff[i] * H + k0 + ak);
+    for (int fn = 0; fn < 2; ++fn) {
+      const f32x8 w = {f.b[fn][0][0], f.b[fn][0][1], f.b[fn][0][2], f.b[fn][0][3],
+                       f.b[fn][1][0], f.b[fn][1][1], f.b[fn][1][2], f.b[fn][1][3]};
+      split3(w, bh[fn], bm[fn], bl[fn]);
+    }
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      rb[i] = *reinterpret_cast<const f32x4*>(Wg + (size_t)boff[i] * H + k0 + bk);
+    for (int fm = 0; fm < 4; ++fm) {
+      const bf16x8 a = as_bf16x8(f.a[fm]);
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) {
+        acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[fn], acc[0][fm][fn], 0, 0, 0);
+        acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[fn], acc[1][fm][fn], 0, 0, 0);
+        acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[fn], acc[2][fm][fn], 0, 0, 0);
+      }
+    }
   };
-  load(0);
-  const int ar = wm * TM + (lane & 15), br = wn * TN + (lane & 15), kofs = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < Hs; k0 += kGBK) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      *reinterpret_cast<u32x4*>(&sA[(arow + 32 * i) * kGLD + ak]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      uint16_t h[4], m[4], l[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split3(rb[i][q], h[q], m[q], l[q]);
-      const int o = (brow + 16 * i) * kGLD + bk;
-      *reinterpret_cast<uint2*>(&sB[0][o]) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
-      *reinterpret_cast<uint2*>(&sB[1][o]) = make_uint2(m[0] | (uint32_t)m[1] << 16, m[2] | (uint32_t)m[3] << 16);
-      *reinterpret_cast<uint2*>(&sB[2][o]) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
-    }
-    __syncthreads();
-    load(min(k0 + kGBK, Hs - kGBK));
-#pragma unroll
-    for (int ks = 0; ks < kGBK; ks += 32) {
-      bf16x8 af[FM];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sA[(ar + fm * 16) * kGLD + ks + kofs]));
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const bf16x8 bfr =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(&sB[j][(br + fn * 16) * kGLD + ks + kofs]));
-#pragma unroll
-          for (int fm = 0; fm < FM; ++fm)
-            acc[j][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[fm], bfr, acc[j][fm][fn], 0, 0, 0);
-        }
-    }
+  // two K-steps in flight; past the end of the slice the loads repeat its last
+  // step (in bounds, never consumed)
+  GateFrag f0, f1;
+  load(f0, 0);
+  load(f1, 32);
+  for (int k = 0; k < Hs; k += 64) {
+    step(f0);
+    load(f0, min(k + 64, Hs - 32));
+    step(f1);
+    load(f1, min(k + 96, Hs - 32));
   }
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
+    for (int fn = 0; fn < 2; ++fn)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = m0 + wm * TM + fm * 16 + (lane >> 4) * 4 + i;
-        const int c = n0 + wn * TN + fn * 16 + (lane & 15);
+        const int r = m0 + fm * 16 + (lane >> 4) * 4 + i;
+        const int c = n0 + fn * 16 + (lane & 15);
         if (r < T && c < E) {
           float v = (acc[0][fm][fn][i] + acc[1][fm][fn][i]) + acc[2][fm][fn][i];
           if (bias) v += bias[c];
@@ -151,23 +141,20 @@ __global__ __launch_bounds__(256) void k_gate_reduce(const float* __restrict__ p
 }
 
 int gate_splits(int T, int E, int H) {
-  const int NT = ceil_div(E, kGBN);
-  const int tiles = ceil_div(T, 64) * NT;
+  // split K until about 1024 waves run (each K slice a multiple of 64); a 2048-wave
+  // target measured slower on the Qwen3-, DeepSeek-R1-shaped and latent layers
+  const int waves = ceil_div(T, kGBM) * ceil_div(E, kGBN) * 4;
   int s = 1;
-  while (tiles * s < 1024 && s < 8 && H % (64 * s * 2) == 0) s *= 2;
+  while (waves * s < 1024 && s < 8 && H % (64 * s * 2) == 0) s *= 2;
   return s;
 }
 
 hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
                             float* partial, int T, int E, int H, hipStream_t st) {
-  const int NT = ceil_div(E, kGBN);
-  // 64-row tiles; the K range is split until there are ~1024 workgroups (each K slice
-  // a multiple of 64), so every workgroup runs a short K loop
   const int S = gate_splits(T, E, H);
   const int Hs = H / S;
-  const dim3 g(ceil_div(T, 64) * NT, S), b(256);
-  hipLaunchKernelGGL(k_gate_split<64>, g, b, 0, st, x, gate_w, bias, S > 1 ? partial : logits, T, E,
-                     H, Hs);
+  const dim3 g(ceil_div(T, kGBM) * ceil_div(E, kGBN), S), b(256);
+  hipLaunchKernelGGL(k_gate, g, b, 0, st, x, gate_w, bias, S > 1 ? partial : logits, T, E, H, Hs);
   if (S > 1) {
     const size_t n = (size_t)T * E;
     hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial, S,

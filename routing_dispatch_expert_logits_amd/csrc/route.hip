@@ -22,7 +22,7 @@ namespace moe {
 // that entry; both reductions are DPP row butterflies plus readlane.  Counts per
 // expert for the block are gathered in LDS (order-independent) and written to
 // block_counts[block][e].
-template <int SLOTS>
+template <int SLOTS, int G>
 __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_in,
                                                const float* __restrict__ bias, int T, int E, int k,
                                                int32_t* __restrict__ topk_ids,
@@ -33,8 +33,8 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
 
-  // the scores of G tokens are loaded before their selection work starts
-  constexpr int G = SLOTS >= 16 ? 2 : 4;
+  // the scores of G tokens (G <= tokens per wave) are loaded before their
+  // selection work starts
   const int tpw = block_tokens(T) / 16;
   float bv[SLOTS];
 #pragma unroll
@@ -55,43 +55,67 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_
         sv[i][s] = e < E ? row[e] : 0.f;
       }
     }
+    // The G tokens run through the k rounds together: their wave reductions are
+    // independent, so their latencies overlap.  Tokens past the end (clamped
+    // rows above) are ranked too but write nothing.
+    uint32_t key[G][SLOTS];
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int t = tbase + i;
-      if (t >= T || g0 + i >= tpw) break;
-      uint32_t key[SLOTS];
+    for (int i = 0; i < G; ++i)
 #pragma unroll
       for (int s = 0; s < SLOTS; ++s) {
         const int e = lane + s * kWave;
         const float v = bias ? sv[i][s] + bv[s] : sv[i][s];
-        key[s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
+        key[i][s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
       }
-      int my_e = 0;
-      float my_s = 0.f, top = 0.f;
-      for (int j = 0; j < k; ++j) {
-        uint32_t lm = key[0];
+    int my_e[G];
+    float my_s[G], top[G];
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
-        const uint32_t best = wave_max_u32(lm);
+    for (int i = 0; i < G; ++i) {
+      my_e[i] = 0;
+      my_s[i] = 0.f;
+      top[i] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+      uint32_t best[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        uint32_t lm = key[i][0];
+#pragma unroll
+        for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[i][s]);
+        best[i] = wave_max_u32(lm);
+      }
+      int sel[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
         uint32_t li = 0xffffffffu;
 #pragma unroll
         for (int s = SLOTS - 1; s >= 0; --s)
-          if (key[s] == best) li = static_cast<uint32_t>(lane + s * kWave);
-        const int e = static_cast<int>(wave_min_u32(li));
-        const float sc = key_to_score(best);
-        if (j == 0) top = sc;
-        if (lane == j) { my_e = e; my_s = sc; }
+          if (key[i][s] == best[i]) li = static_cast<uint32_t>(lane + s * kWave);
+        sel[i] = static_cast<int>(wave_min_u32(li));
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float sc = key_to_score(best[i]);
+        if (j == 0) top[i] = sc;
+        if (lane == j) {
+          my_e[i] = sel[i];
+          my_s[i] = sc;
+        }
 #pragma unroll
         for (int s = 0; s < SLOTS; ++s)
-          if (lane + s * kWave == e) key[s] = 0u;
+          if (lane + s * kWave == sel[i]) key[i][s] = 0u;
       }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int t = tbase + i;
       // Renormalised softmax over the selected k: the full-E denominator cancels.
-      const float ex = lane < k ? expf(my_s - top) : 0.f;
+      const float ex = lane < k ? expf(my_s[i] - top[i]) : 0.f;
       const float sum = wave_sum_f32(ex);
-      if (lane < k) {
-        topk_ids[(size_t)t * k + lane] = my_e;
+      if (t < T && g0 + i < tpw && lane < k) {
+        topk_ids[(size_t)t * k + lane] = my_e[i];
         topk_w[(size_t)t * k + lane] = ex / sum;
-        atomicAdd(&cnt[my_e], 1);
+        atomicAdd(&cnt[my_e[i]], 1);
       }
     }
   }
@@ -158,8 +182,20 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
   const bool active = p < P;
   const int b0 = active ? (int)((long)nb * p / P) : 0;
   const int b1 = active ? (int)((long)nb * (p + 1) / P) : 0;
+  // loads are batched eight at a time so their latencies overlap
+  constexpr int U = 8;
   int part = 0;
-  for (int b = b0; b < b1; ++b) part += block_counts[(size_t)b * E + e];
+  {
+    int b = b0;
+    for (; b + U <= b1; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = block_counts[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) part += v[u];
+    }
+    for (; b < b1; ++b) part += block_counts[(size_t)b * E + e];
+  }
   if (active) psum[p * E + e] = part;
   __syncthreads();
   int c = 0;
@@ -180,7 +216,18 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
   if (active) {
     int run = off_s[e];
     for (int q = 0; q < p; ++q) run += psum[q * E + e];
-    for (int b = b0; b < b1; ++b) {
+    int b = b0;
+    for (; b + U <= b1; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = block_counts[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        block_counts[(size_t)(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; b < b1; ++b) {
       const size_t i = (size_t)b * E + e;
       const int v = block_counts[i];
       block_counts[i] = run;
@@ -224,12 +271,24 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
                        float* w, int32_t* block_counts, hipStream_t st) {
   const int nb = ceil_div(T, block_tokens(T));
   const int slots = ceil_div(E, kWave);
+  const bool one = block_tokens(T) == 16;  // one token per wave
   dim3 g(nb), b(1024);
-  if (slots <= 1) hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 2) hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 4) hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 8) hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+#define MOE_TOPK(SL, GG) \
+  hipLaunchKernelGGL((k_topk<SL, GG>), g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts)
+  if (one) {
+    if (slots <= 1) MOE_TOPK(1, 1);
+    else if (slots <= 2) MOE_TOPK(2, 1);
+    else if (slots <= 4) MOE_TOPK(4, 1);
+    else if (slots <= 8) MOE_TOPK(8, 1);
+    else MOE_TOPK(16, 1);
+  } else {
+    if (slots <= 1) MOE_TOPK(1, 4);
+    else if (slots <= 2) MOE_TOPK(2, 4);
+    else if (slots <= 4) MOE_TOPK(4, 4);
+    else if (slots <= 8) MOE_TOPK(8, 4);
+    else MOE_TOPK(16, 2);
+  }
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
