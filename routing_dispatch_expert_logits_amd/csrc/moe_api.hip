@@ -230,7 +230,8 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
   }
   int32_t* bc = at<int32_t>(ws, w.bc);
   MOE_HIP(launch_topk(logits, gate_w ? nullptr : gate_bias, d.T, d.E, d.k, topk_ids, topk_w, bc, st));
-  MOE_HIP(launch_scan(bc, d.nb, d.E, nullptr, counts, offsets, 0, nullptr, st));
+  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
+  MOE_HIP(launch_offsets(counts, nullptr, d.E, offsets, 0, nullptr, st));
   return MOE_OK;
 }
 
@@ -248,9 +249,9 @@ moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const in
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* bc = at<int32_t>(ws, w.bc);
   MOE_HIP(launch_block_counts(topk_ids, d.T, d.E, d.k, bc, st));
-  MOE_HIP(launch_scan(bc, d.nb, d.E, offsets, nullptr, nullptr, 0, nullptr, st));
-  MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, bc, x_perm, row_token,
-                         token_row, st));
+  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, nullptr, st));
+  MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, offsets, bc, x_perm,
+                         row_token, token_row, st));
   return MOE_OK;
 }
 
@@ -266,7 +267,7 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const voi
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* mtile = at<int32_t>(ws, w.mtile);
-  MOE_HIP(launch_mtiles(offsets, d.E, gemm_bm(expert_kind(d)), mtile, st));
+  MOE_HIP(launch_offsets(nullptr, offsets, d.E, nullptr, gemm_bm(expert_kind(d)), mtile, st));
   return expert_ffn(d, x_perm, offsets, mtile, w1, w3, w2, at<void>(ws, w.act), y_perm, st);
 }
 
@@ -353,10 +354,12 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   if (!ev(2)) return MOE_ERR_HIP;
   // a2 + a3
   MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
-  MOE_HIP(launch_scan(bc, d.nb, d.E, nullptr, counts, offs, gemm_bm(kind), mtile, st));
+  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
+  MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
   if (!ev(3)) return MOE_ERR_HIP;
   // a4
-  MOE_HIP(launch_permute(d.L ? z : x, d.D * d.es / 16, ids, d.T, d.E, d.k, bc, xperm, rtok, trow, st));
+  MOE_HIP(launch_permute(d.L ? z : x, d.D * d.es / 16, ids, d.T, d.E, d.k, offs, bc, xperm, rtok,
+                         trow, st));
   if (!ev(4)) return MOE_ERR_HIP;
   // a5
   if (kind == GEMM_SIMT) {

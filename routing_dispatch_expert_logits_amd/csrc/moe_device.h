@@ -7,11 +7,11 @@
 namespace moe {
 
 constexpr int kWave = 64;
-// Tokens per ranking block (one bit per token in a 64-bit mask): 64, or 16 for
-// small token counts so the top-k kernel runs one token per wave on more CUs.
-constexpr int kBlockTokLarge = 64;
-constexpr int kBlockTokSmall = 16;
-__host__ __device__ __forceinline__ int block_tokens(int T) { return T <= 2048 ? kBlockTokSmall : kBlockTokLarge; }
+// Tokens per ranking block (one bit per token in a mask): the top-k kernel ranks
+// one block per workgroup, one token per wave, so T / 16 workgroups spread over
+// the CUs (64-token blocks left most CUs idle at T = 4096).
+constexpr int kBlockTok = 16;
+__host__ __device__ __forceinline__ int block_tokens(int) { return kBlockTok; }
 constexpr int kMaxE = 1024;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

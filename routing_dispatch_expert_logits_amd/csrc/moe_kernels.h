@@ -25,14 +25,17 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
                        float* w, int32_t* block_counts, hipStream_t st);
 hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t* block_counts,
                                hipStream_t st);
-hipError_t launch_scan(int32_t* block_counts, int nb, int E, const int32_t* offsets_in,
-                       int32_t* counts_out, int32_t* offsets_out, int bm, int32_t* mtile_start,
-                       hipStream_t st);
-hipError_t launch_mtiles(const int32_t* offsets, int E, int bm, int32_t* mtile_start,
-                         hipStream_t st);
+// block_counts[b][e] -> rows of e in blocks before b; counts_out[e] = total (if non-NULL).
+hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int32_t* counts_out,
+                              hipStream_t st);
+// offsets_out from counts (if non-NULL) and, for bm > 0, the m-tile tables for tile heights
+// bm and 2 bm; with offsets_in the counts are its differences.
+hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int E,
+                          int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st);
+// bases: per-block rows before each block (launch_expert_scan); offsets: segment starts.
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
-                          const int32_t* bases, void* x_perm, int32_t* row_token,
-                          int32_t* token_row, hipStream_t st);
+                          const int32_t* offsets, const int32_t* bases, void* x_perm,
+                          int32_t* row_token, int32_t* token_row, hipStream_t st);
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
                           const float* w, int T, int k, void* out, bool out_f32, hipStream_t st);
 hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
@@ -41,7 +44,7 @@ hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, co
                                   int T, int k, void* out, bool out_f32, hipStream_t st);
 // bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.
 // mtile_start holds the m-tile tables for tile heights gemm_bm(kind) and 2 * gemm_bm(kind)
-// (E + 1 entries each, as written by launch_scan / launch_mtiles).
+// (E + 1 entries each, as written by launch_offsets).
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st);

@@ -9,9 +9,9 @@
 // local and no padding.
 //
 // Row order inside an expert's segment is ascending token id, independent of
-// scheduling: row = base[block][e] + (number of lower tokens of the same
-// 64-token block that picked e), the latter a popcount of a per-expert token
-// bitmask built with order-independent LDS atomicOr.
+// scheduling: row = offsets[e] + base[block][e] + (number of lower tokens of the
+// same 16-token ranking block that picked e), the latter a popcount of a per-expert
+// token bitmask built with order-independent LDS atomicOr.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -26,6 +26,7 @@ constexpr int kCopyUnroll = 4;
 __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int row16,
                                                  const int32_t* __restrict__ topk_ids, int T,
                                                  int E, int k, int tpw,
+                                                 const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ bases,
                                                  u32x4* __restrict__ x_perm,
                                                  int32_t* __restrict__ row_token,
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
       const int e = topk_ids[(size_t)t * k + lane];
       const int tl = t - bt0;
       const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
-      row = bases[(size_t)blk * E + e] + rank;
+      row = offsets[e] + bases[(size_t)blk * E + e] + rank;
       if (meta) {
         token_row[(size_t)t * k + lane] = row;
         row_token[row] = t;
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
 }
 
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
-                          const int32_t* bases, void* x_perm, int32_t* row_token,
-                          int32_t* token_row, hipStream_t st) {
+                          const int32_t* offsets, const int32_t* bases, void* x_perm,
+                          int32_t* row_token, int32_t* token_row, hipStream_t st) {
   // 4 tokens per wave for large T, 1 for small T (a workgroup's tokens always lie
   // in one ranking block); split columns until ~1024 workgroups
   const int tpw = T >= 4096 ? 4 : 1;
@@ -93,7 +94,8 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
   int cs = 1;
   while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
   hipLaunchKernelGGL(k_permute, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
-                     ids, T, E, k, tpw, bases, static_cast<u32x4*>(x_perm), row_token, token_row);
+                     ids, T, E, k, tpw, offsets, bases, static_cast<u32x4*>(x_perm), row_token,
+                     token_row);
   return hipGetLastError();
 }
 

@@ -14,109 +14,65 @@
 
 namespace moe {
 
-// One workgroup per ranking block of 16 * tpw tokens: 16 waves x tpw tokens
-// (tpw = 4 for 64-token blocks, 1 for 16-token blocks).  A wave holds
-// one token's E scores as order keys (order_key(score): larger score, larger
+// One workgroup per 16-token ranking block, one token per wave.  A wave holds
+// the token's E scores as order keys (order_key(score): larger score, larger
 // key).  Each of the k rounds takes the wave-wide largest key, then the lowest
 // expert index holding it (so equal scores go to the lower index), and removes
 // that entry; both reductions are DPP row butterflies plus readlane.  Counts per
 // expert for the block are gathered in LDS (order-independent) and written to
 // block_counts[block][e].
-template <int SLOTS, int G>
+template <int SLOTS>
 __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_in,
                                                const float* __restrict__ bias, int T, int E, int k,
                                                int32_t* __restrict__ topk_ids,
                                                float* __restrict__ topk_w,
                                                int32_t* __restrict__ block_counts) {
+  static_assert(kBlockTok == 16, "one token per wave of a 1024-thread workgroup");
   __shared__ int cnt[kMaxE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
 
-  // the scores of G tokens (G <= tokens per wave) are loaded before their
-  // selection work starts
-  const int tpw = block_tokens(T) / 16;
-  float bv[SLOTS];
+  const int t = blockIdx.x * kBlockTok + wave;
+  if (t < T) {
+    const float* row = scores_in + (size_t)t * E;
+    uint32_t key[SLOTS];
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) {
-    const int e = lane + s * kWave;
-    bv[s] = (bias && e < E) ? bias[e] : 0.f;
-  }
-  for (int g0 = 0; g0 < tpw; g0 += G) {
-    const int tbase = blockIdx.x * 16 * tpw + wave * tpw + g0;
-    float sv[G][SLOTS];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int t = min(tbase + i, T - 1);
-      const float* row = scores_in + (size_t)t * E;
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const int e = lane + s * kWave;
-        sv[i][s] = e < E ? row[e] : 0.f;
-      }
+    for (int s = 0; s < SLOTS; ++s) {
+      const int e = lane + s * kWave;
+      float v = e < E ? row[e] : 0.f;
+      if (bias && e < E) v += bias[e];
+      key[s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
     }
-    // The G tokens run through the k rounds together: their wave reductions are
-    // independent, so their latencies overlap.  Tokens past the end (clamped
-    // rows above) are ranked too but write nothing.
-    uint32_t key[G][SLOTS];
-#pragma unroll
-    for (int i = 0; i < G; ++i)
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s) {
-        const int e = lane + s * kWave;
-        const float v = bias ? sv[i][s] + bv[s] : sv[i][s];
-        key[i][s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
-      }
-    int my_e[G];
-    float my_s[G], top[G];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      my_e[i] = 0;
-      my_s[i] = 0.f;
-      top[i] = 0.f;
-    }
+    int my_e = 0;
+    float my_s = 0.f, top = 0.f;
     for (int j = 0; j < k; ++j) {
-      uint32_t best[G];
+      uint32_t lm = key[0];
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        uint32_t lm = key[i][0];
+      for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
+      const uint32_t best = wave_max_u32(lm);
+      uint32_t li = 0xffffffffu;
 #pragma unroll
-        for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[i][s]);
-        best[i] = wave_max_u32(lm);
-      }
-      int sel[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        uint32_t li = 0xffffffffu;
-#pragma unroll
-        for (int s = SLOTS - 1; s >= 0; --s)
-          if (key[i][s] == best[i]) li = static_cast<uint32_t>(lane + s * kWave);
-        sel[i] = static_cast<int>(wave_min_u32(li));
+      for (int s = SLOTS - 1; s >= 0; --s)
+        if (key[s] == best) li = static_cast<uint32_t>(lane + s * kWave);
+      const int e = static_cast<int>(wave_min_u32(li));
+      const float sc = key_to_score(best);
+      if (j == 0) top = sc;
+      if (lane == j) {
+        my_e = e;
+        my_s = sc;
       }
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float sc = key_to_score(best[i]);
-        if (j == 0) top[i] = sc;
-        if (lane == j) {
-          my_e[i] = sel[i];
-          my_s[i] = sc;
-        }
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s)
-          if (lane + s * kWave == sel[i]) key[i][s] = 0u;
-      }
+      for (int s = 0; s < SLOTS; ++s)
+        if (lane + s * kWave == e) key[s] = 0u;
     }
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int t = tbase + i;
-      // Renormalised softmax over the selected k: the full-E denominator cancels.
-      const float ex = lane < k ? expf(my_s[i] - top[i]) : 0.f;
-      const float sum = wave_sum_f32(ex);
-      if (t < T && g0 + i < tpw && lane < k) {
-        topk_ids[(size_t)t * k + lane] = my_e[i];
-        topk_w[(size_t)t * k + lane] = ex / sum;
-        atomicAdd(&cnt[my_e[i]], 1);
-      }
+    // Renormalised softmax over the selected k: the full-E denominator cancels.
+    const float ex = lane < k ? expf(my_s - top) : 0.f;
+    const float sum = wave_sum_f32(ex);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = ex / sum;
+      atomicAdd(&cnt[my_e], 1);
     }
   }
   __syncthreads();
@@ -158,34 +114,23 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem
   return res;
 }
 
-// Counts -> offsets -> per-block row bases (+ the GEMM m-tile table).
-//   block_counts[b][e] in: assignments of expert e in ranking block b;
-//                      out: first row of block b's assignments to e.
-//   offsets_in  non-NULL: use these segment starts (moe_dispatch_permute);
-//               NULL: write counts_out / offsets_out from the block counts.
-//   bm > 0: GEMM m-tile tables for two tile heights, bm and 2 bm:
-//           mtile_start[e] = sum_{e' < e} ceil(count_e' / bm), mtile_start[E] = total,
-//           and the same for 2 bm at mtile_start[E + 1 + e].
-// Thread t works on expert t % E and on the P = 1024 / E contiguous block ranges
-// of part t / E, so the column sums and the per-block prefix run P-wide.
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_counts, int nb, int E,
-                                               const int32_t* __restrict__ offsets_in,
-                                               int32_t* __restrict__ counts_out,
-                                               int32_t* __restrict__ offsets_out, int bm,
-                                               int32_t* __restrict__ mtile_start) {
-  __shared__ int smem[48];
-  __shared__ int psum[1024];
-  __shared__ int off_s[kMaxE];
-  const int t = threadIdx.x;
-  const int P = 1024 / E;
-  const int e = t % E, p = t / E;
-  const bool active = p < P;
-  const int b0 = active ? (int)((long)nb * p / P) : 0;
-  const int b1 = active ? (int)((long)nb * (p + 1) / P) : 0;
-  // loads are batched eight at a time so their latencies overlap
-  constexpr int U = 8;
+// Per-expert scan of the block counts: block_counts[b][e] (rows of expert e in
+// ranking block b) becomes the number of rows of e in the blocks before b, and
+// counts_out[e] (if non-NULL) the expert's total.  Workgroup x covers experts
+// 64x .. 64x + 63, one per lane, so every load is a coalesced 256-byte row slice;
+// its 16 waves split the blocks into 16 contiguous ranges.  The experts'
+// segment starts are added by the consumer (offsets[e] + base), so no
+// workgroup waits for another.
+__global__ __launch_bounds__(1024) void k_expert_scan(int32_t* __restrict__ block_counts, int nb,
+                                                      int E, int32_t* __restrict__ counts_out) {
+  __shared__ int psum[16][kWave];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * kWave + lane;
+  const bool on = e < E;
+  const int b0 = (int)((long)nb * w / 16), b1 = (int)((long)nb * (w + 1) / 16);
+  constexpr int U = 16;  // loads in flight per lane
   int part = 0;
-  {
+  if (on) {
     int b = b0;
     for (; b + U <= b1; b += U) {
       int v[U];
@@ -196,26 +141,17 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
     }
     for (; b < b1; ++b) part += block_counts[(size_t)b * E + e];
   }
-  if (active) psum[p * E + e] = part;
+  psum[w][lane] = part;
   __syncthreads();
-  int c = 0;
-  if (t < E)
-    for (int q = 0; q < P; ++q) c += psum[q * E + t];
-  int total = 0;
-  int off = block_exclusive_scan(t < E ? c : 0, &total, smem);
-  if (t < E) {
-    if (offsets_in) off = offsets_in[t];
-    off_s[t] = off;
-    if (counts_out) counts_out[t] = c;
-    if (offsets_out) {
-      offsets_out[t] = off;
-      if (t == E - 1) offsets_out[E] = off + c;
-    }
+  int run = 0, total = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int v = psum[q][lane];
+    run += q < w ? v : 0;
+    total += v;
   }
-  __syncthreads();
-  if (active) {
-    int run = off_s[e];
-    for (int q = 0; q < p; ++q) run += psum[q * E + e];
+  if (on && w == 0 && counts_out) counts_out[e] = total;
+  if (on) {
     int b = b0;
     for (; b + U <= b1; b += U) {
       int v[U];
@@ -234,6 +170,27 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
       run += v;
     }
   }
+}
+
+// Segment starts and GEMM m-tile tables from the per-expert counts (or, when
+// offsets_in is given, from those segment starts).
+//   offsets_out non-NULL: offsets_out[e] = sum_{e' < e} counts[e'], offsets_out[E] = total.
+//   bm > 0: m-tile tables for two tile heights, bm and 2 bm:
+//           mtile_start[e] = sum_{e' < e} ceil(count_e' / bm), mtile_start[E] = total,
+//           and the same for 2 bm at mtile_start[E + 1 + e].
+__global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ counts,
+                                                  const int32_t* __restrict__ offsets_in, int E,
+                                                  int32_t* __restrict__ offsets_out, int bm,
+                                                  int32_t* __restrict__ mtile_start) {
+  __shared__ int smem[48];
+  const int t = threadIdx.x;
+  const int c = t < E ? (offsets_in ? offsets_in[t + 1] - offsets_in[t] : counts[t]) : 0;
+  if (offsets_out) {
+    int total = 0;
+    const int off = block_exclusive_scan(c, &total, smem);
+    if (t < E) offsets_out[t] = off;
+    if (t == E - 1) offsets_out[E] = off + c;
+  }
   if (bm > 0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -247,48 +204,18 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ block_count
   }
 }
 
-// m-tile tables (tile heights bm and 2 bm, as in k_scan) from given offsets
-// (moe_grouped_ffn on its own).
-__global__ __launch_bounds__(1024) void k_mtiles(const int32_t* __restrict__ offsets, int E, int bm,
-                                                 int32_t* __restrict__ mtile_start) {
-  __shared__ int smem[48];
-  const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int mt = e < E ? ceil_div(c, bm << h) : 0;
-    int tot = 0;
-    const int st = block_exclusive_scan(mt, &tot, smem);
-    int32_t* tab = mtile_start + h * (E + 1);
-    if (e < E) tab[e] = st;
-    if (e == E - 1) tab[E] = st + mt;
-  }
-}
-
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
                        float* w, int32_t* block_counts, hipStream_t st) {
   const int nb = ceil_div(T, block_tokens(T));
   const int slots = ceil_div(E, kWave);
-  const bool one = block_tokens(T) == 16;  // one token per wave
   dim3 g(nb), b(1024);
-#define MOE_TOPK(SL, GG) \
-  hipLaunchKernelGGL((k_topk<SL, GG>), g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts)
-  if (one) {
-    if (slots <= 1) MOE_TOPK(1, 1);
-    else if (slots <= 2) MOE_TOPK(2, 1);
-    else if (slots <= 4) MOE_TOPK(4, 1);
-    else if (slots <= 8) MOE_TOPK(8, 1);
-    else MOE_TOPK(16, 1);
-  } else {
-    if (slots <= 1) MOE_TOPK(1, 4);
-    else if (slots <= 2) MOE_TOPK(2, 4);
-    else if (slots <= 4) MOE_TOPK(4, 4);
-    else if (slots <= 8) MOE_TOPK(8, 4);
-    else MOE_TOPK(16, 2);
-  }
-#undef MOE_TOPK
+  if (slots <= 1) hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+  else if (slots <= 2) hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+  else if (slots <= 4) hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+  else if (slots <= 8) hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+  else hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
   return hipGetLastError();
 }
 
@@ -299,17 +226,17 @@ hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_scan(int32_t* block_counts, int nb, int E, const int32_t* offsets_in,
-                       int32_t* counts_out, int32_t* offsets_out, int bm, int32_t* mtile_start,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, st, block_counts, nb, E, offsets_in,
-                     counts_out, offsets_out, bm, mtile_start);
+hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int32_t* counts_out,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_expert_scan, dim3(ceil_div(E, kWave)), dim3(1024), 0, st, block_counts, nb, E,
+                     counts_out);
   return hipGetLastError();
 }
 
-hipError_t launch_mtiles(const int32_t* offsets, int E, int bm, int32_t* mtile_start,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(k_mtiles, dim3(1), dim3(1024), 0, st, offsets, E, bm, mtile_start);
+hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int E,
+                          int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st) {
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, counts, offsets_in, E, offsets_out, bm,
+                     mtile_start);
   return hipGetLastError();
 }
 

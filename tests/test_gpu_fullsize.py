@@ -74,6 +74,10 @@ def test_layer_full_size_sampled(name):
     assert got["counts"].sum() == T * k
     np.testing.assert_array_equal(got["counts"], np.diff(got["offsets"]))
     check_permutation_valid(got["topk_ids"], got["offsets"], got["row_token"], got["token_row"])
+    # the row order is a function of the ids alone: bit-exact against the oracle's
+    rt, tr = oracle.permutation(got["topk_ids"], E)
+    np.testing.assert_array_equal(got["row_token"], rt)
+    np.testing.assert_array_equal(got["token_row"], tr)
     assert R * D * cfg.elem_bytes == oracle.dispatch_bytes(T, k, D, cfg.elem_bytes)
     np.testing.assert_array_equal(host(out16, True), rne_bf16_bits(o32))
     # sampled tokens against the oracle

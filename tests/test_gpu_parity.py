@@ -79,6 +79,19 @@ def test_route_ties_and_signed_zeros(E, k):
     _check_route(cfg, lg, None)
 
 
+@pytest.mark.parametrize("E,k", [(300, 8), (500, 9), (1024, 64)])
+def test_route_many_tokens_wide(E, k):
+    """More than 2048 tokens (over 128 ranking blocks, so every scan thread walks
+    several batches of block counts) with wide expert sets: drawn scores with a
+    block of exact ties."""
+    T = 2100
+    r = np.random.default_rng(E * 7 + k)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    lg[100:164, : E // 3] = 1.5
+    cfg = PARITY_CONFIGS["all_ties"].with_(T=T, E=E, k=k)
+    _check_route(cfg, lg, None)
+
+
 @pytest.mark.parametrize("cfg", [c for c in CFGS if c.gate == "computed"],
                          ids=[c.name for c in CFGS if c.gate == "computed"])
 def test_gate_logits(cfg):

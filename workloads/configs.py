@@ -110,7 +110,7 @@ PARITY_CONFIGS = {c.name: c for c in (
     MoEConfig(name="many_empty", T=5, H=128, E=64, k=2, I=64, seed=19, gate="drawn"),
     MoEConfig(name="small_f32_computed", T=97, H=96, E=6, k=3, I=80, dtype="f32",
               seed=20, w_std=0.05, gate="computed", gate_std=0.1),
-    # more than 2048 tokens: 64-token ranking blocks, 4 tokens per wave
+    # more than 2048 tokens: 163 ranking blocks of 16 tokens
     MoEConfig(name="many_tokens", T=2600, H=128, E=40, k=3, I=128, seed=21, gate="drawn",
               zipf_s=1.1, zipf_alpha=0.5),
     # wide experts: 16 n-tiles of 128 in the gate/up GEMM and K = 2048 in the down
