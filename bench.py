@@ -17,6 +17,15 @@ stream the kernels run on.  The roofline object describes the dominant kernel
 event-timed duration, against MI355X's 8 TB/s HBM peak.  cpu_baseline is the
 CPU oracle (tests' reference implementation) timed on a bounded token sample of
 the same layer on this host's cores.
+
+Besides the contract's back-to-back steps, the line carries:
+  cold            layers run after a 1 GiB write that evicts every XCD's L2 and
+                  the 256 MB last-level cache (median / p95 of event times);
+  combine_alone   moe_combine on its own, fused and as the unpermute +
+                  weighted-reduce pair;
+  ep_rank_share   (--ep-rank-share R) the grouped expert FFN at the share one
+                  rank of R-way expert parallelism would run: R source batches
+                  routed on this GPU, the rows of experts [0, E/R) gathered.
 """
 from __future__ import annotations
 
@@ -51,6 +60,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         evs = []
@@ -66,6 +76,10 @@ class HipEvents:
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
         assert rc == 0, f"hipEventElapsedTime failed: {rc}"
         return ms.value
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        assert rc == 0, f"hipEventRecord failed: {rc}"
 
     def destroy(self, evs):
         for e in evs:
@@ -94,6 +108,100 @@ def stage_bytes_flops(cfg, counts):
     return st, touched
 
 
+def pct(vals, q):
+    """Nearest-rank q-th percentile."""
+    srt = sorted(vals)
+    return float(srt[max(0, -(-q * len(srt) // 100) - 1)])
+
+
+def time_combine_alone(B, torch, cfg, w, x, logits, od, s, ws, counts, stream, hip, reps=20):
+    """moe_combine on its own over one layer's y_perm: fused, and the unpermute +
+    weighted-reduce pair (UNFUSED); mean ms per call over `reps` calls each."""
+    dev = x.device
+    act = torch.int16 if cfg.dtype == "bf16" else torch.float32
+    yp = torch.empty((cfg.R, cfg.D), dtype=act, device=dev)
+    trow = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16 if od == B.MOE_BF16 else torch.float32, device=dev)
+    B.layer_forward(w, x, logits, out, od, s, ws, aux={"counts": counts, "y_perm": yp, "token_row": trow,
+                                                       "topk_w": tw}, stream=stream)
+    cod = B.MOE_BF16 if cfg.dtype == "bf16" and (cfg.L or od == B.MOE_BF16) else B.MOE_F32
+    oc = torch.empty((cfg.T, cfg.D), dtype=torch.int16 if cod == B.MOE_BF16 else torch.float32, device=dev)
+    wsc = torch.empty(max(B.workspace_bytes(s, B.MOE_CALL_COMBINE), 256), dtype=torch.uint8, device=dev)
+    res = {}
+    for name, flag in (("fused_ms", B.MOE_COMBINE_FUSED), ("unpermute_plus_reduce_ms", B.MOE_COMBINE_UNFUSED)):
+        B.combine(yp, trow, tw, oc, cod, flag, s, wsc, stream=stream)
+        e = hip.create(2)
+        hip.record(e[0], stream)
+        for _ in range(reps):
+            B.combine(yp, trow, tw, oc, cod, flag, s, wsc, stream=stream)
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        res[name] = round(hip.elapsed_ms(e[0], e[1]) / reps, 5)
+        hip.destroy(e)
+    return res
+
+
+def ep_rank_share(B, torch, np, gen, cfg, ranks, up, stream, hip, reps=10):
+    """The grouped expert FFN at one rank's share of `ranks`-way expert parallelism.
+
+    Every rank holds E / ranks experts and receives, from each of the `ranks`
+    source batches of T tokens (reseeded steps 0 .. ranks-1 of the same layer),
+    the rows routed to its experts.  The batches are routed on this GPU; the rows
+    of experts [0, E / ranks) form the rank-0 expert input (seeded random
+    activations: the values do not change the time), and moe_grouped_ffn runs
+    over them with those experts' weights."""
+    dev = torch.device("cuda:0")
+    assert cfg.E % ranks == 0, "experts must split evenly over the ranks"
+    el = cfg.E // ranks
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    cnt = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev)
+    lg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    wsr = torch.empty(max(B.workspace_bytes(s, B.MOE_CALL_ROUTE), 256), dtype=torch.uint8, device=dev)
+    gw = up(gen.gate_weight(cfg)) if cfg.gate == "computed" else None
+    bias = gen.zipf_bias(cfg)
+    bias = up(bias) if bias is not None else None
+    local = np.zeros(el, dtype=np.int64)
+    for r in range(ranks):
+        if cfg.gate == "computed":
+            B.route_topk(up(gen.activations(cfg, r)), gw, bias, lg, ids, tw, cnt, offs, s, wsr, stream=stream)
+        else:
+            B.route_topk(None, None, bias, up(gen.drawn_logits(cfg, r)), ids, tw, cnt, offs, s, wsr,
+                         stream=stream)
+        local += cnt.cpu().numpy()[:el]
+    rows = int(local.sum())
+    offsets = np.concatenate([[0], np.cumsum(local)]).astype(np.int32)
+    ls = B.shape(rows, cfg.H, el, 1, cfg.I, cfg.L, cfg.dtype)  # one row per assignment
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    xp = torch.randn((rows, cfg.D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+    ew = gen.expert_weights(cfg, experts=range(el))
+    w1, w3, w2 = up(ew["w1"]), up(ew["w3"]), up(ew["w2"])
+    yp = torch.empty((rows, cfg.D), dtype=torch.int16, device=dev)
+    wsf = torch.empty(max(B.workspace_bytes(ls, B.MOE_CALL_FFN), 256), dtype=torch.uint8, device=dev)
+    doffs = torch.from_numpy(offsets).to(dev)
+    B.grouped_ffn(xp, doffs, w1, w3, w2, yp, ls, wsf, stream=stream)
+    e = hip.create(2)
+    hip.record(e[0], stream)
+    for _ in range(reps):
+        B.grouped_ffn(xp, doffs, w1, w3, w2, yp, ls, wsf, stream=stream)
+    hip.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e[0], e[1]) / reps
+    hip.destroy(e)
+    flops = 6.0 * rows * cfg.D * cfg.I
+    wbytes = 3 * el * cfg.D * cfg.I * cfg.elem_bytes
+    log(f"ep rank share: {rows} rows over {el} experts, {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
+    return {"ranks": ranks, "local_experts": el, "rows": rows,
+            "rows_per_expert_mean": round(rows / el, 1), "rows_per_expert_max": int(local.max()),
+            "ms": round(ms, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "weight_bytes": wbytes, "weight_gbps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
@@ -116,8 +224,9 @@ def cpu_baseline(cfg, inp, target_s):
         sub["x"] = inp["x"][:n]
         if "logits" in inp:
             sub["logits"] = inp["logits"][:n]
+        timers = {}
         t0 = time.perf_counter()
-        oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16")
+        oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers)
         dt = time.perf_counter() - t0
         log(f"cpu oracle: {n} tokens in {dt:.2f} s")
         if dt >= target_s / 3 or n >= cfg.T:
@@ -127,15 +236,28 @@ def cpu_baseline(cfg, inp, target_s):
     if n >= cfg.T:
         while total < target_s:
             t0 = time.perf_counter()
-            oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16")
+            oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers)
             total += time.perf_counter() - t0
             runs += 1
         log(f"cpu oracle: whole layer {runs} times in {total:.2f} s")
     dt = total / runs
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    try:
+        blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                       if i.get("user_api") == "blas"})
+    except Exception:  # pragma: no cover
+        blas = []
     return {"value": n * cfg.k / dt, "unit": "assignments/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same layer (all {cfg.E} experts' "
-                      f"weights), float64 numpy oracle, {runs} run(s), {dt:.2f} s each"}
+                      f"weights), float64 numpy oracle, {runs} run(s), {dt:.2f} s each",
+            "stages_s": {k_: round(v / runs, 4) for k_, v in timers.items()},
+            "cpu_model": cpu, "blas": blas}
 
 
 def gate_up_kernel(cfg):
@@ -212,6 +334,10 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra layers timed after a 1 GiB cache-evicting write each (0: none)")
+    ap.add_argument("--ep-rank-share", type=int, default=0,
+                    help="time the grouped expert FFN at one rank's share of R-way expert parallelism")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB 3 times "
                          "(reference kernel of known size for HBM counter scaling)")
@@ -274,9 +400,35 @@ def main(argv=None):
 
     names = B.STAGE_NAMES
     stage_ms = {n: float(np.mean([hip.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, n in enumerate(names)}
-    layer_ev_ms = float(np.mean([hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]))
+    layer_list = [hip.elapsed_ms(e[0], e[nev - 1]) for e in evs]
+    layer_ev_ms = float(np.mean(layer_list))
     for e in evs:
         hip.destroy(e)
+
+    cold = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = [hip.create(nev) for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)  # same stream: the write ends before the layer starts
+            B.layer_forward(w, x, logits, out, od, s, ws, aux=aux, stage_events=cev[i], stream=stream)
+        torch.cuda.synchronize()
+        cl = [hip.elapsed_ms(e[0], e[nev - 1]) for e in cev]
+        cst = {n: float(np.median([hip.elapsed_ms(e[j], e[j + 1]) for e in cev]))
+               for j, n in enumerate(names)}
+        for e in cev:
+            hip.destroy(e)
+        del flush
+        cold = {"steps": args.cold_steps, "flush_bytes": 1 << 30,
+                "ms_per_layer_median": round(float(np.median(cl)), 5),
+                "ms_per_layer_p95": round(pct(cl, 95), 5),
+                "value_median": round(cfg.R / (float(np.median(cl)) * 1e-3), 1),
+                "stages_median_ms": cst}
+        log(f"cold: {cold['ms_per_layer_median']:.4f} ms per layer (median of {args.cold_steps})")
+
+    combine_alone = time_combine_alone(B, torch, cfg, w, x, logits, od, s, ws, counts, stream, hip)
+    ep_share = (ep_rank_share(B, torch, np, gen, cfg, args.ep_rank_share, up, stream, hip)
+                if args.ep_rank_share > 1 else None)
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -294,7 +446,11 @@ def main(argv=None):
     for n in names:
         byt, flp = sb[n]
         if byt == 0 and flp == 0:
+            if cold:
+                cold["stages_median_ms"].pop(n, None)
             continue
+        if cold:
+            cold["stages_median_ms"][n] = round(cold["stages_median_ms"][n], 5)
         t_s = stage_ms[n] * 1e-3
         stages[n] = {"ms": round(stage_ms[n], 5), "GB/s": round(byt / t_s / 1e9, 1) if t_s > 0 else None}
         if flp:
@@ -355,6 +511,11 @@ def main(argv=None):
         "permute_gbps": stages["permute"]["GB/s"],
         "combine_gbps": stages["combine"]["GB/s"],
         "layer_event_ms": round(layer_ev_ms, 5),
+        "layer_event_ms_median": round(float(np.median(layer_list)), 5),
+        "layer_event_ms_p95": round(pct(layer_list, 95), 5),
+        "cold": cold,
+        "combine_alone": combine_alone,
+        "ep_rank_share": ep_share,
         "stages": stages,
         "p95_skew": round(p95, 3) if p95 is not None else None,
         "touched_experts": touched,

@@ -37,6 +37,7 @@ the pages print).
 """
 from __future__ import annotations
 
+import time
 from typing import Dict, Optional
 
 import numpy as np
@@ -332,14 +333,26 @@ def route(scores_f32: np.ndarray, k: int, E: int) -> Dict[str, np.ndarray]:
     return {"ids": ids, "weights": w, "counts": counts, "offsets": segment_offsets(counts)}
 
 
-def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool) -> Dict[str, np.ndarray]:
+def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
+                  timers: Optional[Dict[str, float]] = None) -> Dict[str, np.ndarray]:
     """The whole routed-expert layer forward on one device, every stage kept.
 
     ``inp`` holds x, then either logits (given router output) or gate_w, an
     optional bias, w1 / w3 / w2, and wd / wu for latent layers.  Given logits
     are routed on fp32(logits + bias); computed logits are exact here and
-    rounded once to fp32 for the selection decision.
+    rounded once to fp32 for the selection decision.  ``timers`` (optional)
+    receives the wall-clock seconds of routing, permutation, expert FFN and
+    combine (the stage timers of Three Parameter Counts, "What the utilization
+    dashboard smooths away").
     """
+    clock = [time.perf_counter()]
+
+    def lap(name):
+        if timers is not None:
+            now = time.perf_counter()
+            timers[name] = timers.get(name, 0.0) + now - clock[0]
+            clock[0] = now
+
     res: Dict[str, np.ndarray] = {}
     if "logits" in inp:
         scores = router_scores(inp["logits"], inp.get("bias"))
@@ -349,6 +362,7 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool) -> 
         scores = lg.astype(np.float32)
     res["scores"] = scores
     res.update(route(scores, k, E))
+    lap("routing")
     rt, tr = permutation(res["ids"], E)
     res["row_token"], res["token_row"] = rt, tr
     if "wd" in inp:
@@ -357,13 +371,16 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool) -> 
     else:
         src = decode(inp["x"])
     res["x_perm"] = gather_rows(src, rt)
+    lap("permutation")
     res["y_perm"] = grouped_expert_ffn(res["x_perm"], res["offsets"], inp["w1"], inp["w3"],
                                        inp["w2"], bf16)
+    lap("expert_ffn")
     res["out_combine"] = combine(res["y_perm"], tr, res["weights"])
     if "wu" in inp:
         res["out"] = latent_up(res["out_combine"], inp["wu"], bf16)
     else:
         res["out"] = res["out_combine"]
+    lap("combine")
     return res
 
 
