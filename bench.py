@@ -9,7 +9,8 @@ HBM before timing starts.  Prints ONE JSON line.
 
 The default workload is the Qwen3-30B-A3B-shaped layer (T=4096, H=2048,
 E=128, k=8, I=768, bf16).  Other configs: deepseek_r1_shaped,
-k3_shaped_decode, latent_moe, tiny_f32.
+k3_shaped_decode, latent_moe, tiny_f32, deepseek_r1_shaped_shared (the
+R1-shaped layer with a shared expert of width 2048).
 
 Per-stage times come from HIP events that moe_layer_forward records on the
 stream the kernels run on.  The roofline object describes the dominant kernel
@@ -103,7 +104,10 @@ def stage_bytes_flops(cfg, counts):
     st["permute"] = (T * D * b + R * D * b + 12 * R, 0)
     st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
     st["gemm_down"] = (touched * D * I * b + R * I * b + R * D * b, 2 * R * D * I)
-    st["combine"] = (R * D * b + 8 * R + T * D * (b if L else out_b), 0)
+    Is = cfg.shared_I
+    st["shared_expert"] = ((T * H * b + 3 * Is * H * b + 2 * T * Is * b + T * H * b, 6 * T * H * Is)
+                           if Is else (0, 0))
+    st["combine"] = (R * D * b + 8 * R + T * D * (b if L else out_b) + (T * D * b if Is else 0), 0)
     st["latent_up"] = (T * L * b + H * L * b + T * H * out_b, 2 * T * L * H) if L else (0, 0)
     return st, touched
 
@@ -363,12 +367,12 @@ def main(argv=None):
     t0 = time.perf_counter()
     inp = gen.layer_inputs(cfg)
     log(f"inputs generated in {time.perf_counter() - t0:.1f} s")
-    w = {n: up(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu") if n in inp}
+    w = {n: up(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu", "ws1", "ws3", "ws2") if n in inp}
     if "bias" in inp:
         w["gate_bias"] = up(inp["bias"])
     x = up(inp["x"])
     logits = up(inp["logits"]) if "logits" in inp else torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype)
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I)
     ws = torch.empty(B.workspace_bytes(s, B.MOE_CALL_LAYER), dtype=torch.uint8, device=dev)
     od = B.MOE_BF16 if args.out_dtype == "bf16" and cfg.dtype == "bf16" else B.MOE_F32
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16 if od == B.MOE_BF16 else torch.float32, device=dev)

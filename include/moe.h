@@ -46,8 +46,8 @@
  *   token; offsets are the exclusive prefix sum of the per-expert counts.
  *
  * Limits: 1 <= k <= E, E <= 1024, k <= 64; T*k < 2^31; bf16 layers need D % 64 == 0,
- * I % 64 == 0 and (for latent layers) H % 64 == 0; fp32 layers need D % 4 == 0
- * and H % 4 == 0.
+ * I % 64 == 0, (latent layers) H % 64 == 0 and (shared expert) shared_I % 64 == 0;
+ * fp32 layers need D % 4 == 0 and H % 4 == 0.  A shared expert needs L == 0.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 #ifndef MOE_API
 #define MOE_API __attribute__((visibility("default")))
@@ -89,11 +89,11 @@ typedef enum moe_call {
 #define MOE_COMBINE_UNFUSED 1 /* two kernels: unpermute to token order, then weighted reduce */
 
 /* Stage events recorded by moe_layer_forward when `stage_events` is non-NULL. */
-#define MOE_NUM_STAGE_EVENTS 9
+#define MOE_NUM_STAGE_EVENTS 10
 /* [0] start  [1] after latent down-projection  [2] after gate  [3] after top-k+count+scan
  * [4] after permute  [5] after expert gate/up GEMM  [6] after expert down GEMM
- * [7] after combine  [8] after latent up-projection.  Stages that do not run leave
- * two consecutive events back to back. */
+ * [7] after the shared expert  [8] after combine  [9] after latent up-projection.
+ * Stages that do not run leave two consecutive events back to back. */
 
 typedef struct moe_shape {
   int64_t T;      /* tokens */
@@ -103,7 +103,7 @@ typedef struct moe_shape {
   int64_t I;      /* expert intermediate width */
   int64_t L;      /* latent dispatch width, 0 = none */
   int32_t dtype;  /* moe_dtype */
-  int32_t reserved;  /* must be 0 */
+  int32_t shared_I;  /* intermediate width of the shared expert, 0 = no shared expert */
 } moe_shape;
 
 /* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
@@ -194,18 +194,23 @@ MOE_API moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, c
  * volume as dispatch).
  *
  * y_perm    [T*k x D] (dtype), token_row [T x k] int32, topk_w [T x k] fp32.
+ * shared_out[T x D] (dtype), nullable: the shared expert's output, added with
+ *           weight 1 (a shared expert runs for every token whatever the router
+ *           picks: "Three Parameter Counts...", "What the utilization dashboard
+ *           smooths away").
  * out       [T x D] out, element type out_dtype (MOE_F32 or MOE_BF16):
- *           out[t] = sum_{j=0..k-1} topk_w[t,j] * y_perm[token_row[t,j]], fp32
- *           accumulation in ascending j, one rounding to out_dtype.  The bf16
- *           result is the round-to-nearest-even of the fp32 result.
+ *           out[t] = sum_{j=0..k-1} topk_w[t,j] * y_perm[token_row[t,j]]
+ *           (+ shared_out[t]), fp32 accumulation in ascending j, the shared term
+ *           added last, one rounding to out_dtype.  The bf16 result is the
+ *           round-to-nearest-even of the fp32 result.
  * flags     MOE_COMBINE_FUSED (one kernel) or MOE_COMBINE_UNFUSED (unpermute to
  *           token order in the workspace, then the weighted reduce: the separate
  *           "unpermutation" and "combine" timers of "Three Parameter Counts...",
  *           "What the utilization dashboard smooths away").  Same result bits.
  */
 MOE_API moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
-                       void* out, int out_dtype, int flags, const moe_shape* s, void* ws,
-                       size_t ws_bytes, void* stream);
+                       const void* shared_out, void* out, int out_dtype, int flags,
+                       const moe_shape* s, void* ws, size_t ws_bytes, void* stream);
 
 /* Weights of one layer for moe_layer_forward (device pointers, layouts as above). */
 typedef struct moe_layer_weights {
@@ -216,6 +221,9 @@ typedef struct moe_layer_weights {
   const void* w2;          /* [E x D x I] */
   const void* wd;          /* [L x H], latent layers only */
   const void* wu;          /* [H x L], latent layers only */
+  const void* ws1;         /* [shared_I x H] shared expert gate branch, when shared_I > 0 */
+  const void* ws3;         /* [shared_I x H] shared expert up branch */
+  const void* ws2;         /* [H x shared_I] shared expert down projection */
 } moe_layer_weights;
 
 /* Optional caller buffers that expose the intermediate results (each nullable;
@@ -242,6 +250,13 @@ typedef struct moe_layer_aux {
  * Latent layers (s->L > 0) follow "Latent MoE" (Definition; Current Synthesis):
  * the router scores the full-width X, the rows dispatched are Z = X wd^T, and the
  * combined latent output (rounded to dtype) is projected back: out = out_L wu^T.
+ *
+ * Shared expert (s->shared_I > 0, non-latent layers): a SwiGLU FFN that every
+ * token passes through regardless of the router ("Three Parameter Counts...",
+ * "What the utilization dashboard smooths away"; it is replicated with the
+ * non-expert weights, research-vault claim IX2-0406):
+ * Ys = (SiLU(X ws1^T) * (X ws3^T)) ws2^T with the intermediate and Ys rounded to
+ * dtype, added in the combine as its shared_out term.
  *
  * x       [T x H] (dtype).
  * logits  [T x E] fp32: input when w->gate_w == NULL, else output (nullable: then

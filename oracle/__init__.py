@@ -12,11 +12,11 @@ brute-force, closed-form and special-case checks on small layers.
 from .moe_oracle import (decode, round_bf16, round_f32, gate_logits, router_scores, topk_ids,
                          routing_weights, routing_margins, expert_counts, segment_offsets,
                          permutation, gather_rows, dispatch_bytes, silu, expert_ffn_rows,
-                         grouped_expert_ffn, combine, latent_down, latent_up, route,
-                         layer_forward, token_outputs, load_skew, p95_nearest_rank)
+                         grouped_expert_ffn, shared_expert_ffn, combine, latent_down, latent_up,
+                         route, layer_forward, token_outputs, load_skew, p95_nearest_rank)
 
 __all__ = ["decode", "round_bf16", "round_f32", "gate_logits", "router_scores", "topk_ids",
            "routing_weights", "routing_margins", "expert_counts", "segment_offsets",
            "permutation", "gather_rows", "dispatch_bytes", "silu", "expert_ffn_rows",
-           "grouped_expert_ffn", "combine", "latent_down", "latent_up", "route",
+           "grouped_expert_ffn", "shared_expert_ffn", "combine", "latent_down", "latent_up", "route",
            "layer_forward", "token_outputs", "load_skew", "p95_nearest_rank"]

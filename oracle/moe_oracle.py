@@ -277,22 +277,40 @@ def grouped_expert_ffn(x_perm: np.ndarray, offsets: np.ndarray, w1: np.ndarray, 
     return y
 
 
+def shared_expert_ffn(x: np.ndarray, ws1: np.ndarray, ws3: np.ndarray, ws2: np.ndarray,
+                      bf16: bool) -> np.ndarray:
+    """The shared expert: a SwiGLU FFN that every token passes through, whatever
+    the router picked ("Three Parameter Counts...", "What the utilization dashboard
+    smooths away": DeepSeekMoE-style shared experts run regardless of the router
+    score; it is one of the non-expert weights every rank replicates,
+    research-vault claim IX2-0406).  The pages give no formula; it is read as an
+    expert of the routed experts' form (and rounding points) with its own
+    intermediate width, on all T rows of the full-width state.  ws1, ws3 are
+    [Is x H], ws2 [H x Is].
+    """
+    return expert_ffn_rows(x, ws1, ws3, ws2, bf16)
+
+
 # --------------------------------------------------------------------------------------
 # a6: combine (unpermute + routing weights)
 # --------------------------------------------------------------------------------------
 
 
-def combine(y_perm: np.ndarray, token_row: np.ndarray, weights: np.ndarray) -> np.ndarray:
-    """out[t] = sum_j w[t, j] * Y[token_row[t, j]], summed over ascending j, exact.
+def combine(y_perm: np.ndarray, token_row: np.ndarray, weights: np.ndarray,
+            shared: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = sum_j w[t, j] * Y[token_row[t, j]] (+ shared[t]), exact.
 
     The combine reverses the route, then the source unpermutes and applies the
     routing weights (WideEP explainer, "The router writes a network schedule").
+    A shared expert's output, when present, enters with weight 1.
     """
     y = decode(y_perm) if y_perm.dtype == np.uint16 else np.asarray(y_perm, dtype=np.float64)
     T, k = token_row.shape
     out = np.zeros((T, y.shape[1]), dtype=np.float64)
     for j in range(k):
         out += weights[:, j:j + 1] * y[token_row[:, j]]
+    if shared is not None:
+        out += decode(shared) if shared.dtype == np.uint16 else np.asarray(shared, dtype=np.float64)
     return out
 
 
@@ -338,7 +356,8 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
     """The whole routed-expert layer forward on one device, every stage kept.
 
     ``inp`` holds x, then either logits (given router output) or gate_w, an
-    optional bias, w1 / w3 / w2, and wd / wu for latent layers.  Given logits
+    optional bias, w1 / w3 / w2, wd / wu for latent layers and ws1 / ws3 / ws2
+    for a shared expert (non-latent layers).  Given logits
     are routed on fp32(logits + bias); computed logits are exact here and
     rounded once to fp32 for the selection decision.  ``timers`` (optional)
     receives the wall-clock seconds of routing, permutation, expert FFN and
@@ -375,7 +394,11 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
     res["y_perm"] = grouped_expert_ffn(res["x_perm"], res["offsets"], inp["w1"], inp["w3"],
                                        inp["w2"], bf16)
     lap("expert_ffn")
-    res["out_combine"] = combine(res["y_perm"], tr, res["weights"])
+    if "ws1" in inp:
+        assert "wd" not in inp, "shared expert on non-latent layers only"
+        res["y_shared"] = shared_expert_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"], bf16)
+    lap("shared_expert")
+    res["out_combine"] = combine(res["y_perm"], tr, res["weights"], res.get("y_shared"))
     if "wu" in inp:
         res["out"] = latent_up(res["out_combine"], inp["wu"], bf16)
     else:
@@ -387,7 +410,8 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
 def token_outputs(inp: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarray,
                   weights: np.ndarray, expert_w: Dict[int, tuple], *, bf16: bool,
                   z: Optional[np.ndarray] = None) -> np.ndarray:
-    """Layer output of selected tokens only: out[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x_t).
+    """Layer output of selected tokens only: out[t] = sum_j w[t, j] * FFN_{ids[t, j]}(x_t)
+    (+ the shared expert's FFN(x_t) when ``inp`` holds ws1 / ws3 / ws2).
 
     For full-size layers.  ``ids`` / ``weights`` are [len(tokens) x k] for the
     selected tokens, ``expert_w[e] = (w1e, w3e, w2e)`` for every expert they
@@ -409,6 +433,8 @@ def token_outputs(inp: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarra
     for j in range(k):
         for i in range(n):
             out[i] += weights[i, j] * y[(i, int(ids[i, j]))]
+    if "ws1" in inp:
+        out += shared_expert_ffn(np.asarray(inp["x"])[tokens], inp["ws1"], inp["ws3"], inp["ws2"], bf16)
     if "wu" in inp:
         out = latent_up(out, inp["wu"], bf16)
     return out

@@ -18,11 +18,11 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_FFN, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
 MOE_COMBINE_FUSED, MOE_COMBINE_UNFUSED = 0, 1
-MOE_NUM_STAGE_EVENTS = 9
-ABI_VERSION = 1
+MOE_NUM_STAGE_EVENTS = 10
+ABI_VERSION = 2
 
 STAGE_NAMES = ["latent_down", "gate", "route", "permute", "gemm_gate_up", "gemm_down",
-               "combine", "latent_up"]
+               "shared_expert", "combine", "latent_up"]
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -37,12 +37,12 @@ class MoeError(RuntimeError):
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", _i64), ("H", _i64), ("E", _i64), ("k", _i64), ("I", _i64), ("L", _i64),
-                ("dtype", _i32), ("reserved", _i32)]
+                ("dtype", _i32), ("shared_I", _i32)]
 
 
 class MoeLayerWeights(ctypes.Structure):
     _fields_ = [("gate_w", _vp), ("gate_bias", _vp), ("w1", _vp), ("w3", _vp), ("w2", _vp),
-                ("wd", _vp), ("wu", _vp)]
+                ("wd", _vp), ("wu", _vp), ("ws1", _vp), ("ws3", _vp), ("ws2", _vp)]
 
 
 class MoeLayerAux(ctypes.Structure):
@@ -70,8 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_route_topk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
     lib.moe_dispatch_permute.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
     lib.moe_grouped_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
-    lib.moe_combine.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, P(MoeShape), _vp,
-                                sz, _vp]
+    lib.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, P(MoeShape),
+                                _vp, sz, _vp]
     lib.moe_layer_forward.argtypes = [P(MoeLayerWeights), _vp, _vp, _vp, ctypes.c_int,
                                       P(MoeShape), P(MoeLayerAux), P(_vp), _vp, sz, _vp]
     for f in ("moe_route_topk", "moe_dispatch_permute", "moe_grouped_ffn", "moe_combine",
@@ -90,8 +90,9 @@ def status_string(status: int) -> str:
     return lib.moe_status_string(int(status)).decode()
 
 
-def shape(T: int, H: int, E: int, k: int, I: int, L: int = 0, dtype: str = "bf16") -> MoeShape:
-    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, 0)
+def shape(T: int, H: int, E: int, k: int, I: int, L: int = 0, dtype: str = "bf16",
+          shared_I: int = 0) -> MoeShape:
+    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, shared_I)
 
 
 def workspace_bytes(s: MoeShape, call: int) -> int:
@@ -144,15 +145,16 @@ def grouped_ffn(x_perm, offsets, w1, w3, w2, y_perm, s: MoeShape, ws, stream=Non
 
 
 def combine(y_perm, token_row, topk_w, out, out_dtype: int, flags: int, s: MoeShape, ws,
-            stream=None):
+            stream=None, shared_out=None):
     _check("moe_combine", lib.moe_combine(
-        _p(y_perm), _p(token_row), _p(topk_w), _p(out), int(out_dtype), int(flags),
+        _p(y_perm), _p(token_row), _p(topk_w), _p(shared_out), _p(out), int(out_dtype), int(flags),
         ctypes.byref(s), _p(ws), _nbytes(ws), _stream(stream)))
 
 
 def layer_forward(weights: dict, x, logits, out, out_dtype: int, s: MoeShape, ws, aux: dict = None,
                   stage_events=None, stream=None):
-    """weights: gate_w, gate_bias, w1, w3, w2, wd, wu (tensors or None); aux: moe_layer_aux fields."""
+    """weights: gate_w, gate_bias, w1, w3, w2, wd, wu, ws1, ws3, ws2 (tensors or None);
+    aux: moe_layer_aux fields."""
     w = MoeLayerWeights(*[_p(weights.get(f)) for f, _ in MoeLayerWeights._fields_])
     a = MoeLayerAux(*[_p((aux or {}).get(f)) for f, _ in MoeLayerAux._fields_])
     ev = None

@@ -5,10 +5,12 @@
 // schedule"); it moves about the same volume as the dispatch ("Top-k
 // multiplies traffic. Locality subtracts it.").
 //
-// out[t] = sum_j w[t,j] * Y[token_row[t,j]] with one fp32 fma per term in
-// ascending j and one rounding to the output type.  The fused kernel gathers
-// the k rows directly; the unfused pair first unpermutes into token order and
-// then reduces, with the same fma sequence, so both give the same bits.
+// out[t] = sum_j w[t,j] * Y[token_row[t,j]] (+ add[t]) with one fp32 fma per
+// term in ascending j, the optional addend (a shared expert's output, which
+// every token receives with weight 1) added last, and one rounding to the output
+// type.  The fused kernel gathers the k rows directly; the unfused pair first
+// unpermutes into token order and then reduces, with the same fma sequence, so
+// both give the same bits.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -58,13 +60,23 @@ __device__ __forceinline__ void store_out(void* out, size_t elem0, const float* 
   }
 }
 
+// acc[i] += the addend's 16-byte chunk, element by element in fp32
+template <typename IT>
+__device__ __forceinline__ void add_row(float* acc, uint4 v) {
+  float f[Vec16<IT>::n];
+  Vec16<IT>::unpack(v, f);
+#pragma unroll
+  for (int i = 0; i < Vec16<IT>::n; ++i) acc[i] += f[i];
+}
+
 constexpr int kCombTokPerWg = 4;  // one wave per token
 
 // Fused: one wave per token, each lane owns 16-byte column chunks of the row.
 template <typename IT>
 __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, int row16,
                                                  const int32_t* __restrict__ token_row,
-                                                 const float* __restrict__ topk_w, int T, int k,
+                                                 const float* __restrict__ topk_w,
+                                                 const uint4* __restrict__ add, int T, int k,
                                                  void* __restrict__ out, int out_f32) {
   constexpr int NV = Vec16<IT>::n;
   const int lane = threadIdx.x & 63;
@@ -108,6 +120,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
     }
+    if (add) add_row<IT>(acc, add[(size_t)t * row16 + c]);
     store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
   }
 }
@@ -128,7 +141,8 @@ __global__ __launch_bounds__(256) void k_unpermute(const uint4* __restrict__ y, 
 // Unfused step 2: out[t] = sum_j w[t, j] * y_tok[t*k + j], same fma order as k_combine.
 template <typename IT>
 __global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict__ y_tok, int row16,
-                                                         const float* __restrict__ topk_w, int T,
+                                                         const float* __restrict__ topk_w,
+                                                         const uint4* __restrict__ add, int T,
                                                          int k, void* __restrict__ out,
                                                          int out_f32) {
   constexpr int NV = Vec16<IT>::n;
@@ -146,12 +160,14 @@ __global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
     }
+    if (add) add_row<IT>(acc, add[(size_t)t * row16 + c]);
     store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
   }
 }
 
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
-                          const float* w, int T, int k, void* out, bool out_f32, hipStream_t st) {
+                          const float* w, const void* add, int T, int k, void* out, bool out_f32,
+                          hipStream_t st) {
   // split columns until ~1024 workgroups (small token counts)
   const int gx = ceil_div(T, kCombTokPerWg);
   int cs = 1;
@@ -159,10 +175,10 @@ hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t*
   const dim3 g(gx, cs), b(256);
   if (in_bf16)
     hipLaunchKernelGGL(k_combine<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y), row16,
-                       token_row, w, T, k, out, (int)out_f32);
+                       token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   else
     hipLaunchKernelGGL(k_combine<float>, g, b, 0, st, static_cast<const uint4*>(y), row16,
-                       token_row, w, T, k, out, (int)out_f32);
+                       token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   return hipGetLastError();
 }
 
@@ -174,14 +190,15 @@ hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, 
 }
 
 hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
-                                  int T, int k, void* out, bool out_f32, hipStream_t st) {
+                                  const void* add, int T, int k, void* out, bool out_f32,
+                                  hipStream_t st) {
   const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
   if (in_bf16)
     hipLaunchKernelGGL(k_weighted_reduce<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, w, T, k, out, (int)out_f32);
+                       row16, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   else
     hipLaunchKernelGGL(k_weighted_reduce<float>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, w, T, k, out, (int)out_f32);
+                       row16, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   return hipGetLastError();
 }
 

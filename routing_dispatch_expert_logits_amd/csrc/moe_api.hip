@@ -30,12 +30,13 @@ bool al16_or_null(const void* p) { return !p || al16(p); }
 
 struct Dims {
   int T, H, E, k, I, L, D, R, nb, es;
+  int Is;  // shared expert intermediate width, 0 = none
   bool bf16;
 };
 
 moe_status check_shape(const moe_shape* s, Dims& d) {
   if (!s) return MOE_ERR_INVALID_ARG;
-  if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->L < 0 || s->reserved != 0)
+  if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->L < 0 || s->shared_I < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
@@ -45,12 +46,14 @@ moe_status check_shape(const moe_shape* s, Dims& d) {
   d.T = (int)s->T; d.H = (int)s->H; d.E = (int)s->E; d.k = (int)s->k; d.I = (int)s->I;
   d.L = (int)s->L; d.D = d.L ? d.L : d.H; d.R = d.T * d.k;
   d.nb = ceil_div(d.T, block_tokens(d.T));
+  d.Is = s->shared_I;
   d.bf16 = s->dtype == MOE_BF16;
   d.es = d.bf16 ? 2 : 4;
+  if (d.Is && d.L) return MOE_ERR_UNSUPPORTED;  // shared expert on non-latent layers only
   if (d.bf16) {
-    if (d.D % 64 || d.I % 64 || (d.L && d.H % 64)) return MOE_ERR_UNSUPPORTED;
+    if (d.D % 64 || d.I % 64 || (d.L && d.H % 64) || d.Is % 64) return MOE_ERR_UNSUPPORTED;
   } else {
-    if (d.D % 4 || d.H % 4) return MOE_ERR_UNSUPPORTED;
+    if (d.D % 4 || d.H % 4 || d.Is % 4) return MOE_ERR_UNSUPPORTED;
   }
   // element counts addressed with int inside some kernels
   if ((long long)d.R * d.D / 8 > INT_MAX || (long long)d.T * d.E > INT_MAX) return MOE_ERR_UNSUPPORTED;
@@ -94,7 +97,7 @@ CombWs comb_ws(const Dims& d) {
 
 struct LayerWs {
   size_t logits, ids, w, counts, offsets, row_token, token_row, bc, gpart, mtile, z, xperm, act, outl,
-      total;
+      soffs, smtile, sact, sy, total;
 };
 LayerWs layer_ws(const Dims& d) {
   Carve c; LayerWs w;
@@ -112,8 +115,24 @@ LayerWs layer_ws(const Dims& d) {
   w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
   w.act = c.take((size_t)d.R * d.I * d.es);
   w.outl = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
+  // shared expert: one group of T rows
+  w.soffs = c.take(d.Is ? 2 * 4 : 0);
+  w.smtile = c.take(d.Is ? 2 * 2 * 4 : 0);
+  w.sact = c.take((size_t)d.T * d.Is * d.es);
+  w.sy = c.take(d.Is ? (size_t)d.T * d.H * d.es : 0);
   w.total = c.cur;
   return w;
+}
+
+// The shared expert's FFN as a grouped FFN of one expert over all T rows.
+Dims shared_dims(const Dims& d) {
+  Dims s = d;
+  s.E = 1;
+  s.k = 1;
+  s.R = d.T;
+  s.I = d.Is;
+  s.D = d.H;
+  return s;
 }
 
 template <typename P>
@@ -272,26 +291,28 @@ moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const voi
 }
 
 moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
-                       void* out, int out_dtype, int flags, const moe_shape* s, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const void* shared_out, void* out, int out_dtype, int flags,
+                       const moe_shape* s, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   moe_status rc = check_shape(s, d);
   if (rc != MOE_OK) return rc;
-  if (!al16(y_perm) || !al16(token_row) || !al16(topk_w) || !al16(out)) return MOE_ERR_INVALID_ARG;
+  if (!al16(y_perm) || !al16(token_row) || !al16(topk_w) || !al16(out) || !al16_or_null(shared_out))
+    return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (flags != MOE_COMBINE_FUSED && flags != MOE_COMBINE_UNFUSED) return MOE_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int row16 = d.D * d.es / 16;
   const bool of32 = out_dtype == MOE_F32;
   if (flags == MOE_COMBINE_FUSED) {
-    MOE_HIP(launch_combine(y_perm, row16, d.bf16, token_row, topk_w, d.T, d.k, out, of32, st));
+    MOE_HIP(launch_combine(y_perm, row16, d.bf16, token_row, topk_w, shared_out, d.T, d.k, out, of32,
+                           st));
     return MOE_OK;
   }
   const CombWs w = comb_ws(d);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   void* ytok = at<void>(ws, w.ytok);
   MOE_HIP(launch_unpermute(y_perm, row16, token_row, d.R, ytok, st));
-  MOE_HIP(launch_weighted_reduce(ytok, row16, d.bf16, topk_w, d.T, d.k, out, of32, st));
+  MOE_HIP(launch_weighted_reduce(ytok, row16, d.bf16, topk_w, shared_out, d.T, d.k, out, of32, st));
   return MOE_OK;
 }
 
@@ -307,6 +328,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     return MOE_ERR_INVALID_ARG;
   if (!wt->gate_w && !logits) return MOE_ERR_INVALID_ARG;  // given logits are required
   if (d.L && (!al16(wt->wd) || !al16(wt->wu))) return MOE_ERR_INVALID_ARG;
+  if (d.Is && (!al16(wt->ws1) || !al16(wt->ws3) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (!d.bf16 && d.L && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   moe_layer_aux none = {};
@@ -380,19 +402,32 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
                              d.E, d.D, d.I, st));
   }
   if (!ev(6)) return MOE_ERR_HIP;
+  // shared expert: every token, whatever the router picked
+  void* sy = nullptr;
+  if (d.Is) {
+    const Dims ds = shared_dims(d);
+    int32_t* soffs = at<int32_t>(ws, w.soffs);
+    int32_t* smtile = at<int32_t>(ws, w.smtile);
+    sy = at<void>(ws, w.sy);
+    MOE_HIP(launch_single_group(d.T, soffs, gemm_bm(expert_kind(ds)), smtile, st));
+    rc = expert_ffn(ds, x, soffs, smtile, wt->ws1, wt->ws3, wt->ws2, at<void>(ws, w.sact), sy, st);
+    if (rc != MOE_OK) return rc;
+  }
+  if (!ev(7)) return MOE_ERR_HIP;
   // a6
   const int row16 = d.D * d.es / 16;
   if (d.L) {
-    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, d.T, d.k, outl, !d.bf16, st));
+    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, nullptr, d.T, d.k, outl, !d.bf16, st));
   } else {
-    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, d.T, d.k, out, out_dtype == MOE_F32, st));
+    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, sy, d.T, d.k, out, out_dtype == MOE_F32,
+                           st));
   }
-  if (!ev(7)) return MOE_ERR_HIP;
+  if (!ev(8)) return MOE_ERR_HIP;
   if (d.L) {  // a7: out = out_L wu^T
     rc = dense_proj(d, outl, wt->wu, out, d.T, d.H, d.L, out_dtype == MOE_F32, st);
     if (rc != MOE_OK) return rc;
   }
-  if (!ev(8)) return MOE_ERR_HIP;
+  if (!ev(9)) return MOE_ERR_HIP;
   return MOE_OK;
 }
 

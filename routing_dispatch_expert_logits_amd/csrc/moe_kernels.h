@@ -36,12 +36,17 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
                           const int32_t* offsets, const int32_t* bases, void* x_perm,
                           int32_t* row_token, int32_t* token_row, hipStream_t st);
+// add: nullable [T x row16 x 16 B] addend of the input element type, added after the k terms.
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
-                          const float* w, int T, int k, void* out, bool out_f32, hipStream_t st);
+                          const float* w, const void* add, int T, int k, void* out, bool out_f32,
+                          hipStream_t st);
 hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
                             hipStream_t st);
 hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
-                                  int T, int k, void* out, bool out_f32, hipStream_t st);
+                                  const void* add, int T, int k, void* out, bool out_f32,
+                                  hipStream_t st);
+// One group of T rows: offsets = {0, T} and the m-tile tables (tile heights bm, 2 bm) for E = 1.
+hipError_t launch_single_group(int T, int32_t* offsets, int bm, int32_t* mtile_start, hipStream_t st);
 // bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.
 // mtile_start holds the m-tile tables for tile heights gemm_bm(kind) and 2 * gemm_bm(kind)
 // (E + 1 entries each, as written by launch_offsets).

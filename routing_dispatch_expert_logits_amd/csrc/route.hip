@@ -204,6 +204,18 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
+// One group of T rows (the shared expert's GEMMs run as a single expert).
+__global__ void k_single_group(int T, int32_t* __restrict__ offsets, int bm,
+                               int32_t* __restrict__ mtile_start) {
+  if (threadIdx.x != 0) return;
+  offsets[0] = 0;
+  offsets[1] = T;
+  mtile_start[0] = 0;
+  mtile_start[1] = ceil_div(T, bm);
+  mtile_start[2] = 0;
+  mtile_start[3] = ceil_div(T, 2 * bm);
+}
+
 // ------------------------------------------------------------------ launchers
 
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
@@ -237,6 +249,11 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
                           int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st) {
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, counts, offsets_in, E, offsets_out, bm,
                      mtile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_single_group(int T, int32_t* offsets, int bm, int32_t* mtile_start, hipStream_t st) {
+  hipLaunchKernelGGL(k_single_group, dim3(1), dim3(64), 0, st, T, offsets, bm, mtile_start);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def ws(s: B.MoeShape, call: int) -> torch.Tensor:
 
 
 def shape_of(cfg) -> B.MoeShape:
-    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype)
+    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I)
 
 
 def act_kind(cfg) -> str:
@@ -70,3 +70,20 @@ def check_permutation_valid(ids: np.ndarray, offsets: np.ndarray, row_token: np.
     for e in range(E):
         s = row_token[offsets[e]:offsets[e + 1]]
         assert np.all(np.diff(s) > 0)
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """One bf16 unit in the last place at |v| (8 significant bits)."""
+    return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-30))) - 7)
+
+
+def out_err_over_rms(got: np.ndarray, ref: np.ndarray, shared_ref=None) -> float:
+    """max |got - ref| / RMS(ref).  With a shared expert, one bf16 ulp of its output
+    is allowed per element first: both sides round that output to bf16 at the same
+    point, an element near a rounding midpoint can land one ulp apart (fp32 sums vs
+    exact ones), and the shared term enters with weight 1 instead of a routing
+    weight, so the flip is not diluted."""
+    err = np.abs(got - ref)
+    if shared_ref is not None:
+        err = np.maximum(err - bf16_ulp(shared_ref), 0.0)
+    return float(err.max() / np.sqrt(np.mean(ref ** 2)))

@@ -48,7 +48,8 @@ def test_abi_version_and_status_strings():
 
 
 def _bytes(cfg, call):
-    return B.workspace_bytes(B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype), call)
+    return B.workspace_bytes(B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I),
+                             call)
 
 
 @pytest.mark.parametrize("cfg", list(FULL_CONFIGS.values()) + list(PARITY_CONFIGS.values()),
@@ -56,13 +57,15 @@ def _bytes(cfg, call):
 def test_workspace_sizes(cfg):
     R, D, es = cfg.R, cfg.D, cfg.elem_bytes
     route = _bytes(cfg, B.MOE_CALL_ROUTE)
-    assert route >= ((cfg.T + 63) // 64) * cfg.E * 4
+    assert route >= ((cfg.T + 15) // 16) * cfg.E * 4       # per 16-token ranking block counts
     assert _bytes(cfg, B.MOE_CALL_FFN) >= R * cfg.I * es
     assert _bytes(cfg, B.MOE_CALL_COMBINE) >= R * D * es
     layer = _bytes(cfg, B.MOE_CALL_LAYER)
-    assert layer >= R * D * es + R * cfg.I * es
+    shared = cfg.T * (cfg.shared_I + cfg.H) * es if cfg.shared_I else 0  # shared expert A and Y
+    assert layer >= R * D * es + R * cfg.I * es + shared
     # one permuted-row buffer serves both x_perm and y_perm
-    assert layer < 2 * R * D * es + R * cfg.I * es + 2 * cfg.T * max(cfg.L, 1) * es + 64 * 1024 * 1024
+    assert layer < (2 * R * D * es + R * cfg.I * es + 2 * cfg.T * max(cfg.L, 1) * es + shared
+                    + 64 * 1024 * 1024)
 
 
 def test_invalid_shapes_have_no_workspace():
@@ -93,8 +96,10 @@ def test_route_rejects_bad_arguments_on_host():
     assert _route(s, ws_bytes=16) == B.MOE_ERR_WORKSPACE
     assert _route(s, ws=None) == B.MOE_ERR_WORKSPACE
     bad = B.shape(64, 128, 8, 2, 256)
-    bad.reserved = 1
+    bad.shared_I = -1
     assert _route(bad) == B.MOE_ERR_INVALID_ARG
+    assert _route(B.shape(64, 128, 8, 2, 256, shared_I=96)) == B.MOE_ERR_UNSUPPORTED   # bf16: % 64
+    assert _route(B.shape(64, 128, 8, 2, 256, L=64, shared_I=128)) == B.MOE_ERR_UNSUPPORTED  # latent
     bad = B.shape(64, 128, 8, 2, 256)
     bad.dtype = 7
     assert _route(bad) == B.MOE_ERR_INVALID_ARG
@@ -111,13 +116,15 @@ def test_other_calls_reject_bad_arguments_on_host():
                              None) == B.MOE_ERR_INVALID_ARG
     assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 8,
                              None) == B.MOE_ERR_WORKSPACE
-    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 5, 0, ctypes.byref(s), FAKE, 1 << 30,
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, FAKE, 5, 0, ctypes.byref(s), FAKE, 1 << 30,
                          None) == B.MOE_ERR_INVALID_ARG                     # out dtype
-    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 0, 3, ctypes.byref(s), FAKE, 1 << 30,
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, FAKE, 0, 3, ctypes.byref(s), FAKE, 1 << 30,
                          None) == B.MOE_ERR_INVALID_ARG                     # flags
-    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE, 0, B.MOE_COMBINE_UNFUSED, ctypes.byref(s), FAKE, 8,
-                         None) == B.MOE_ERR_WORKSPACE
-    w = B.MoeLayerWeights(None, None, FAKE, FAKE, FAKE, None, None)
+    assert L.moe_combine(FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0, 0, ctypes.byref(s), FAKE, 1 << 30,
+                         None) == B.MOE_ERR_INVALID_ARG                     # misaligned shared_out
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, FAKE, 0, B.MOE_COMBINE_UNFUSED, ctypes.byref(s), FAKE,
+                         8, None) == B.MOE_ERR_WORKSPACE
+    w = B.MoeLayerWeights(None, None, FAKE, FAKE, FAKE, None, None, None, None, None)
     aux = B.MoeLayerAux()
     # no gate weight and no given logits
     assert L.moe_layer_forward(ctypes.byref(w), FAKE, None, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
@@ -133,4 +140,8 @@ def test_other_calls_reject_bad_arguments_on_host():
     assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
                                None, FAKE, 1024, None) == B.MOE_ERR_WORKSPACE
     assert L.moe_layer_forward(None, FAKE, FAKE, FAKE, 0, ctypes.byref(s), ctypes.byref(aux),
+                               None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    # shared expert declared without its weights
+    ss = B.shape(64, 128, 8, 2, 256, shared_I=128)
+    assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(ss), ctypes.byref(aux),
                                None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG

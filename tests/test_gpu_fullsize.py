@@ -18,7 +18,8 @@ import torch
 import oracle
 from workloads import FULL_CONFIGS, generator as gen
 from routing_dispatch_expert_logits_amd import binding as B
-from tests.gpu_util import dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits, check_permutation_valid
+from tests.gpu_util import (dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits,
+                            check_permutation_valid, out_err_over_rms)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -43,7 +44,7 @@ def test_route_full_size_bit_exact(name):
     assert np.max(np.abs(host(w) - ref["weights"])) <= 1e-6
 
 
-@pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("name", NAMES + ["deepseek_r1_shaped_shared"])
 def test_layer_full_size_sampled(name):
     cfg = FULL_CONFIGS[name]
     bf = cfg.dtype == "bf16"
@@ -51,7 +52,8 @@ def test_layer_full_size_sampled(name):
     inp = gen.layer_inputs(cfg)
     s = shape_of(cfg)
     T, E, k, R, D = cfg.T, cfg.E, cfg.k, cfg.R, cfg.D
-    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu") if n in inp}
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu", "ws1", "ws3", "ws2")
+         if n in inp}
     if "bias" in inp:
         w["gate_bias"] = dev(inp["bias"])
     x = dev(inp["x"])
@@ -102,7 +104,9 @@ def test_layer_full_size_sampled(name):
     print(f"[{name}] oracle on {keep.sum()} sampled tokens, {len(need)} experts", flush=True)
     ref_out = oracle.token_outputs(inp, tok[keep], r["ids"][keep], r["weights"][keep], ew, bf16=bf,
                                    z=None if z is None else z[keep])
-    rms = float(np.sqrt(np.mean(ref_out ** 2)))
-    err = float(np.max(np.abs(o32[tok][keep] - ref_out))) / rms
+    ysh = None
+    if cfg.shared_I and bf:
+        ysh = oracle.shared_expert_ffn(inp["x"][tok[keep]], inp["ws1"], inp["ws3"], inp["ws2"], bf)
+    err = out_err_over_rms(o32[tok][keep], ref_out, ysh)
     print(f"[{name}] max|err|/RMS = {err:.3e}", flush=True)
     assert err <= (2e-2 if bf else 1e-5)

@@ -439,3 +439,58 @@ def test_token_outputs_match_whole_layer():
         z = ref["z"][tok] if cfg.L else None
         got = oracle.token_outputs(inp, tok, ref["ids"][tok], ref["weights"][tok], ew, bf16=True, z=z)
         np.testing.assert_allclose(got, ref["out"][tok], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ shared expert
+
+def test_shared_expert_is_swiglu_of_every_token():
+    """The shared expert is the SwiGLU FFN on all T rows, independent of the routing."""
+    r = _rng(30)
+    T, H, Is = 13, 10, 18
+    x = r.standard_normal((T, H)).astype(np.float32)
+    ws1, ws3 = ((r.standard_normal((Is, H)) * 0.3).astype(np.float32) for _ in range(2))
+    ws2 = (r.standard_normal((H, Is)) * 0.3).astype(np.float32)
+    np.testing.assert_allclose(oracle.shared_expert_ffn(x, ws1, ws3, ws2, bf16=False),
+                               _torch_swiglu(x, ws1, ws3, ws2), rtol=1e-12, atol=1e-13)
+
+
+def test_shared_expert_enters_with_weight_one():
+    """Two routed experts and the shared expert all equal to one FFN: the routing
+    weights sum to 1, so the layer is exactly twice that FFN (a shared term scaled by
+    a routing weight would give (1 + w) FFN instead)."""
+    r = _rng(31)
+    T, H, E, k, I = 17, 8, 2, 2, 12
+    x = r.standard_normal((T, H)).astype(np.float32)
+    f1 = (r.standard_normal((I, H)) * 0.3).astype(np.float32)
+    f3 = (r.standard_normal((I, H)) * 0.3).astype(np.float32)
+    f2 = (r.standard_normal((H, I)) * 0.3).astype(np.float32)
+    inp = {"x": x, "logits": r.standard_normal((T, E)).astype(np.float32),
+           "w1": np.stack([f1] * E), "w3": np.stack([f3] * E), "w2": np.stack([f2] * E),
+           "ws1": f1, "ws3": f3, "ws2": f2}
+    res = oracle.layer_forward(inp, k=k, E=E, bf16=False)
+    ffn = _torch_swiglu(x, f1, f3, f2)
+    np.testing.assert_allclose(res["out"], 2.0 * ffn, rtol=1e-12, atol=1e-13)
+    # planted: the shared term weighted by the first routing weight
+    wrong = oracle.combine(res["y_perm"], res["token_row"], res["weights"]) + \
+        res["weights"][:, :1] * res["y_shared"]
+    assert not np.allclose(wrong, 2.0 * ffn, rtol=1e-6, atol=1e-6)
+
+
+def test_shared_expert_with_zero_up_branch_adds_nothing():
+    cfg = PARITY_CONFIGS["shared_expert"]
+    inp = gen.layer_inputs(cfg)
+    plain = {n: v for n, v in inp.items() if n not in ("ws1", "ws3", "ws2")}
+    zero = dict(inp, ws3=np.zeros_like(inp["ws3"]))
+    a = oracle.layer_forward(zero, k=cfg.k, E=cfg.E, bf16=True)
+    b = oracle.layer_forward(plain, k=cfg.k, E=cfg.E, bf16=True)
+    np.testing.assert_array_equal(a["out"], b["out"])
+
+
+def test_token_outputs_match_whole_layer_with_shared_expert():
+    cfg = PARITY_CONFIGS["shared_expert"]
+    inp = gen.layer_inputs(cfg)
+    ref = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True)
+    tok = np.array([0, 5, 99, cfg.T - 1])
+    ew = {e: (inp["w1"][e], inp["w3"][e], inp["w2"][e]) for e in range(cfg.E)}
+    got = oracle.token_outputs(inp, tok, ref["ids"][tok], ref["weights"][tok], ew, bf16=True)
+    np.testing.assert_allclose(got, ref["out"][tok], rtol=1e-12, atol=1e-14)

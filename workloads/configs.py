@@ -35,6 +35,7 @@ class MoEConfig:
     zipf_s: Optional[float] = None     # per-expert bias -alpha*s*ln(rank) when set
     zipf_alpha: float = 0.0
     const_logits: bool = False         # every router logit equal (all-tie routing)
+    shared_I: int = 0                  # shared expert intermediate width (0 = none)
 
     @property
     def D(self) -> int:
@@ -85,8 +86,11 @@ LATENT_MOE = MoEConfig(
     name="latent_moe", T=4096, H=7168, L=2048, E=256, k=8, I=4096, seed=505,
     gate="computed", gate_std=None)
 
+# DeepSeek-R1-shaped layer with its shared expert (one, of the routed experts' width)
+DEEPSEEK_R1_SHAPED_SHARED = DEEPSEEK_R1_SHAPED.with_(name="deepseek_r1_shaped_shared", shared_I=2048)
+
 FULL_CONFIGS = {c.name: c for c in (TINY_F32, QWEN3_30B_A3B_SHAPED, DEEPSEEK_R1_SHAPED,
-                                    K3_SHAPED_DECODE, LATENT_MOE)}
+                                    K3_SHAPED_DECODE, LATENT_MOE, DEEPSEEK_R1_SHAPED_SHARED)}
 
 # Cut-down layers for element-by-element parity (oracle runs in seconds).
 PARITY_CONFIGS = {c.name: c for c in (
@@ -117,4 +121,12 @@ PARITY_CONFIGS = {c.name: c for c in (
     # GEMM (the large-layer kernel choices), skewed counts spanning several m-tiles
     MoEConfig(name="wide_experts", T=400, H=256, E=4, k=2, I=2048, seed=22, gate="drawn",
               zipf_s=1.1, zipf_alpha=1.0),
+    # a shared expert next to the routed ones: 128-row tiles (T >= 48), 16-row
+    # tiles (T < 48) and fp32
+    MoEConfig(name="shared_expert", T=300, H=256, E=16, k=4, I=192, seed=23, gate="computed",
+              gate_std=0.0625, zipf_s=1.1, zipf_alpha=1.0, shared_I=320),
+    MoEConfig(name="shared_expert_decode", T=24, H=512, E=96, k=6, I=128, seed=24, gate="drawn",
+              gate_std=None, zipf_s=1.2, zipf_alpha=ZIPF_ALPHA, shared_I=256),
+    MoEConfig(name="shared_expert_f32", T=97, H=96, E=6, k=3, I=80, dtype="f32", seed=25,
+              w_std=0.05, gate="computed", gate_std=0.1, shared_I=64),
 )}

@@ -25,6 +25,7 @@ from .configs import MoEConfig
 
 TAG_X, TAG_GATE_W, TAG_BIAS_RANK, TAG_W1, TAG_W3, TAG_W2, TAG_WD, TAG_WU, TAG_LOGITS, TAG_Y = \
     1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+TAG_WS1, TAG_WS3, TAG_WS2 = 11, 12, 13
 
 
 def _threads() -> int:
@@ -118,6 +119,15 @@ def expert_weights(cfg: MoEConfig, experts: Optional[Iterable[int]] = None,
     return {"w1": w1, "w3": w3, "w2": w2, "experts": np.asarray(ex, dtype=np.int64)}
 
 
+def shared_weights(cfg: MoEConfig) -> Dict[str, np.ndarray]:
+    """Shared expert ws1, ws3 [Is x H] and ws2 [H x Is] (layers with shared_I > 0)."""
+    assert cfg.shared_I > 0
+    Is, H = cfg.shared_I, cfg.H
+    return {"ws1": draw(cfg, TAG_WS1, 0, (Is, H), cfg.w_std),
+            "ws3": draw(cfg, TAG_WS3, 0, (Is, H), cfg.w_std),
+            "ws2": draw(cfg, TAG_WS2, 0, (H, Is), cfg.w_std)}
+
+
 def latent_weights(cfg: MoEConfig) -> Dict[str, np.ndarray]:
     """Down projection wd [L x H] and up projection wu [H x L] (latent layers only)."""
     assert cfg.L > 0
@@ -139,6 +149,8 @@ def layer_inputs(cfg: MoEConfig, step: int = 0, with_experts: bool = True) -> Di
         d.update(latent_weights(cfg))
     if with_experts:
         d.update({k: v for k, v in expert_weights(cfg).items() if k != "experts"})
+        if cfg.shared_I:
+            d.update(shared_weights(cfg))
     return d
 
 
