@@ -499,13 +499,15 @@ template <int NB, int FN, int EPI>
 __global__ __launch_bounds__(256) void k_gemm_decode(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, const int32_t* __restrict__ gather) {
   constexpr int BM = 16, BN = 4 * 16 * FN;
   TileCoord tc;
   if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = (lane >> 4) * 16;
-  const uint16_t* pa = A + (size_t)(tc.row0 + min(lane & 15, tc.rows - 1)) * K + kl;
+  // gather non-NULL: operand row r is A[gather[r]] (token rows read in permuted order)
+  const int ar = tc.row0 + min(lane & 15, tc.rows - 1);
+  const uint16_t* pa = A + (size_t)(gather ? gather[ar] : ar) * K + kl;
   const uint16_t* pb[NB][FN];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -645,6 +647,9 @@ int max_mtiles(int M, int E, int bm) {
 
 #define MOE_LAUNCH(kern, grid) \
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K)
+#define MOE_LAUNCH_DEC(kern, grid)                                                                   \
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K, \
+                     static_cast<const int32_t*>(nullptr))
 
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
@@ -716,10 +721,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
   } else {
     const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
     switch (epi) {
-      case EPI_SWIGLU_BF16: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), g); break;
-      case EPI_SWIGLU_F32: MOE_LAUNCH((k_gemm_decode<2, 2, EPI_SWIGLU_F32>), g); break;
-      case EPI_BF16: MOE_LAUNCH((k_gemm_decode<1, 2, EPI_BF16>), g); break;
-      case EPI_F32: MOE_LAUNCH((k_gemm_decode<1, 2, EPI_F32>), g); break;
+      case EPI_SWIGLU_BF16: MOE_LAUNCH_DEC((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), g); break;
+      case EPI_SWIGLU_F32: MOE_LAUNCH_DEC((k_gemm_decode<2, 2, EPI_SWIGLU_F32>), g); break;
+      case EPI_BF16: MOE_LAUNCH_DEC((k_gemm_decode<1, 2, EPI_BF16>), g); break;
+      case EPI_F32: MOE_LAUNCH_DEC((k_gemm_decode<1, 2, EPI_F32>), g); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -749,6 +754,19 @@ hipError_t launch_gemm_simt(bool a_bf16, int epi, const void* A, int M, const fl
     }
   }
 #undef MOE_SIMT
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
+                                     const uint16_t* B0, const uint16_t* B1, void* C,
+                                     const int32_t* offsets, const int32_t* mtile_start, int E, int N,
+                                     int K, hipStream_t st) {
+  const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
+  if (epi == EPI_SWIGLU_BF16)
+    hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), dim3(g), dim3(256), 0, st, X, M, B0, B1, C,
+                       offsets, mtile_start, E, N, K, gather);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -374,17 +374,39 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     if (rc != MOE_OK) return rc;
   }
   if (!ev(2)) return MOE_ERR_HIP;
-  // a2 + a3
-  MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
-  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
-  MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
-  if (!ev(3)) return MOE_ERR_HIP;
-  // a4
-  MOE_HIP(launch_permute(d.L ? z : x, d.D * d.es / 16, ids, d.T, d.E, d.k, offs, bc, xperm, rtok,
-                         trow, st));
+  const void* src = d.L ? z : x;  // the rows that are dispatched
+  const int row16 = d.D * d.es / 16;
+  // Decode-scale steps (16-row expert tiles, T <= kSmallT): routing, counts, offsets,
+  // tile tables and row metadata in one launch, and the gate/up GEMM reads its rows
+  // straight from the token rows through row_token (no permuted copy unless the
+  // caller asks for it in aux.x_perm).
+  const bool small = kind == GEMM_DECODE && d.T <= kSmallT;
+  if (small) {
+    MOE_HIP(launch_route_small(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, counts,
+                               offs, rtok, trow, gemm_bm(kind), mtile, st));
+    if (!ev(3)) return MOE_ERR_HIP;
+    if (ax.x_perm) MOE_HIP(launch_unpermute(src, row16, rtok, d.R, ax.x_perm, st));
+  } else {
+    // a2 + a3
+    MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
+    MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
+    MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
+    if (!ev(3)) return MOE_ERR_HIP;
+    // a4
+    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, offs, bc, xperm, rtok, trow, st));
+  }
   if (!ev(4)) return MOE_ERR_HIP;
   // a5
-  if (kind == GEMM_SIMT) {
+  if (small) {
+    MOE_HIP(launch_gemm_decode_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
+                                      static_cast<const uint16_t*>(wt->w1),
+                                      static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,
+                                      d.D, st));
+    if (!ev(5)) return MOE_ERR_HIP;
+    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
+                             d.E, d.D, d.I, st));
+  } else if (kind == GEMM_SIMT) {
     MOE_HIP(launch_gemm_simt(false, EPI_SWIGLU_F32, xperm, d.R, static_cast<const float*>(wt->w1),
                              static_cast<const float*>(wt->w3), act, offs, mtile, d.E, d.I, d.D,
                              nullptr, st));
@@ -415,7 +437,6 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   }
   if (!ev(7)) return MOE_ERR_HIP;
   // a6
-  const int row16 = d.D * d.es / 16;
   if (d.L) {
     MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, nullptr, d.T, d.k, outl, !d.bf16, st));
   } else {

@@ -13,6 +13,9 @@ constexpr int kWave = 64;
 constexpr int kBlockTok = 16;
 __host__ __device__ __forceinline__ int block_tokens(int) { return kBlockTok; }
 constexpr int kMaxE = 1024;
+// Largest token count routed by the one-workgroup decode-scale kernel (one bit per
+// token in a 64-bit mask).
+constexpr int kSmallT = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

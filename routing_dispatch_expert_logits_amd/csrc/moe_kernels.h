@@ -45,6 +45,17 @@ hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, 
 hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
                                   const void* add, int T, int k, void* out, bool out_f32,
                                   hipStream_t st);
+// Decode-scale routing (T <= kSmallT) in one launch: ids, weights, counts, offsets, the m-tile
+// tables (bm > 0) and row_token / token_row, as the large-T kernels produce them.
+hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
+                             float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                             int32_t* token_row, int bm, int32_t* mtile_start, hipStream_t st);
+// Decode GEMM whose A rows are read through an index: row r of the operand is X[gather[r]]
+// (the expert gate/up GEMM reading the token rows directly instead of a permuted copy).
+hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
+                                     const uint16_t* B0, const uint16_t* B1, void* C,
+                                     const int32_t* offsets, const int32_t* mtile_start, int E, int N,
+                                     int K, hipStream_t st);
 // One group of T rows: offsets = {0, T} and the m-tile tables (tile heights bm, 2 bm) for E = 1.
 hipError_t launch_single_group(int T, int32_t* offsets, int bm, int32_t* mtile_start, hipStream_t st);
 // bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.

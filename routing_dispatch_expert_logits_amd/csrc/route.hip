@@ -21,6 +21,63 @@ namespace moe {
 // that entry; both reductions are DPP row butterflies plus readlane.  Counts per
 // expert for the block are gathered in LDS (order-independent) and written to
 // block_counts[block][e].
+// The k experts of one token, ranked by one wave: lane j < k receives the j-th
+// expert id and its renormalised weight.  Scores become order keys
+// (order_key(score): larger score, larger key); each of the k rounds takes the
+// wave-wide largest key, then the lowest expert index holding it (so equal scores
+// go to the lower index), and removes that entry; both reductions are DPP row
+// butterflies plus readlane.
+template <int SLOTS>
+__device__ __forceinline__ void rank_token(const float* __restrict__ row,
+                                           const float* __restrict__ bias, int E, int k, int lane,
+                                           int& my_e, float& my_w) {
+  // every load is issued unconditionally (lanes past E read the last score and
+  // are masked afterwards) so they overlap instead of each waiting in a branch
+  float v[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) v[s] = row[min(lane + s * kWave, E - 1)];
+  if (bias) {
+    float b[SLOTS];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) b[s] = bias[min(lane + s * kWave, E - 1)];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) v[s] += b[s];
+  }
+  uint32_t key[SLOTS];
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s)
+    key[s] = lane + s * kWave < E ? order_key(v[s]) : 0u;  // 0 is below every real key
+  my_e = 0;
+  float my_s = 0.f, top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
+    const uint32_t best = wave_max_u32(lm);
+    uint32_t li = 0xffffffffu;
+#pragma unroll
+    for (int s = SLOTS - 1; s >= 0; --s)
+      if (key[s] == best) li = static_cast<uint32_t>(lane + s * kWave);
+    const int e = static_cast<int>(wave_min_u32(li));
+    const float sc = key_to_score(best);
+    if (j == 0) top = sc;
+    if (lane == j) {
+      my_e = e;
+      my_s = sc;
+    }
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+      if (lane + s * kWave == e) key[s] = 0u;
+  }
+  // Renormalised softmax over the selected k: the full-E denominator cancels.
+  const float ex = lane < k ? expf(my_s - top) : 0.f;
+  const float sum = wave_sum_f32(ex);
+  my_w = ex / sum;
+}
+
+// One workgroup per 16-token ranking block, one token per wave.  Counts per
+// expert for the block are gathered in LDS (order-independent) and written to
+// block_counts[block][e].
 template <int SLOTS>
 __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_in,
                                                const float* __restrict__ bias, int T, int E, int k,
@@ -35,43 +92,12 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_
 
   const int t = blockIdx.x * kBlockTok + wave;
   if (t < T) {
-    const float* row = scores_in + (size_t)t * E;
-    uint32_t key[SLOTS];
-#pragma unroll
-    for (int s = 0; s < SLOTS; ++s) {
-      const int e = lane + s * kWave;
-      float v = e < E ? row[e] : 0.f;
-      if (bias && e < E) v += bias[e];
-      key[s] = e < E ? order_key(v) : 0u;  // 0 is below every real key
-    }
-    int my_e = 0;
-    float my_s = 0.f, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint32_t lm = key[0];
-#pragma unroll
-      for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
-      const uint32_t best = wave_max_u32(lm);
-      uint32_t li = 0xffffffffu;
-#pragma unroll
-      for (int s = SLOTS - 1; s >= 0; --s)
-        if (key[s] == best) li = static_cast<uint32_t>(lane + s * kWave);
-      const int e = static_cast<int>(wave_min_u32(li));
-      const float sc = key_to_score(best);
-      if (j == 0) top = sc;
-      if (lane == j) {
-        my_e = e;
-        my_s = sc;
-      }
-#pragma unroll
-      for (int s = 0; s < SLOTS; ++s)
-        if (lane + s * kWave == e) key[s] = 0u;
-    }
-    // Renormalised softmax over the selected k: the full-E denominator cancels.
-    const float ex = lane < k ? expf(my_s - top) : 0.f;
-    const float sum = wave_sum_f32(ex);
+    int my_e;
+    float my_w;
+    rank_token<SLOTS>(scores_in + (size_t)t * E, bias, E, k, lane, my_e, my_w);
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_e;
-      topk_w[(size_t)t * k + lane] = ex / sum;
+      topk_w[(size_t)t * k + lane] = my_w;
       atomicAdd(&cnt[my_e], 1);
     }
   }
@@ -204,6 +230,71 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
+// Routing of a decode-scale step (T <= 64) in one workgroup: top-k per token
+// (one wave per token, tokens t = wave + 16 i), counts, offsets, the GEMM m-tile
+// tables and the row metadata, so a small step pays one launch for what the
+// large-T path does in four.  Row order inside an expert's segment is ascending
+// token id, as there: row = offsets[e] + popcount(mask[e] below t), mask[e] the
+// tokens that picked e (built with order-independent LDS atomicOr).
+template <int SLOTS>
+__global__ __launch_bounds__(1024) void k_route_small(
+    const float* __restrict__ scores_in, const float* __restrict__ bias, int T, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+    int bm, int32_t* __restrict__ mtile_start) {
+  __shared__ int cnt[kMaxE];
+  __shared__ int off_s[kMaxE];
+  __shared__ unsigned long long mask[kMaxE];
+  __shared__ int s_ids[kSmallT * kWave];
+  __shared__ int smem[48];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 1024) {
+    cnt[e] = 0;
+    mask[e] = 0ull;
+  }
+  __syncthreads();
+  for (int t = wave; t < T; t += 16) {
+    int my_e;
+    float my_w;
+    rank_token<SLOTS>(scores_in + (size_t)t * E, bias, E, k, lane, my_e, my_w);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = my_w;
+      s_ids[t * k + lane] = my_e;
+      atomicAdd(&cnt[my_e], 1);
+      atomicOr(&mask[my_e], 1ull << t);
+    }
+  }
+  __syncthreads();
+  const int c = tid < E ? cnt[tid] : 0;
+  int total = 0;
+  const int off = block_exclusive_scan(c, &total, smem);
+  if (tid < E) {
+    off_s[tid] = off;
+    counts[tid] = c;
+    offsets[tid] = off;
+    if (tid == E - 1) offsets[E] = off + c;
+  }
+  if (bm > 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mt = tid < E ? ceil_div(c, bm << h) : 0;
+      int tot = 0;
+      const int st = block_exclusive_scan(mt, &tot, smem);
+      int32_t* tab = mtile_start + h * (E + 1);
+      if (tid < E) tab[tid] = st;
+      if (tid == E - 1) tab[E] = st + mt;
+    }
+  }
+  __syncthreads();
+  for (int a = tid; a < T * k; a += 1024) {
+    const int t = a / k, e = s_ids[a];
+    const int row = off_s[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
+    token_row[a] = row;
+    row_token[row] = t;
+  }
+}
+
 // One group of T rows (the shared expert's GEMMs run as a single expert).
 __global__ void k_single_group(int T, int32_t* __restrict__ offsets, int bm,
                                int32_t* __restrict__ mtile_start) {
@@ -249,6 +340,24 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
                           int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st) {
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(1024), 0, st, counts, offsets_in, E, offsets_out, bm,
                      mtile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
+                             float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                             int32_t* token_row, int bm, int32_t* mtile_start, hipStream_t st) {
+  if (T > kSmallT) return hipErrorInvalidValue;
+  const int slots = ceil_div(E, kWave);
+  dim3 g(1), b(1024);
+#define MOE_RS(SL)                                                                                   \
+  hipLaunchKernelGGL((k_route_small<SL>), g, b, 0, st, scores, bias, T, E, k, ids, w, counts, offsets, \
+                     row_token, token_row, bm, mtile_start)
+  if (slots <= 1) MOE_RS(1);
+  else if (slots <= 2) MOE_RS(2);
+  else if (slots <= 4) MOE_RS(4);
+  else if (slots <= 8) MOE_RS(8);
+  else MOE_RS(16);
+#undef MOE_RS
   return hipGetLastError();
 }
 

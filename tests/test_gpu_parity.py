@@ -328,11 +328,14 @@ def test_layer_matches_separate_calls_and_is_deterministic(name):
     np.testing.assert_array_equal(offs, a["offsets"])
 
 
-@pytest.mark.parametrize("name", ["shared_expert", "shared_expert_decode", "shared_expert_f32"])
-def test_shared_expert_layer_equals_separate_calls(name):
-    """Fused layer with a shared expert == route, permute, grouped FFN, the shared
-    expert as a one-expert grouped FFN over all tokens, and the combine with its
-    shared term, bit for bit (the fusion is execution-only)."""
+@pytest.mark.parametrize("name", ["shared_expert", "shared_expert_decode", "shared_expert_f32",
+                                  "small_bf16_decode", "single_token", "many_empty"])
+def test_layer_output_equals_separate_calls(name):
+    """Fused layer == route, permute, grouped FFN, (the shared expert as a
+    one-expert grouped FFN over all tokens,) and the combine, bit for bit: the
+    fusion is execution-only.  Decode-scale layers (T <= 64 with 16-row tiles)
+    take the one-launch routing and the gathering gate/up GEMM in the fused call,
+    the general kernels in the separate calls."""
     cfg = PARITY_CONFIGS[name]
     inp = gen.layer_inputs(cfg)
     a = run_layer(cfg, inp)
@@ -347,16 +350,20 @@ def test_shared_expert_layer_equals_separate_calls(name):
     yp = empty((R, D), kind)
     B.grouped_ffn(xp, dev(offs), dev(inp["w1"]), dev(inp["w3"]), dev(inp["w2"]), yp, s,
                   ws(s, B.MOE_CALL_FFN))
-    s1 = B.shape(T, H, 1, 1, cfg.shared_I, 0, cfg.dtype)
-    ysh = empty((T, H), kind)
-    B.grouped_ffn(dev(inp["x"]), dev(np.array([0, T], dtype=np.int32)), dev(inp["ws1"]),
-                  dev(inp["ws3"]), dev(inp["ws2"]), ysh, s1, ws(s1, B.MOE_CALL_FFN))
+    ysh = None
+    if cfg.shared_I:
+        s1 = B.shape(T, H, 1, 1, cfg.shared_I, 0, cfg.dtype)
+        ysh = empty((T, H), kind)
+        B.grouped_ffn(dev(inp["x"]), dev(np.array([0, T], dtype=np.int32)), dev(inp["ws1"]),
+                      dev(inp["ws3"]), dev(inp["ws2"]), ysh, s1, ws(s1, B.MOE_CALL_FFN))
     out = empty((T, H), "f32")
     B.combine(yp, tr, dev(w), out, B.MOE_F32, B.MOE_COMBINE_FUSED, s, ws(s, B.MOE_CALL_COMBINE),
               shared_out=ysh)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(out), a["out"])
-    # and the shared expert alone matches the oracle's
-    bf = cfg.dtype == "bf16"
-    ref_sh = oracle.shared_expert_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"], bf)
-    _check_y(cfg, host(ysh, bf), ref_sh)
+    for n, t in (("x_perm", xp), ("row_token", rt), ("token_row", tr)):
+        np.testing.assert_array_equal(host(t, cfg.dtype == "bf16" and n == "x_perm"), a[n], err_msg=n)
+    if cfg.shared_I:  # and the shared expert alone matches the oracle's
+        bf = cfg.dtype == "bf16"
+        ref_sh = oracle.shared_expert_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"], bf)
+        _check_y(cfg, host(ysh, bf), ref_sh)

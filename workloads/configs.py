@@ -86,11 +86,15 @@ LATENT_MOE = MoEConfig(
     name="latent_moe", T=4096, H=7168, L=2048, E=256, k=8, I=4096, seed=505,
     gate="computed", gate_std=None)
 
+# the K3-shaped decode layer at a small step (8 tokens): the latency-bound regime
+K3_SHAPED_DECODE_T8 = K3_SHAPED_DECODE.with_(name="k3_shaped_decode_t8", T=8, seed=406)
+
 # DeepSeek-R1-shaped layer with its shared expert (one, of the routed experts' width)
 DEEPSEEK_R1_SHAPED_SHARED = DEEPSEEK_R1_SHAPED.with_(name="deepseek_r1_shaped_shared", shared_I=2048)
 
 FULL_CONFIGS = {c.name: c for c in (TINY_F32, QWEN3_30B_A3B_SHAPED, DEEPSEEK_R1_SHAPED,
-                                    K3_SHAPED_DECODE, LATENT_MOE, DEEPSEEK_R1_SHAPED_SHARED)}
+                                    K3_SHAPED_DECODE, LATENT_MOE, DEEPSEEK_R1_SHAPED_SHARED,
+                                    K3_SHAPED_DECODE_T8)}
 
 # Cut-down layers for element-by-element parity (oracle runs in seconds).
 PARITY_CONFIGS = {c.name: c for c in (
