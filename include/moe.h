@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 #ifndef MOE_API
 #define MOE_API __attribute__((visibility("default")))
@@ -104,6 +104,12 @@ typedef struct moe_shape {
   int64_t L;      /* latent dispatch width, 0 = none */
   int32_t dtype;  /* moe_dtype */
   int32_t shared_I;  /* intermediate width of the shared expert, 0 = no shared expert */
+  int64_t capacity;  /* rows kept per expert, 0 = no limit.  With C > 0 each expert keeps
+                      * its first C assignments in ascending token order and drops the rest
+                      * (their token_row is -1 and they add nothing to the combine; the kept
+                      * routing weights are not renormalised).  Dropping changes the layer's
+                      * output: WideEP explainer, "An imbalanced router creates a network
+                      * hotspot".  C >= T can drop nothing and behaves as 0. */
 } moe_shape;
 
 /* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
@@ -135,8 +141,10 @@ MOE_API int moe_abi_version(void);
  * topk_w   [T x k] fp32 out: softmax over all E scores gathered at topk_ids and
  *          renormalised over the k (equal to exp(s_j - s_max) / sum_i exp(s_i - s_max)
  *          over the selected i).  A token whose scores are all -inf gets NaN.
- * counts   [E] int32 out: assignments per expert (sum = T*k).
- * offsets  [E+1] int32 out: exclusive prefix sum of counts, offsets[E] = T*k.
+ * counts   [E] int32 out: assignments per expert (sum = T*k), or with an expert
+ *          capacity C the rows kept, min(assignments, C).
+ * offsets  [E+1] int32 out: exclusive prefix sum of counts, offsets[E] = T*k (the kept
+ *          rows with a capacity).
  */
 MOE_API moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
                           float* logits, int32_t* topk_ids, float* topk_w, int32_t* counts,
@@ -156,9 +164,10 @@ MOE_API moe_status moe_route_topk(const void* x, const float* gate_w, const floa
  * topk_ids  [T x k] int32, offsets [E+1] int32 (as written by moe_route_topk).
  * x_perm    [T*k x D] out: expert e's rows occupy [offsets[e], offsets[e+1]),
  *           holding, in ascending token order, a bitwise copy of every token
- *           that picked e.
- * row_token [T*k] int32 out: source token of each row.
- * token_row [T x k] int32 out: row holding token t's j-th assignment.
+ *           that picked e (with a capacity C: the first C of them; rows from
+ *           offsets[E] on are left untouched).
+ * row_token [T*k] int32 out: source token of each row (the first offsets[E] entries).
+ * token_row [T x k] int32 out: row holding token t's j-th assignment, -1 if dropped.
  */
 MOE_API moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
                                 void* x_perm, int32_t* row_token, int32_t* token_row,
@@ -193,7 +202,8 @@ MOE_API moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, c
  * weights) and "Top-k multiplies traffic..." (combine moves about the same
  * volume as dispatch).
  *
- * y_perm    [T*k x D] (dtype), token_row [T x k] int32, topk_w [T x k] fp32.
+ * y_perm    [T*k x D] (dtype), token_row [T x k] int32 (-1: dropped assignment, no
+ *           term), topk_w [T x k] fp32.
  * shared_out[T x D] (dtype), nullable: the shared expert's output, added with
  *           weight 1 (a shared expert runs for every token whatever the router
  *           picks: "Three Parameter Counts...", "What the utilization dashboard

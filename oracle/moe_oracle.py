@@ -188,7 +188,7 @@ def segment_offsets(counts: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def permutation(ids: np.ndarray, E: int):
+def permutation(ids: np.ndarray, E: int, capacity: int = 0):
     """Expert-contiguous row order and its inverse.
 
     Expert e's segment holds, in ascending token order, every token that picked
@@ -196,19 +196,25 @@ def permutation(ids: np.ndarray, E: int):
     (row holding token t's j-th assignment), the routing metadata attached to
     the permuted rows (WideEP explainer, "The router writes a network
     schedule").
+
+    With ``capacity`` C > 0 an expert keeps only its first C assignments in that
+    order; the later ones are dropped (``token_row`` = -1) and ``row_token`` holds
+    the kept rows only.  Dropping is value-changing (WideEP explainer, "An
+    imbalanced router creates a network hotspot"); C = 0 keeps everything.
     """
     T, k = ids.shape
-    row_token = np.empty(T * k, dtype=np.int64)
-    token_row = np.empty((T, k), dtype=np.int64)
-    r = 0
+    row_token = []
+    token_row = np.full((T, k), -1, dtype=np.int64)
     for e in range(E):
         hit_t, hit_j = np.nonzero(ids == e)       # row-major scan: ascending token
-        for t, j in zip(hit_t.tolist(), hit_j.tolist()):
-            row_token[r] = t
-            token_row[t, j] = r
-            r += 1
-    assert r == T * k
-    return row_token, token_row
+        for n, (t, j) in enumerate(zip(hit_t.tolist(), hit_j.tolist())):
+            if capacity and n >= capacity:
+                break
+            token_row[t, j] = len(row_token)
+            row_token.append(t)
+    if not capacity:
+        assert len(row_token) == T * k
+    return np.asarray(row_token, dtype=np.int64), token_row
 
 
 def gather_rows(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
@@ -302,13 +308,16 @@ def combine(y_perm: np.ndarray, token_row: np.ndarray, weights: np.ndarray,
 
     The combine reverses the route, then the source unpermutes and applies the
     routing weights (WideEP explainer, "The router writes a network schedule").
-    A shared expert's output, when present, enters with weight 1.
+    A shared expert's output, when present, enters with weight 1.  Assignments
+    dropped by an expert capacity (token_row = -1) add nothing; the kept weights
+    are not renormalised.
     """
     y = decode(y_perm) if y_perm.dtype == np.uint16 else np.asarray(y_perm, dtype=np.float64)
     T, k = token_row.shape
     out = np.zeros((T, y.shape[1]), dtype=np.float64)
     for j in range(k):
-        out += weights[:, j:j + 1] * y[token_row[:, j]]
+        kept = token_row[:, j] >= 0               # dropped assignments (capacity) add nothing
+        out[kept] += weights[kept, j:j + 1] * y[token_row[kept, j]]
     if shared is not None:
         out += decode(shared) if shared.dtype == np.uint16 else np.asarray(shared, dtype=np.float64)
     return out
@@ -343,15 +352,22 @@ def latent_up(out_l: np.ndarray, wu: np.ndarray, bf16: bool) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def route(scores_f32: np.ndarray, k: int, E: int) -> Dict[str, np.ndarray]:
-    """a2 + a3 on given fp32 scores: ids, weights, counts, offsets."""
+def route(scores_f32: np.ndarray, k: int, E: int, capacity: int = 0) -> Dict[str, np.ndarray]:
+    """a2 + a3 on given fp32 scores: ids, weights, counts, offsets.
+
+    With an expert capacity C > 0 the slots allocated per expert are
+    min(count, C): ``counts`` and ``offsets`` describe the kept rows, and
+    ``routed_counts`` keeps the assignments before dropping.
+    """
     ids = topk_ids(scores_f32, k)
     w = routing_weights(scores_f32, ids)
-    counts = expert_counts(ids, E)
-    return {"ids": ids, "weights": w, "counts": counts, "offsets": segment_offsets(counts)}
+    routed = expert_counts(ids, E)
+    counts = np.minimum(routed, capacity) if capacity else routed
+    return {"ids": ids, "weights": w, "counts": counts, "offsets": segment_offsets(counts),
+            "routed_counts": routed}
 
 
-def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
+def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool, capacity: int = 0,
                   timers: Optional[Dict[str, float]] = None) -> Dict[str, np.ndarray]:
     """The whole routed-expert layer forward on one device, every stage kept.
 
@@ -362,7 +378,8 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
     rounded once to fp32 for the selection decision.  ``timers`` (optional)
     receives the wall-clock seconds of routing, permutation, expert FFN and
     combine (the stage timers of Three Parameter Counts, "What the utilization
-    dashboard smooths away").
+    dashboard smooths away").  ``capacity`` C > 0 drops each expert's assignments
+    beyond its first C (value-changing, see ``permutation``).
     """
     clock = [time.perf_counter()]
 
@@ -380,9 +397,9 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool,
         res["logits"] = lg
         scores = lg.astype(np.float32)
     res["scores"] = scores
-    res.update(route(scores, k, E))
+    res.update(route(scores, k, E, capacity))
     lap("routing")
-    rt, tr = permutation(res["ids"], E)
+    rt, tr = permutation(res["ids"], E, capacity)
     res["row_token"], res["token_row"] = rt, tr
     if "wd" in inp:
         res["z"] = latent_down(inp["x"], inp["wd"], bf16)

@@ -19,7 +19,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_FFN, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
 MOE_COMBINE_FUSED, MOE_COMBINE_UNFUSED = 0, 1
 MOE_NUM_STAGE_EVENTS = 10
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STAGE_NAMES = ["latent_down", "gate", "route", "permute", "gemm_gate_up", "gemm_down",
                "shared_expert", "combine", "latent_up"]
@@ -37,7 +37,7 @@ class MoeError(RuntimeError):
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", _i64), ("H", _i64), ("E", _i64), ("k", _i64), ("I", _i64), ("L", _i64),
-                ("dtype", _i32), ("shared_I", _i32)]
+                ("dtype", _i32), ("shared_I", _i32), ("capacity", _i64)]
 
 
 class MoeLayerWeights(ctypes.Structure):
@@ -91,8 +91,8 @@ def status_string(status: int) -> str:
 
 
 def shape(T: int, H: int, E: int, k: int, I: int, L: int = 0, dtype: str = "bf16",
-          shared_I: int = 0) -> MoeShape:
-    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, shared_I)
+          shared_I: int = 0, capacity: int = 0) -> MoeShape:
+    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, shared_I, capacity)
 
 
 def workspace_bytes(s: MoeShape, call: int) -> int:

@@ -10,7 +10,8 @@
 // every token receives with weight 1) added last, and one rounding to the output
 // type.  The fused kernel gathers the k rows directly; the unfused pair first
 // unpermutes into token order and then reduces, with the same fma sequence, so
-// both give the same bits.
+// both give the same bits.  An assignment dropped by an expert capacity
+// (token_row = -1) contributes no term; the kept weights are used as they are.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -98,14 +99,16 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
     for (; j + 4 <= k; j += 4) {
       uint4 v[4];
       float wj[4];
+      int r[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int r = __shfl(my_row, j + u, kWave);
+        r[u] = __shfl(my_row, j + u, kWave);
         wj[u] = __shfl(my_w, j + u, kWave);
-        v[u] = y[(size_t)r * row16 + c];
+        v[u] = y[(size_t)max(r[u], 0) * row16 + c];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (r[u] < 0) continue;  // dropped (uniform over the wave)
         float f[NV];
         Vec16<IT>::unpack(v[u], f);
 #pragma unroll
@@ -114,6 +117,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
     }
     for (; j < k; ++j) {
       const int r = __shfl(my_row, j, kWave);
+      if (r < 0) continue;
       const float wj = __shfl(my_w, j, kWave);
       float f[NV];
       Vec16<IT>::unpack(y[(size_t)r * row16 + c], f);
@@ -125,14 +129,18 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
   }
 }
 
-// Unfused step 1: y_tok[t*k + j] = Y[token_row[t, j]] (one wave per assignment).
+// Unfused step 1: y_tok[t*k + j] = Y[token_row[t, j]] (one wave per assignment);
+// dropped assignments (-1) are skipped.  Also the plain row gather
+// dst[a] = src[index[a]] for a < min(R, *limit) (limit nullable).
 __global__ __launch_bounds__(256) void k_unpermute(const uint4* __restrict__ y, int row16,
                                                    const int32_t* __restrict__ token_row, int R,
+                                                   const int32_t* __restrict__ limit,
                                                    uint4* __restrict__ y_tok) {
   const int lane = threadIdx.x & 63;
   const int a = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (a >= R) return;
+  if (a >= R || (limit && a >= *limit)) return;
   const int r = token_row[a];
+  if (r < 0) return;
   const uint4* src = y + (size_t)r * row16;
   uint4* dst = y_tok + (size_t)a * row16;
   for (int c = lane; c < row16; c += kWave) dst[c] = src[c];
@@ -141,6 +149,7 @@ __global__ __launch_bounds__(256) void k_unpermute(const uint4* __restrict__ y, 
 // Unfused step 2: out[t] = sum_j w[t, j] * y_tok[t*k + j], same fma order as k_combine.
 template <typename IT>
 __global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict__ y_tok, int row16,
+                                                         const int32_t* __restrict__ token_row,
                                                          const float* __restrict__ topk_w,
                                                          const uint4* __restrict__ add, int T,
                                                          int k, void* __restrict__ out,
@@ -154,6 +163,7 @@ __global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
     for (int j = 0; j < k; ++j) {
+      if (token_row[(size_t)t * k + j] < 0) continue;  // dropped
       const float wj = topk_w[(size_t)t * k + j];
       float f[NV];
       Vec16<IT>::unpack(y_tok[((size_t)t * k + j) * row16 + c], f);
@@ -182,23 +192,24 @@ hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
-                            hipStream_t st) {
+hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R,
+                            const int32_t* limit, void* y_tok, hipStream_t st) {
   hipLaunchKernelGGL(k_unpermute, dim3(ceil_div(R, 4)), dim3(256), 0, st,
-                     static_cast<const uint4*>(y), row16, token_row, R, static_cast<uint4*>(y_tok));
+                     static_cast<const uint4*>(y), row16, token_row, R, limit,
+                     static_cast<uint4*>(y_tok));
   return hipGetLastError();
 }
 
-hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
-                                  const void* add, int T, int k, void* out, bool out_f32,
-                                  hipStream_t st) {
+hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const int32_t* token_row,
+                                  const float* w, const void* add, int T, int k, void* out,
+                                  bool out_f32, hipStream_t st) {
   const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
   if (in_bf16)
     hipLaunchKernelGGL(k_weighted_reduce<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
+                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   else
     hipLaunchKernelGGL(k_weighted_reduce<float>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
+                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
   return hipGetLastError();
 }
 

@@ -30,13 +30,15 @@ bool al16_or_null(const void* p) { return !p || al16(p); }
 
 struct Dims {
   int T, H, E, k, I, L, D, R, nb, es;
-  int Is;  // shared expert intermediate width, 0 = none
+  int Is;   // shared expert intermediate width, 0 = none
+  int cap;  // rows kept per expert, 0 = no limit
   bool bf16;
 };
 
 moe_status check_shape(const moe_shape* s, Dims& d) {
   if (!s) return MOE_ERR_INVALID_ARG;
-  if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->L < 0 || s->shared_I < 0)
+  if (s->T < 1 || s->H < 1 || s->E < 1 || s->k < 1 || s->I < 1 || s->L < 0 || s->shared_I < 0 ||
+      s->capacity < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
@@ -47,6 +49,8 @@ moe_status check_shape(const moe_shape* s, Dims& d) {
   d.L = (int)s->L; d.D = d.L ? d.L : d.H; d.R = d.T * d.k;
   d.nb = ceil_div(d.T, block_tokens(d.T));
   d.Is = s->shared_I;
+  // a token picks an expert at most once, so no expert holds more than T rows
+  d.cap = s->capacity >= s->T ? 0 : (int)s->capacity;
   d.bf16 = s->dtype == MOE_BF16;
   d.es = d.bf16 ? 2 : 4;
   if (d.Is && d.L) return MOE_ERR_UNSUPPORTED;  // shared expert on non-latent layers only
@@ -249,7 +253,7 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
   }
   int32_t* bc = at<int32_t>(ws, w.bc);
   MOE_HIP(launch_topk(logits, gate_w ? nullptr : gate_bias, d.T, d.E, d.k, topk_ids, topk_w, bc, st));
-  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
+  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, counts, st));
   MOE_HIP(launch_offsets(counts, nullptr, d.E, offsets, 0, nullptr, st));
   return MOE_OK;
 }
@@ -268,8 +272,8 @@ moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const in
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* bc = at<int32_t>(ws, w.bc);
   MOE_HIP(launch_block_counts(topk_ids, d.T, d.E, d.k, bc, st));
-  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, nullptr, st));
-  MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, offsets, bc, x_perm,
+  MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, nullptr, st));
+  MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, d.cap, offsets, bc, x_perm,
                          row_token, token_row, st));
   return MOE_OK;
 }
@@ -311,8 +315,9 @@ moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float
   const CombWs w = comb_ws(d);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   void* ytok = at<void>(ws, w.ytok);
-  MOE_HIP(launch_unpermute(y_perm, row16, token_row, d.R, ytok, st));
-  MOE_HIP(launch_weighted_reduce(ytok, row16, d.bf16, topk_w, shared_out, d.T, d.k, out, of32, st));
+  MOE_HIP(launch_unpermute(y_perm, row16, token_row, d.R, nullptr, ytok, st));
+  MOE_HIP(launch_weighted_reduce(ytok, row16, d.bf16, token_row, topk_w, shared_out, d.T, d.k, out,
+                                 of32, st));
   return MOE_OK;
 }
 
@@ -383,17 +388,18 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   const bool small = kind == GEMM_DECODE && d.T <= kSmallT;
   if (small) {
     MOE_HIP(launch_route_small(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, counts,
-                               offs, rtok, trow, gemm_bm(kind), mtile, st));
+                               offs, rtok, trow, d.cap, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
-    if (ax.x_perm) MOE_HIP(launch_unpermute(src, row16, rtok, d.R, ax.x_perm, st));
+    // rows [0, offsets[E]) are the kept ones
+    if (ax.x_perm) MOE_HIP(launch_unpermute(src, row16, rtok, d.R, offs + d.E, ax.x_perm, st));
   } else {
     // a2 + a3
     MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
-    MOE_HIP(launch_expert_scan(bc, d.nb, d.E, counts, st));
+    MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, counts, st));
     MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
     // a4
-    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, offs, bc, xperm, rtok, trow, st));
+    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, rtok, trow, st));
   }
   if (!ev(4)) return MOE_ERR_HIP;
   // a5

@@ -26,30 +26,33 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
 hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t* block_counts,
                                hipStream_t st);
 // block_counts[b][e] -> rows of e in blocks before b; counts_out[e] = total (if non-NULL).
-hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int32_t* counts_out,
+// cap > 0: counts_out[e] = min(total, cap) (expert capacity; later assignments are dropped).
+hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int cap, int32_t* counts_out,
                               hipStream_t st);
 // offsets_out from counts (if non-NULL) and, for bm > 0, the m-tile tables for tile heights
 // bm and 2 bm; with offsets_in the counts are its differences.
 hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int E,
                           int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st);
 // bases: per-block rows before each block (launch_expert_scan); offsets: segment starts.
-hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
+hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
                           const int32_t* offsets, const int32_t* bases, void* x_perm,
                           int32_t* row_token, int32_t* token_row, hipStream_t st);
 // add: nullable [T x row16 x 16 B] addend of the input element type, added after the k terms.
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
                           const float* w, const void* add, int T, int k, void* out, bool out_f32,
                           hipStream_t st);
-hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R, void* y_tok,
-                            hipStream_t st);
-hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const float* w,
-                                  const void* add, int T, int k, void* out, bool out_f32,
-                                  hipStream_t st);
+// dst[a] = src[index[a]] for a < min(R, *limit) (limit nullable), index < 0 skipped.
+hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R,
+                            const int32_t* limit, void* y_tok, hipStream_t st);
+hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const int32_t* token_row,
+                                  const float* w, const void* add, int T, int k, void* out,
+                                  bool out_f32, hipStream_t st);
 // Decode-scale routing (T <= kSmallT) in one launch: ids, weights, counts, offsets, the m-tile
 // tables (bm > 0) and row_token / token_row, as the large-T kernels produce them.
 hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                             int32_t* token_row, int bm, int32_t* mtile_start, hipStream_t st);
+                             int32_t* token_row, int cap, int bm, int32_t* mtile_start,
+                             hipStream_t st);
 // Decode GEMM whose A rows are read through an index: row r of the operand is X[gather[r]]
 // (the expert gate/up GEMM reading the token rows directly instead of a permuted copy).
 hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* gather, int M,

@@ -11,7 +11,10 @@
 // Row order inside an expert's segment is ascending token id, independent of
 // scheduling: row = offsets[e] + base[block][e] + (number of lower tokens of the
 // same 16-token ranking block that picked e), the latter a popcount of a per-expert
-// token bitmask built with order-independent LDS atomicOr.
+// token bitmask built with order-independent LDS atomicOr.  With an expert capacity
+// cap > 0 an assignment whose rank in its expert (base + popcount) is cap or more
+// is dropped: token_row = -1 and no row is written (dropping changes the model's
+// output: WideEP explainer, "An imbalanced router creates a network hotspot").
 #include "moe_kernels.h"
 
 namespace moe {
@@ -25,7 +28,7 @@ constexpr int kCopyUnroll = 4;
 // 16-byte units long.
 __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int row16,
                                                  const int32_t* __restrict__ topk_ids, int T,
-                                                 int E, int k, int tpw,
+                                                 int E, int k, int tpw, int cap,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ bases,
                                                  u32x4* __restrict__ x_perm,
@@ -56,11 +59,11 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
     if (lane < k) {
       const int e = topk_ids[(size_t)t * k + lane];
       const int tl = t - bt0;
-      const int rank = __popcll(mask[e] & ((1ull << tl) - 1ull));
-      row = offsets[e] + bases[(size_t)blk * E + e] + rank;
+      const int rank = bases[(size_t)blk * E + e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
+      row = (cap > 0 && rank >= cap) ? -1 : offsets[e] + rank;
       if (meta) {
         token_row[(size_t)t * k + lane] = row;
-        row_token[row] = t;
+        if (row >= 0) row_token[row] = t;
       }
     }
     const u32x4* src = x + (size_t)t * row16;
@@ -73,6 +76,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
       }
       for (int j = 0; j < k; ++j) {
         const int r = __shfl(row, j, kWave);
+        if (r < 0) continue;  // dropped (uniform over the wave)
         u32x4* dst = x_perm + (size_t)r * row16;
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
   }
 }
 
-hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k,
+hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
                           const int32_t* offsets, const int32_t* bases, void* x_perm,
                           int32_t* row_token, int32_t* token_row, hipStream_t st) {
   // 4 tokens per wave for large T, 1 for small T (a workgroup's tokens always lie
@@ -94,7 +98,7 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
   int cs = 1;
   while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
   hipLaunchKernelGGL(k_permute, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
-                     ids, T, E, k, tpw, offsets, bases, static_cast<u32x4*>(x_perm), row_token,
+                     ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), row_token,
                      token_row);
   return hipGetLastError();
 }

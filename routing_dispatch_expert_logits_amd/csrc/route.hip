@@ -142,13 +142,15 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* smem
 
 // Per-expert scan of the block counts: block_counts[b][e] (rows of expert e in
 // ranking block b) becomes the number of rows of e in the blocks before b, and
-// counts_out[e] (if non-NULL) the expert's total.  Workgroup x covers experts
+// counts_out[e] (if non-NULL) the expert's total, or min(total, cap) with an
+// expert capacity cap > 0 (the slots allocated; later assignments are dropped).  Workgroup x covers experts
 // 64x .. 64x + 63, one per lane, so every load is a coalesced 256-byte row slice;
 // its 16 waves split the blocks into 16 contiguous ranges.  The experts'
 // segment starts are added by the consumer (offsets[e] + base), so no
 // workgroup waits for another.
 __global__ __launch_bounds__(1024) void k_expert_scan(int32_t* __restrict__ block_counts, int nb,
-                                                      int E, int32_t* __restrict__ counts_out) {
+                                                      int E, int cap,
+                                                      int32_t* __restrict__ counts_out) {
   __shared__ int psum[16][kWave];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int e = blockIdx.x * kWave + lane;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(1024) void k_expert_scan(int32_t* __restrict__ bloc
     run += q < w ? v : 0;
     total += v;
   }
-  if (on && w == 0 && counts_out) counts_out[e] = total;
+  if (on && w == 0 && counts_out) counts_out[e] = cap > 0 ? min(total, cap) : total;
   if (on) {
     int b = b0;
     for (; b + U <= b1; b += U) {
@@ -235,13 +237,15 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
 // tables and the row metadata, so a small step pays one launch for what the
 // large-T path does in four.  Row order inside an expert's segment is ascending
 // token id, as there: row = offsets[e] + popcount(mask[e] below t), mask[e] the
-// tokens that picked e (built with order-independent LDS atomicOr).
+// tokens that picked e (built with order-independent LDS atomicOr).  With an
+// expert capacity cap > 0, assignments ranked cap or later in their expert are
+// dropped (token_row = -1) and counts are min(count, cap).
 template <int SLOTS>
 __global__ __launch_bounds__(1024) void k_route_small(
     const float* __restrict__ scores_in, const float* __restrict__ bias, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
-    int bm, int32_t* __restrict__ mtile_start) {
+    int cap, int bm, int32_t* __restrict__ mtile_start) {
   __shared__ int cnt[kMaxE];
   __shared__ int off_s[kMaxE];
   __shared__ unsigned long long mask[kMaxE];
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
     }
   }
   __syncthreads();
-  const int c = tid < E ? cnt[tid] : 0;
+  const int c = tid < E ? (cap > 0 ? min(cnt[tid], cap) : cnt[tid]) : 0;
   int total = 0;
   const int off = block_exclusive_scan(c, &total, smem);
   if (tid < E) {
@@ -289,9 +293,13 @@ __global__ __launch_bounds__(1024) void k_route_small(
   __syncthreads();
   for (int a = tid; a < T * k; a += 1024) {
     const int t = a / k, e = s_ids[a];
-    const int row = off_s[e] + __popcll(mask[e] & ((1ull << t) - 1ull));
-    token_row[a] = row;
-    row_token[row] = t;
+    const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
+    if (cap > 0 && rank >= cap) {
+      token_row[a] = -1;  // dropped: past the expert's capacity
+    } else {
+      token_row[a] = off_s[e] + rank;
+      row_token[off_s[e] + rank] = t;
+    }
   }
 }
 
@@ -329,10 +337,10 @@ hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int32_t* counts_out,
+hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int cap, int32_t* counts_out,
                               hipStream_t st) {
   hipLaunchKernelGGL(k_expert_scan, dim3(ceil_div(E, kWave)), dim3(1024), 0, st, block_counts, nb, E,
-                     counts_out);
+                     cap, counts_out);
   return hipGetLastError();
 }
 
@@ -345,13 +353,14 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
 
 hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                             int32_t* token_row, int bm, int32_t* mtile_start, hipStream_t st) {
+                             int32_t* token_row, int cap, int bm, int32_t* mtile_start,
+                             hipStream_t st) {
   if (T > kSmallT) return hipErrorInvalidValue;
   const int slots = ceil_div(E, kWave);
   dim3 g(1), b(1024);
 #define MOE_RS(SL)                                                                                   \
   hipLaunchKernelGGL((k_route_small<SL>), g, b, 0, st, scores, bias, T, E, k, ids, w, counts, offsets, \
-                     row_token, token_row, bm, mtile_start)
+                     row_token, token_row, cap, bm, mtile_start)
   if (slots <= 1) MOE_RS(1);
   else if (slots <= 2) MOE_RS(2);
   else if (slots <= 4) MOE_RS(4);

@@ -35,7 +35,7 @@ def ws(s: B.MoeShape, call: int) -> torch.Tensor:
 
 
 def shape_of(cfg) -> B.MoeShape:
-    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I)
+    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
 
 
 def act_kind(cfg) -> str:

@@ -48,8 +48,8 @@ def test_abi_version_and_status_strings():
 
 
 def _bytes(cfg, call):
-    return B.workspace_bytes(B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I),
-                             call)
+    return B.workspace_bytes(B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I,
+                                     cfg.capacity), call)
 
 
 @pytest.mark.parametrize("cfg", list(FULL_CONFIGS.values()) + list(PARITY_CONFIGS.values()),
@@ -100,6 +100,7 @@ def test_route_rejects_bad_arguments_on_host():
     assert _route(bad) == B.MOE_ERR_INVALID_ARG
     assert _route(B.shape(64, 128, 8, 2, 256, shared_I=96)) == B.MOE_ERR_UNSUPPORTED   # bf16: % 64
     assert _route(B.shape(64, 128, 8, 2, 256, L=64, shared_I=128)) == B.MOE_ERR_UNSUPPORTED  # latent
+    assert _route(B.shape(64, 128, 8, 2, 256, capacity=-1)) == B.MOE_ERR_INVALID_ARG
     bad = B.shape(64, 128, 8, 2, 256)
     bad.dtype = 7
     assert _route(bad) == B.MOE_ERR_INVALID_ARG

@@ -51,7 +51,7 @@ def _route_gpu(cfg, logits, bias):
 
 def _check_route(cfg, logits, bias):
     ids, w, counts, offs = _route_gpu(cfg, logits, bias)
-    ref = oracle.route(oracle.router_scores(logits, bias), cfg.k, cfg.E)
+    ref = oracle.route(oracle.router_scores(logits, bias), cfg.k, cfg.E, cfg.capacity)
     np.testing.assert_array_equal(ids, ref["ids"])
     np.testing.assert_array_equal(counts, ref["counts"])
     np.testing.assert_array_equal(offs, ref["offsets"])
@@ -112,28 +112,30 @@ def test_gate_logits(cfg):
 @pytest.mark.parametrize("cfg", CFGS, ids=IDS)
 def test_dispatch_permute_bit_exact(cfg):
     lg, bias = _scores_input(cfg)
-    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
-    rt, tr = oracle.permutation(ref["ids"], cfg.E)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E, cfg.capacity)
+    rt, tr = oracle.permutation(ref["ids"], cfg.E, cfg.capacity)
     x = gen.activations(cfg)
     s = shape_of(cfg)
     R, D = cfg.R, cfg.H
-    sc = s if not cfg.L else B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, 0, cfg.dtype)
+    sc = s if not cfg.L else B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, 0, cfg.dtype, 0, cfg.capacity)
     x_perm = empty((R, D), act_kind(cfg))
     row_token, token_row = empty((R,), "i32"), empty((cfg.T, cfg.k), "i32")
     B.dispatch_permute(dev(x), dev(ref["ids"].astype(np.int32)), dev(ref["offsets"].astype(np.int32)),
                        x_perm, row_token, token_row, sc, ws(sc, B.MOE_CALL_DISPATCH))
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(row_token), rt)
+    n = len(rt)                      # kept rows (all T*k without a capacity)
+    np.testing.assert_array_equal(host(row_token)[:n], rt)
     np.testing.assert_array_equal(host(token_row), tr)
-    xp = host(x_perm, bf16=cfg.dtype == "bf16")
+    xp = host(x_perm, bf16=cfg.dtype == "bf16")[:n]
     np.testing.assert_array_equal(xp, oracle.gather_rows(x, rt))
-    assert xp.nbytes == oracle.dispatch_bytes(cfg.T, cfg.k, D, cfg.elem_bytes)
+    if not cfg.capacity:
+        assert xp.nbytes == oracle.dispatch_bytes(cfg.T, cfg.k, D, cfg.elem_bytes)
 
 
 def _ffn_inputs(cfg):
     lg, bias = _scores_input(cfg)
-    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
-    rt, _ = oracle.permutation(ref["ids"], cfg.E)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E, cfg.capacity)
+    rt, _ = oracle.permutation(ref["ids"], cfg.E, cfg.capacity)
     x = gen.draw(cfg, gen.TAG_X, 0, (cfg.T, cfg.D), cfg.x_std)
     return ref, oracle.gather_rows(x, rt)
 
@@ -168,7 +170,7 @@ def test_grouped_ffn(cfg):
     torch.cuda.synchronize()
     ref_y = oracle.grouped_expert_ffn(xp, ref["offsets"], wts["w1"], wts["w3"], wts["w2"],
                                       bf16=cfg.dtype == "bf16")
-    _check_y(cfg, host(y, bf16=cfg.dtype == "bf16"), ref_y)
+    _check_y(cfg, host(y, bf16=cfg.dtype == "bf16")[:len(ref_y)], ref_y)
 
 
 def test_grouped_ffn_never_reads_empty_experts():
@@ -197,8 +199,8 @@ def test_grouped_ffn_never_reads_empty_experts():
 @pytest.mark.parametrize("cfg", CFGS, ids=IDS)
 def test_combine(cfg):
     lg, bias = _scores_input(cfg)
-    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
-    _, tr = oracle.permutation(ref["ids"], cfg.E)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E, cfg.capacity)
+    _, tr = oracle.permutation(ref["ids"], cfg.E, cfg.capacity)
     w32 = ref["weights"].astype(np.float32)
     y = gen.stage_rows(cfg, cfg.R, cfg.D)
     s = shape_of(cfg)
@@ -223,8 +225,8 @@ def test_combine(cfg):
 def test_combine_with_shared_term(cfg):
     """A shared expert's output enters the combine with weight 1, after the k routed terms."""
     lg, bias = _scores_input(cfg)
-    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
-    _, tr = oracle.permutation(ref["ids"], cfg.E)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E, cfg.capacity)
+    _, tr = oracle.permutation(ref["ids"], cfg.E, cfg.capacity)
     w32 = ref["weights"].astype(np.float32)
     y = gen.stage_rows(cfg, cfg.R, cfg.D)
     ysh = gen.stage_rows(cfg, cfg.T, cfg.D, index=1)
@@ -284,15 +286,16 @@ def test_layer_forward(cfg):
     inp = gen.layer_inputs(cfg)
     bf = cfg.dtype == "bf16"
     got = run_layer(cfg, inp)
-    ref = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=bf)
+    ref = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=bf, capacity=cfg.capacity)
     if "logits" in inp:   # given router output: routing must be bit-exact everywhere
         keep = np.ones(cfg.T, dtype=bool)
         np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
         np.testing.assert_array_equal(got["counts"], ref["counts"])
         np.testing.assert_array_equal(got["offsets"], ref["offsets"])
-        np.testing.assert_array_equal(got["row_token"], ref["row_token"])
+        np.testing.assert_array_equal(got["row_token"][:len(ref["row_token"])], ref["row_token"])
         np.testing.assert_array_equal(got["token_row"], ref["token_row"])
     else:                 # computed logits: compare routing where the scores decide it uniquely
+        assert not cfg.capacity, "capacity layers use given logits (dropping needs exact routing)"
         tol = 1e-5 * float(np.sqrt(np.mean(ref["logits"] ** 2)))
         assert rel_err(got["logits"], ref["logits"]) <= 1e-5
         keep = unambiguous_tokens(ref["logits"], cfg.k, tol)
@@ -329,7 +332,8 @@ def test_layer_matches_separate_calls_and_is_deterministic(name):
 
 
 @pytest.mark.parametrize("name", ["shared_expert", "shared_expert_decode", "shared_expert_f32",
-                                  "small_bf16_decode", "single_token", "many_empty"])
+                                  "small_bf16_decode", "single_token", "many_empty",
+                                  "capacity_prefill", "capacity_decode", "capacity_f32"])
 def test_layer_output_equals_separate_calls(name):
     """Fused layer == route, permute, grouped FFN, (the shared expert as a
     one-expert grouped FFN over all tokens,) and the combine, bit for bit: the
@@ -361,8 +365,11 @@ def test_layer_output_equals_separate_calls(name):
               shared_out=ysh)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(out), a["out"])
-    for n, t in (("x_perm", xp), ("row_token", rt), ("token_row", tr)):
-        np.testing.assert_array_equal(host(t, cfg.dtype == "bf16" and n == "x_perm"), a[n], err_msg=n)
+    kept = int(offs[-1])
+    for n, t in (("x_perm", xp), ("row_token", rt)):
+        np.testing.assert_array_equal(host(t, cfg.dtype == "bf16" and n == "x_perm")[:kept], a[n][:kept],
+                                      err_msg=n)
+    np.testing.assert_array_equal(host(tr), a["token_row"])
     if cfg.shared_I:  # and the shared expert alone matches the oracle's
         bf = cfg.dtype == "bf16"
         ref_sh = oracle.shared_expert_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"], bf)

@@ -494,3 +494,69 @@ def test_token_outputs_match_whole_layer_with_shared_expert():
     ew = {e: (inp["w1"][e], inp["w3"][e], inp["w2"][e]) for e in range(cfg.E)}
     got = oracle.token_outputs(inp, tok, ref["ids"][tok], ref["weights"][tok], ew, bf16=True)
     np.testing.assert_allclose(got, ref["out"][tok], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------ expert capacity (dropping)
+
+def test_capacity_worked_example():
+    """Hand-worked: 4 tokens, 3 experts, k = 2, capacity 2 per expert."""
+    ids = np.array([[0, 1], [0, 2], [0, 1], [1, 0]])
+    rt, tr = oracle.permutation(ids, 3, capacity=2)
+    # expert 0 keeps tokens 0, 1 (drops 2, 3); expert 1 keeps 0, 2 (drops 3); expert 2 keeps 1
+    np.testing.assert_array_equal(rt, [0, 1, 0, 2, 1])
+    np.testing.assert_array_equal(tr, [[0, 2], [1, 4], [-1, 3], [-1, -1]])
+    r = oracle.route(np.array([[3., 2., 1.], [3., 1., 2.], [3., 2., 1.], [2., 3., 1.]], np.float32),
+                     2, 3, capacity=2)
+    np.testing.assert_array_equal(r["ids"], ids)
+    np.testing.assert_array_equal(r["routed_counts"], [4, 3, 1])
+    np.testing.assert_array_equal(r["counts"], [2, 2, 1])
+    np.testing.assert_array_equal(r["offsets"], [0, 2, 4, 5])
+
+
+@pytest.mark.parametrize("C", [1, 3, 7])
+def test_capacity_keeps_each_experts_first_tokens(C):
+    r = _rng(40 + C)
+    T, E, k = 60, 9, 3
+    ids = oracle.topk_ids(r.standard_normal((T, E)).astype(np.float32), k)
+    rt, tr = oracle.permutation(ids, E, capacity=C)
+    counts = oracle.expert_counts(ids, E)
+    assert int((tr < 0).sum()) == int(np.maximum(counts - C, 0).sum())
+    for e in range(E):
+        toks = sorted(t for t in range(T) if e in ids[t])
+        keep = set(toks[:C])
+        for t in toks:
+            j = int(np.nonzero(ids[t] == e)[0][0])
+            assert (tr[t, j] >= 0) == (t in keep)
+            if t in keep:
+                assert rt[tr[t, j]] == t
+    # kept rows are expert-contiguous and ascending inside each segment
+    off = oracle.segment_offsets(np.minimum(counts, C))
+    for e in range(E):
+        seg = rt[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_capacity_above_max_count_changes_nothing():
+    cfg = PARITY_CONFIGS["small_bf16_zipf"]
+    inp = gen.layer_inputs(cfg)
+    a = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True)
+    b = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True, capacity=int(a["counts"].max()))
+    for key in ("ids", "counts", "offsets", "row_token", "token_row", "out"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_capacity_drops_only_the_dropped_terms():
+    """Each token's output is the sum over its kept assignments only (brute force)."""
+    cfg = PARITY_CONFIGS["small_bf16_zipf"]
+    inp = gen.layer_inputs(cfg)
+    C = 40
+    full = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True)
+    cap = oracle.layer_forward(inp, k=cfg.k, E=cfg.E, bf16=True, capacity=C)
+    assert (cap["token_row"] < 0).any() and (cap["token_row"] >= 0).any()
+    y_full = full["y_perm"]
+    for t in range(cfg.T):
+        want = np.zeros(cfg.D)
+        for j in range(cfg.k):
+            if cap["token_row"][t, j] >= 0:      # same expert row value with or without dropping
+                want += full["weights"][t, j] * y_full[full["token_row"][t, j]]
+        np.testing.assert_allclose(cap["out"][t], want, rtol=1e-12, atol=1e-14)

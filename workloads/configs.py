@@ -36,6 +36,7 @@ class MoEConfig:
     zipf_alpha: float = 0.0
     const_logits: bool = False         # every router logit equal (all-tie routing)
     shared_I: int = 0                  # shared expert intermediate width (0 = none)
+    capacity: int = 0                  # rows kept per expert (0 = no limit, nothing dropped)
 
     @property
     def D(self) -> int:
@@ -133,4 +134,12 @@ PARITY_CONFIGS = {c.name: c for c in (
               gate_std=None, zipf_s=1.2, zipf_alpha=ZIPF_ALPHA, shared_I=256),
     MoEConfig(name="shared_expert_f32", T=97, H=96, E=6, k=3, I=80, dtype="f32", seed=25,
               w_std=0.05, gate="computed", gate_std=0.1, shared_I=64),
+    # expert capacity (value-changing dropping) on skewed routing: 128-row tiles,
+    # the decode-scale path and fp32
+    MoEConfig(name="capacity_prefill", T=300, H=256, E=16, k=4, I=192, seed=26, gate="drawn",
+              zipf_s=1.1, zipf_alpha=1.0, capacity=60),
+    MoEConfig(name="capacity_decode", T=24, H=512, E=96, k=6, I=128, seed=27, gate="drawn",
+              zipf_s=1.2, zipf_alpha=1.0, capacity=2),
+    MoEConfig(name="capacity_f32", T=97, H=96, E=6, k=3, I=80, dtype="f32", seed=28, w_std=0.05,
+              gate="drawn", zipf_s=1.1, zipf_alpha=1.0, capacity=40),
 )}
