@@ -90,9 +90,11 @@ class HipEvents:
 def stage_bytes_flops(cfg, counts):
     """Algorithmic HBM bytes and FLOPs per stage for one layer forward.
 
-    b = element bytes of activations/weights; touched = experts with >= 1 row.
+    b = element bytes of activations/weights; touched = experts with >= 1 row; the
+    row count R is the rows kept (all T*k unless an expert capacity drops some).
     """
-    T, H, E, k, I, L, D, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.D, cfg.R
+    T, H, E, k, I, L, D = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.D
+    R = int(sum(counts))
     b = cfg.elem_bytes
     touched = int(sum(1 for c in counts if c > 0))
     out_b = 2 if cfg.dtype == "bf16" else 4
@@ -340,6 +342,8 @@ def main(argv=None):
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra layers timed after a 1 GiB cache-evicting write each (0: none)")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="expert capacity C = ceil(f * T * k / E) rows (drops the rest; value-changing)")
     ap.add_argument("--ep-rank-share", type=int, default=0,
                     help="time the grouped expert FFN at one rank's share of R-way expert parallelism")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -357,6 +361,8 @@ def main(argv=None):
     from workloads import FULL_CONFIGS, generator as gen
 
     cfg = FULL_CONFIGS[args.config]
+    if args.capacity_factor > 0:
+        cfg = cfg.with_(capacity=int(np.ceil(args.capacity_factor * cfg.R / cfg.E)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} L={cfg.L} {cfg.dtype}")
@@ -372,7 +378,7 @@ def main(argv=None):
         w["gate_bias"] = up(inp["bias"])
     x = up(inp["x"])
     logits = up(inp["logits"]) if "logits" in inp else torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I)
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
     ws = torch.empty(B.workspace_bytes(s, B.MOE_CALL_LAYER), dtype=torch.uint8, device=dev)
     od = B.MOE_BF16 if args.out_dtype == "bf16" and cfg.dtype == "bf16" else B.MOE_F32
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16 if od == B.MOE_BF16 else torch.float32, device=dev)
@@ -523,6 +529,8 @@ def main(argv=None):
         "stages": stages,
         "p95_skew": round(p95, 3) if p95 is not None else None,
         "touched_experts": touched,
+        "expert_capacity": cfg.capacity,
+        "dropped_assignments": int(cfg.R - int(cnt.sum())),
         "dispatch_bytes": cfg.T * cfg.k * cfg.D * cfg.elem_bytes,
         "dispatch_bytes_full_width": cfg.T * cfg.k * cfg.H * cfg.elem_bytes,
         "resident_expert_bytes": resident,
