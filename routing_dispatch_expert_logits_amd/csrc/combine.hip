@@ -91,7 +91,12 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
     my_row = token_row[(size_t)t * k + lane];
     my_w = topk_w[(size_t)t * k + lane];
   }
-  for (int c = c0 + lane; c < c1; c += kWave) {
+  // The trip count is wave-uniform so every lane takes part in the shuffles of the
+  // row indices and weights (a shuffle from an inactive lane returns no defined
+  // value); lanes past the end of the row clamp their loads and store nothing.
+  for (int cb = c0; cb < c1; cb += kWave) {
+    const bool on = cb + lane < c1;
+    const int c = on ? cb + lane : c1 - 1;
     float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.f;
@@ -117,13 +122,14 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
     }
     for (; j < k; ++j) {
       const int r = __shfl(my_row, j, kWave);
-      if (r < 0) continue;
       const float wj = __shfl(my_w, j, kWave);
+      if (r < 0) continue;
       float f[NV];
       Vec16<IT>::unpack(y[(size_t)r * row16 + c], f);
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
     }
+    if (!on) continue;
     if (add) add_row<IT>(acc, add[(size_t)t * row16 + c]);
     store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
   }

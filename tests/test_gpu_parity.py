@@ -21,7 +21,7 @@ import pytest
 import torch
 
 import oracle
-from workloads import PARITY_CONFIGS, generator as gen
+from workloads import MoEConfig, PARITY_CONFIGS, generator as gen
 from routing_dispatch_expert_logits_amd import binding as B
 from tests.gpu_util import (dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits, rel_err,
                             check_permutation_valid, out_err_over_rms)
@@ -227,6 +227,36 @@ def test_combine_with_shared_term(cfg):
     lg, bias = _scores_input(cfg)
     ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E, cfg.capacity)
     _, tr = oracle.permutation(ref["ids"], cfg.E, cfg.capacity)
+    w32 = ref["weights"].astype(np.float32)
+    y = gen.stage_rows(cfg, cfg.R, cfg.D)
+    ysh = gen.stage_rows(cfg, cfg.T, cfg.D, index=1)
+    s = shape_of(cfg)
+    got = {}
+    for flags in (B.MOE_COMBINE_FUSED, B.MOE_COMBINE_UNFUSED):
+        o = empty((cfg.T, cfg.D), "f32")
+        B.combine(dev(y), dev(tr.astype(np.int32)), dev(w32), o, B.MOE_F32, flags, s,
+                  ws(s, B.MOE_CALL_COMBINE), shared_out=dev(ysh))
+        got[flags] = o
+    torch.cuda.synchronize()
+    f32 = host(got[B.MOE_COMBINE_FUSED])
+    assert rel_err(f32, oracle.combine(y, tr, w32.astype(np.float64), ysh)) <= 1e-5
+    np.testing.assert_array_equal(host(got[B.MOE_COMBINE_UNFUSED]), f32)
+
+
+# Rows whose last 64-lane column pass leaves fewer active lanes than k: every lane
+# must still take part in the shuffles of the k row indices and weights.
+NARROW = [MoEConfig(name="narrow_f32_k7", T=50, H=16, E=20, k=7, I=16, dtype="f32", seed=31,
+                    gate="drawn"),
+          MoEConfig(name="narrow_bf16_k9", T=33, H=64, E=12, k=9, I=64, seed=32, gate="drawn"),
+          MoEConfig(name="split_tail_bf16_k16", T=256, H=1088, E=64, k=16, I=64, seed=33,
+                    gate="drawn")]
+
+
+@pytest.mark.parametrize("cfg", NARROW, ids=[c.name for c in NARROW])
+def test_combine_rows_narrower_than_k(cfg):
+    lg, bias = _scores_input(cfg)
+    ref = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
+    _, tr = oracle.permutation(ref["ids"], cfg.E)
     w32 = ref["weights"].astype(np.float32)
     y = gen.stage_rows(cfg, cfg.R, cfg.D)
     ysh = gen.stage_rows(cfg, cfg.T, cfg.D, index=1)
