@@ -368,7 +368,8 @@ def route(scores_f32: np.ndarray, k: int, E: int, capacity: int = 0) -> Dict[str
 
 
 def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool, capacity: int = 0,
-                  timers: Optional[Dict[str, float]] = None) -> Dict[str, np.ndarray]:
+                  timers: Optional[Dict[str, float]] = None,
+                  dispatch: str = "dtype") -> Dict[str, np.ndarray]:
     """The whole routed-expert layer forward on one device, every stage kept.
 
     ``inp`` holds x, then either logits (given router output) or gate_w, an
@@ -379,7 +380,11 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool, cap
     receives the wall-clock seconds of routing, permutation, expert FFN and
     combine (the stage timers of Three Parameter Counts, "What the utilization
     dashboard smooths away").  ``capacity`` C > 0 drops each expert's assignments
-    beyond its first C (value-changing, see ``permutation``).
+    beyond its first C (value-changing, see ``permutation``).  ``dispatch="mxfp8"``
+    (bf16 layers) sends the dispatched rows as MXFP8 and runs the gate/up
+    contraction on MXFP8 rows and weights (value-changing, see ``oracle.mxfp8``):
+    each token row is quantised once (``x_q``, ``x_scale``), the permutation copies
+    codes and scales, and W1 / W3 are quantised along their contraction axis.
     """
     clock = [time.perf_counter()]
 
@@ -406,10 +411,24 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool, cap
         src = res["z"]
     else:
         src = decode(inp["x"])
-    res["x_perm"] = gather_rows(src, rt)
-    lap("permutation")
-    res["y_perm"] = grouped_expert_ffn(res["x_perm"], res["offsets"], inp["w1"], inp["w3"],
-                                       inp["w2"], bf16)
+    if dispatch == "mxfp8":
+        from . import mxfp8
+        assert bf16, "MXFP8 dispatch of bf16 layers"
+        res["x_q"], res["x_scale"] = mxfp8.mx_quantize(src)
+        res["x_perm_q"] = res["x_q"][rt]
+        res["x_perm_scale"] = res["x_scale"][rt]
+        lap("permutation")
+        res["w1_q"], res["w1_scale"] = mxfp8.mx_quantize(decode(inp["w1"]))
+        res["w3_q"], res["w3_scale"] = mxfp8.mx_quantize(decode(inp["w3"]))
+        res["y_perm"] = mxfp8.grouped_expert_ffn_mx(res["x_perm_q"], res["x_perm_scale"], res["offsets"],
+                                                    res["w1_q"], res["w1_scale"], res["w3_q"],
+                                                    res["w3_scale"], inp["w2"])
+    else:
+        assert dispatch == "dtype"
+        res["x_perm"] = gather_rows(src, rt)
+        lap("permutation")
+        res["y_perm"] = grouped_expert_ffn(res["x_perm"], res["offsets"], inp["w1"], inp["w3"],
+                                           inp["w2"], bf16)
     lap("expert_ffn")
     if "ws1" in inp:
         assert "wd" not in inp, "shared expert on non-latent layers only"
