@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 F32_PEAK_TFLOPS = 157.3
 GEMM_SRC = os.path.join(ROOT, "routing_dispatch_expert_logits_amd", "csrc", "gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{config}.json")
@@ -103,8 +104,14 @@ def stage_bytes_flops(cfg, counts):
     st["gate"] = ((T * H * b + E * H * 4 + T * E * 4, 2 * T * H * E) if cfg.gate == "computed"
                   else (0, 0))
     st["route"] = (T * E * 4 + 8 * R + (2 * E + 1) * 4, 0)
-    st["permute"] = (T * D * b + R * D * b + 12 * R, 0)
-    st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
+    if cfg.dispatch == "mxfp8":
+        # rows and W1 / W3 as one code byte per element plus one scale byte per 32
+        q = D * 33 // 32
+        st["permute"] = (T * D * b + R * q + 12 * R, 0)
+        st["gemm_gate_up"] = (touched * 2 * q * I + R * q + R * I * b, 4 * R * D * I)
+    else:
+        st["permute"] = (T * D * b + R * D * b + 12 * R, 0)
+        st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
     st["gemm_down"] = (touched * D * I * b + R * I * b + R * D * b, 2 * R * D * I)
     Is = cfg.shared_I
     st["shared_expert"] = ((T * H * b + 3 * Is * H * b + 2 * T * Is * b + T * H * b, 6 * T * H * Is)
@@ -232,7 +239,8 @@ def cpu_baseline(cfg, inp, target_s):
             sub["logits"] = inp["logits"][:n]
         timers = {}
         t0 = time.perf_counter()
-        oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers)
+        oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers,
+                             dispatch=cfg.dispatch)
         dt = time.perf_counter() - t0
         log(f"cpu oracle: {n} tokens in {dt:.2f} s")
         if dt >= target_s / 3 or n >= cfg.T:
@@ -242,7 +250,8 @@ def cpu_baseline(cfg, inp, target_s):
     if n >= cfg.T:
         while total < target_s:
             t0 = time.perf_counter()
-            oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers)
+            oracle.layer_forward(sub, k=cfg.k, E=cfg.E, bf16=cfg.dtype == "bf16", timers=timers,
+                                 dispatch=cfg.dispatch)
             total += time.perf_counter() - t0
             runs += 1
         log(f"cpu oracle: whole layer {runs} times in {total:.2f} s")
@@ -273,9 +282,15 @@ def gate_up_kernel(cfg):
     weight-streaming tiles below 48 rows, SIMT for fp32)."""
     if cfg.dtype != "bf16":
         return "k_gemm_simt<SwiGLU> (expert gate/up GEMM, fp32)"
+    mx = cfg.dispatch == "mxfp8"
     if cfg.R >= 48 * cfg.E:
+        if mx:
+            g = "2" if -(-cfg.I // 128) >= 16 else "1"
+            return f"k_gemm_ws<128,128,2,SwiGLU,3,8,64,{g},MXFP8> (expert gate/up GEMM, MXFP8)"
         g = ",64,2" if -(-cfg.I // 128) >= 16 else ""
         return f"k_gemm_ws<128,128,2,SwiGLU,3,8{g}> (expert gate/up GEMM)"
+    if mx:
+        return "k_gemm_decode<2,2,SwiGLU,MXFP8> (expert gate/up GEMM, MXFP8)"
     return "k_gemm_decode<2,2,SwiGLU> (expert gate/up GEMM)"
 
 
@@ -342,6 +357,9 @@ def main(argv=None):
     ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra layers timed after a 1 GiB cache-evicting write each (0: none)")
+    ap.add_argument("--dispatch", default="dtype", choices=["dtype", "mxfp8"],
+                    help="mxfp8: dispatched rows and W1 / W3 as MXFP8 (value-changing; the accuracy "
+                         "change against the bf16 layer is reported)")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="expert capacity C = ceil(f * T * k / E) rows (drops the rest; value-changing)")
     ap.add_argument("--ep-rank-share", type=int, default=0,
@@ -363,6 +381,8 @@ def main(argv=None):
     cfg = FULL_CONFIGS[args.config]
     if args.capacity_factor > 0:
         cfg = cfg.with_(capacity=int(np.ceil(args.capacity_factor * cfg.R / cfg.E)))
+    if args.dispatch != "dtype":
+        cfg = cfg.with_(dispatch=args.dispatch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} L={cfg.L} {cfg.dtype}")
@@ -378,12 +398,37 @@ def main(argv=None):
         w["gate_bias"] = up(inp["bias"])
     x = up(inp["x"])
     logits = up(inp["logits"]) if "logits" in inp else torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
-    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity,
+                cfg.dispatch)
     ws = torch.empty(B.workspace_bytes(s, B.MOE_CALL_LAYER), dtype=torch.uint8, device=dev)
     od = B.MOE_BF16 if args.out_dtype == "bf16" and cfg.dtype == "bf16" else B.MOE_F32
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16 if od == B.MOE_BF16 else torch.float32, device=dev)
     counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
     aux = {"counts": counts}
+    mx_info = None
+    if cfg.dispatch == "mxfp8":
+        # the bf16 layer once on the same inputs (for the accuracy change), then W1 / W3
+        # converted once on the GPU (offline weight preparation, timed on its own)
+        s16 = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
+        ws16 = torch.empty(B.workspace_bytes(s16, B.MOE_CALL_LAYER), dtype=torch.uint8, device=dev)
+        out16 = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+        B.layer_forward(w, x, logits, out16, B.MOE_F32, s16, ws16)
+        del ws16
+        hq = HipEvents()
+        qe = hq.create(2)
+        stream0 = torch.cuda.current_stream().cuda_stream
+        hq.record(qe[0], stream0)
+        for n in ("w1", "w3"):
+            q = torch.empty((cfg.E, cfg.I, cfg.D), dtype=torch.uint8, device=dev)
+            sc = torch.empty((cfg.E, cfg.I, cfg.D // 32), dtype=torch.uint8, device=dev)
+            B.quantize_mxfp8(w[n], q, sc, stream=stream0)
+            w[n], w[n + "_scale"] = q, sc
+        hq.record(qe[1], stream0)
+        torch.cuda.synchronize()
+        mx_info = {"format": "MXFP8 E4M3, one E8M0 scale per 32 along K",
+                   "weight_conversion_ms": round(hq.elapsed_ms(qe[0], qe[1]), 4),
+                   "out_bf16_dispatch": out16}
+        hq.destroy(qe)
     torch.cuda.synchronize()
     resident = sum(t.numel() * t.element_size() for t in w.values())
     log(f"uploaded; resident weights {resident / 1e9:.2f} GB, workspace {ws.numel() / 1e9:.2f} GB")
@@ -438,7 +483,19 @@ def main(argv=None):
 
     combine_alone = time_combine_alone(B, torch, cfg, w, x, logits, od, s, ws, counts, stream, hip)
     ep_share = (ep_rank_share(B, torch, np, gen, cfg, args.ep_rank_share, up, stream, hip)
-                if args.ep_rank_share > 1 else None)
+                if args.ep_rank_share > 1 and cfg.dispatch == "dtype" else None)
+    if mx_info is not None:
+        # the value change against the bf16 layer (same inputs, same routing)
+        o32 = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=dev)
+        B.layer_forward(w, x, logits, o32, B.MOE_F32, s, ws, stream=stream)
+        torch.cuda.synchronize()
+        ref16 = mx_info.pop("out_bf16_dispatch").double()
+        d = o32.double() - ref16
+        rms = float(torch.sqrt(torch.mean(ref16 * ref16)))
+        mx_info["accuracy_vs_bf16_dispatch"] = {
+            "max_abs_over_rms": round(float(d.abs().max()) / rms, 5),
+            "rms_over_rms": round(float(torch.sqrt(torch.mean(d * d))) / rms, 5)}
+        log(f"MXFP8 vs bf16 dispatch: {mx_info['accuracy_vs_bf16_dispatch']}")
 
     if args.copy_calibration_mib:
         nbytes = args.copy_calibration_mib << 20
@@ -498,8 +555,10 @@ def main(argv=None):
             "kernel": gate_up_kernel(cfg),
             "algorithmic_bytes": int(g_bytes), "avg_ms": round(stage_ms["gemm_gate_up"], 5),
             "mfma_tflops": round(g_flops / g_s / 1e12, 1),
-            "mfma_frac": round(g_flops / g_s / 1e12 / (BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else F32_PEAK_TFLOPS), 4)}
-    tf = TRAFFIC_FILE.format(config=cfg.name)
+            "mfma_frac": round(g_flops / g_s / 1e12 / (
+                F32_PEAK_TFLOPS if cfg.dtype != "bf16" else FP8_PEAK_TFLOPS if cfg.dispatch == "mxfp8"
+                else BF16_PEAK_TFLOPS), 4)}
+    tf = TRAFFIC_FILE.format(config=cfg.name + ("_mxfp8" if cfg.dispatch == "mxfp8" else ""))
     if os.path.exists(tf):
         tr = json.load(open(tf))
         if tr.get("gemm_src_sha256_16") == src_hash(GEMM_SRC):
@@ -513,10 +572,11 @@ def main(argv=None):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": ("mxfp8-e4m3/bf16" if cfg.dispatch == "mxfp8" else "bf16") if cfg.dtype == "bf16" else "f32",
         "data": "synthetic: seeded numpy PCG64 inputs, random-init weights",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "L": cfg.L, "out_dtype": "bf16" if od == B.MOE_BF16 else "f32"},
+                   "I": cfg.I, "L": cfg.L, "out_dtype": "bf16" if od == B.MOE_BF16 else "f32",
+                   "dispatch": cfg.dispatch},
         "grouped_gemm_tflops": round((sb["gemm_gate_up"][1] + sb["gemm_down"][1]) / (gemm_ms * 1e-3) / 1e12, 1),
         "permute_gbps": stages["permute"]["GB/s"],
         "combine_gbps": stages["combine"]["GB/s"],
@@ -531,7 +591,9 @@ def main(argv=None):
         "touched_experts": touched,
         "expert_capacity": cfg.capacity,
         "dropped_assignments": int(cfg.R - int(cnt.sum())),
-        "dispatch_bytes": cfg.T * cfg.k * cfg.D * cfg.elem_bytes,
+        "dispatch_bytes": (cfg.T * cfg.k * cfg.D * 33 // 32 if cfg.dispatch == "mxfp8"
+                           else cfg.T * cfg.k * cfg.D * cfg.elem_bytes),
+        "mxfp8": mx_info,
         "dispatch_bytes_full_width": cfg.T * cfg.k * cfg.H * cfg.elem_bytes,
         "resident_expert_bytes": resident,
         "roofline": roof,

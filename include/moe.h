@@ -48,6 +48,28 @@
  * Limits: 1 <= k <= E, E <= 1024, k <= 64; T*k < 2^31; bf16 layers need D % 64 == 0,
  * I % 64 == 0, (latent layers) H % 64 == 0 and (shared expert) shared_I % 64 == 0;
  * fp32 layers need D % 4 == 0 and H % 4 == 0.  A shared expert needs L == 0.
+ * MXFP8 dispatch needs a bf16 layer and D % 128 == 0.
+ *
+ * MXFP8 dispatch (moe_shape.dispatch = MOE_DISPATCH_MXFP8; value-changing)
+ * -------------------------------------------------------------------------
+ * "Top-k multiplies traffic. Locality subtracts it." (WideEP explainer): a runtime
+ * may quantise the outbound activation, carry scales, compute in another format
+ * and return at higher precision; the comparison must count the conversion
+ * kernels, the scale metadata and the accuracy impact.  Quantisation is a
+ * value-changing optimisation ("Three Parameter Counts...", table of "Which
+ * optimizations need a task-level gate").  The format is OCP MX "MXFP8-E4M3", the
+ * one gfx950's scaled matrix instructions take: E4M3 codes (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, largest magnitude 448) with one E8M0 scale
+ * byte 2^(s-127) per 32 consecutive elements of a row along the contraction axis.
+ * A block with largest magnitude m gets s = 127 + floor(log2 m) - 8 (clamped to
+ * 0..254; an all-zero block gets 0), and each element is divided by the scale,
+ * clamped to +-448 and rounded to the nearest E4M3 value, ties to even
+ * (moe_quantize_mxfp8).  Then the dispatched rows x_perm are [T*k x D] codes plus
+ * x_perm_scale [T*k x D/32] scales (one byte per element plus one per 32: the
+ * dispatch bytes become T*k*D*33/32), W1 / W3 are codes [E x I x D] with scales
+ * [E x I x D/32], the gate/up products run on the fp8 matrix cores with fp32
+ * accumulation, and everything after them (SwiGLU intermediate, W2, Y, combine)
+ * stays bf16.  Routing does not change.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -59,7 +81,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 #ifndef MOE_API
 #define MOE_API __attribute__((visibility("default")))
@@ -74,6 +96,12 @@ typedef enum moe_status {
 } moe_status;
 
 typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Element format of the dispatched rows (moe_shape.dispatch). */
+typedef enum moe_dispatch_fmt {
+  MOE_DISPATCH_DTYPE = 0,  /* the layer dtype */
+  MOE_DISPATCH_MXFP8 = 1   /* MXFP8-E4M3 codes + E8M0 scales per 32 (bf16 layers, value-changing) */
+} moe_dispatch_fmt;
 
 /* Which call a workspace size is asked for. */
 typedef enum moe_call {
@@ -110,6 +138,8 @@ typedef struct moe_shape {
                       * routing weights are not renormalised).  Dropping changes the layer's
                       * output: WideEP explainer, "An imbalanced router creates a network
                       * hotspot".  C >= T can drop nothing and behaves as 0. */
+  int32_t dispatch;  /* moe_dispatch_fmt */
+  int32_t reserved;  /* 0 */
 } moe_shape;
 
 /* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
@@ -165,13 +195,17 @@ MOE_API moe_status moe_route_topk(const void* x, const float* gate_w, const floa
  * x_perm    [T*k x D] out: expert e's rows occupy [offsets[e], offsets[e+1]),
  *           holding, in ascending token order, a bitwise copy of every token
  *           that picked e (with a capacity C: the first C of them; rows from
- *           offsets[E] on are left untouched).
+ *           offsets[E] on are left untouched).  With MXFP8 dispatch: the E4M3 codes
+ *           of each token's row (quantised once per token, then copied).
+ * x_perm_scale [T*k x D/32] uint8 out: the rows' E8M0 scales (MXFP8 dispatch only;
+ *           must be NULL otherwise).
  * row_token [T*k] int32 out: source token of each row (the first offsets[E] entries).
  * token_row [T x k] int32 out: row holding token t's j-th assignment, -1 if dropped.
  */
 MOE_API moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
-                                void* x_perm, int32_t* row_token, int32_t* token_row,
-                                const moe_shape* s, void* ws, size_t ws_bytes, void* stream);
+                                void* x_perm, uint8_t* x_perm_scale, int32_t* row_token,
+                                int32_t* token_row, const moe_shape* s, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * Grouped SwiGLU expert FFN over ragged row counts (step a5).
@@ -189,10 +223,29 @@ MOE_API moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, 
  * y_perm [T*k x D] out (dtype): row r of expert e holds
  *        (SiLU(x w1[e]^T) * (x w3[e]^T)) w2[e]^T, with the intermediate rounded
  *        to dtype; unweighted (weights apply in the combine).
+ * MXFP8 dispatch: x_perm holds E4M3 codes with x_perm_scale [T*k x D/32], w1 / w3
+ *        hold codes with w1_scale / w3_scale [E x I x D/32] (as moe_quantize_mxfp8
+ *        writes them); x w1^T and x w3^T are products of the dequantised values with
+ *        fp32 accumulation.  The scale pointers must be NULL otherwise.
  */
-MOE_API moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
-                           const void* w3, const void* w2, void* y_perm, const moe_shape* s,
+MOE_API moe_status moe_grouped_ffn(const void* x_perm, const uint8_t* x_perm_scale, const int32_t* offsets,
+                           const void* w1, const uint8_t* w1_scale, const void* w3,
+                           const uint8_t* w3_scale, const void* w2, void* y_perm, const moe_shape* s,
                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MXFP8 conversion kernel (the conversion and scale metadata of a low-precision
+ * dispatch: "Top-k multiplies traffic. Locality subtracts it.", WideEP explainer).
+ *
+ * src   [rows x cols] bf16 (src_dtype MOE_BF16) or fp32 (MOE_F32) values, finite.
+ * q     [rows x cols] uint8 out: E4M3 codes.
+ * scale [rows x cols/32] uint8 out: E8M0 scales, one per 32 consecutive elements of
+ *       a row (the rule is in the MXFP8 section at the top of this file).
+ * Used for the expert weights W1 / W3 (once, offline) and inside the dispatch for the
+ * activations.  cols % 32 != 0 -> MOE_ERR_UNSUPPORTED; rows == 0 does nothing.
+ */
+MOE_API moe_status moe_quantize_mxfp8(const void* src, int src_dtype, int64_t rows, int64_t cols,
+                                      uint8_t* q, uint8_t* scale, void* stream);
 
 /*
  * Combine: unpermute and apply routing weights (step a6).
@@ -234,6 +287,8 @@ typedef struct moe_layer_weights {
   const void* ws1;         /* [shared_I x H] shared expert gate branch, when shared_I > 0 */
   const void* ws3;         /* [shared_I x H] shared expert up branch */
   const void* ws2;         /* [H x shared_I] shared expert down projection */
+  const uint8_t* w1_scale; /* [E x I x D/32] E8M0 scales of w1 (MXFP8 dispatch only, else NULL) */
+  const uint8_t* w3_scale; /* [E x I x D/32] E8M0 scales of w3 (MXFP8 dispatch only, else NULL) */
 } moe_layer_weights;
 
 /* Optional caller buffers that expose the intermediate results (each nullable;
@@ -249,6 +304,7 @@ typedef struct moe_layer_aux {
   void* y_perm;        /* [T*k x D] dtype */
   void* z;             /* [T x L] dtype, latent layers */
   void* out_latent;    /* [T x L] dtype, latent layers: combine output before up-projection */
+  uint8_t* x_perm_scale;  /* [T*k x D/32] E8M0 scales of x_perm (MXFP8 dispatch only) */
 } moe_layer_aux;
 
 /*
@@ -267,6 +323,11 @@ typedef struct moe_layer_aux {
  * non-expert weights, research-vault claim IX2-0406):
  * Ys = (SiLU(X ws1^T) * (X ws3^T)) ws2^T with the intermediate and Ys rounded to
  * dtype, added in the combine as its shared_out term.
+ *
+ * MXFP8 dispatch (s->dispatch): w->w1 / w->w3 are E4M3 codes with w1_scale /
+ * w3_scale; the dispatched rows are quantised in the dispatch (see the section at
+ * the top of this file); aux->x_perm then receives codes and aux->x_perm_scale
+ * their scales.
  *
  * x       [T x H] (dtype).
  * logits  [T x E] fp32: input when w->gate_w == NULL, else output (nullable: then

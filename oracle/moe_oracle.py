@@ -420,9 +420,9 @@ def layer_forward(inp: Dict[str, np.ndarray], *, k: int, E: int, bf16: bool, cap
         lap("permutation")
         res["w1_q"], res["w1_scale"] = mxfp8.mx_quantize(decode(inp["w1"]))
         res["w3_q"], res["w3_scale"] = mxfp8.mx_quantize(decode(inp["w3"]))
-        res["y_perm"] = mxfp8.grouped_expert_ffn_mx(res["x_perm_q"], res["x_perm_scale"], res["offsets"],
-                                                    res["w1_q"], res["w1_scale"], res["w3_q"],
-                                                    res["w3_scale"], inp["w2"])
+        res["y_perm"], res["ffn_parts"] = mxfp8.grouped_expert_ffn_mx(
+            res["x_perm_q"], res["x_perm_scale"], res["offsets"], res["w1_q"], res["w1_scale"], res["w3_q"],
+            res["w3_scale"], inp["w2"], parts=True)
     else:
         assert dispatch == "dtype"
         res["x_perm"] = gather_rows(src, rt)

@@ -110,31 +110,45 @@ def mx_dequantize(codes: np.ndarray, scales: np.ndarray, block: int = MX_BLOCK) 
 
 
 def expert_ffn_rows_mx(xq: np.ndarray, xs: np.ndarray, w1q: np.ndarray, w1s: np.ndarray,
-                       w3q: np.ndarray, w3s: np.ndarray, w2e: np.ndarray) -> np.ndarray:
+                       w3q: np.ndarray, w3s: np.ndarray, w2e: np.ndarray, parts: bool = False):
     """One expert's SwiGLU FFN with MXFP8 rows and gate/up weights.
 
     G = A W1^T and U = A W3^T on the dequantised operands, exact; then as the bf16
     layer: the intermediate SiLU(G) * U and the output (intermediate) W2^T are
     rounded to bf16.  w1q / w3q [I x D] with scales [I x D/32]; xq [rows x D] with
-    scales [rows x D/32]; w2e [D x I] bf16.
+    scales [rows x D/32]; w2e [D x I] bf16.  With parts=True also returns the
+    intermediates {"x", "w1", "w3", "g", "u", "a"} (dequantised operands, exact G and
+    U, rounded A).
     """
     x = mx_dequantize(xq, xs)
-    g = x @ mx_dequantize(w1q, w1s).T
-    u = x @ mx_dequantize(w3q, w3s).T
+    w1 = mx_dequantize(w1q, w1s)
+    w3 = mx_dequantize(w3q, w3s)
+    g = x @ w1.T
+    u = x @ w3.T
     a = round_bf16(silu(g) * u)
-    return round_bf16(a @ decode(w2e).T)
+    y = round_bf16(a @ decode(w2e).T)
+    if parts:
+        return y, {"x": x, "w1": w1, "w3": w3, "g": g, "u": u, "a": a}
+    return y
 
 
 def grouped_expert_ffn_mx(xq: np.ndarray, xs: np.ndarray, offsets: np.ndarray, w1q, w1s, w3q, w3s,
-                          w2: np.ndarray) -> np.ndarray:
-    """Expert e runs expert_ffn_rows_mx on rows [offsets[e], offsets[e+1])."""
+                          w2: np.ndarray, parts: bool = False):
+    """Expert e runs expert_ffn_rows_mx on rows [offsets[e], offsets[e+1]).  With
+    parts=True also returns, per expert with rows, (e, lo, hi, intermediates)."""
     E = len(offsets) - 1
     y = np.zeros((int(offsets[-1]), w2.shape[1]), dtype=np.float64)
+    pieces = []
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
-            y[lo:hi] = expert_ffn_rows_mx(xq[lo:hi], xs[lo:hi], w1q[e], w1s[e], w3q[e], w3s[e], w2[e])
-    return y
+            r = expert_ffn_rows_mx(xq[lo:hi], xs[lo:hi], w1q[e], w1s[e], w3q[e], w3s[e], w2[e], parts)
+            if parts:
+                y[lo:hi], pr = r
+                pieces.append((e, lo, hi, pr))
+            else:
+                y[lo:hi] = r
+    return (y, pieces) if parts else y
 
 
 def dispatch_bytes_mx(rows: int, width: int) -> int:

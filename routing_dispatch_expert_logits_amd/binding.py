@@ -18,8 +18,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_FFN, MOE_CALL_COMBINE, MOE_CALL_LAYER = range(5)
 MOE_COMBINE_FUSED, MOE_COMBINE_UNFUSED = 0, 1
+MOE_DISPATCH_DTYPE, MOE_DISPATCH_MXFP8 = 0, 1
 MOE_NUM_STAGE_EVENTS = 10
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STAGE_NAMES = ["latent_down", "gate", "route", "permute", "gemm_gate_up", "gemm_down",
                "shared_expert", "combine", "latent_up"]
@@ -37,18 +38,20 @@ class MoeError(RuntimeError):
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", _i64), ("H", _i64), ("E", _i64), ("k", _i64), ("I", _i64), ("L", _i64),
-                ("dtype", _i32), ("shared_I", _i32), ("capacity", _i64)]
+                ("dtype", _i32), ("shared_I", _i32), ("capacity", _i64), ("dispatch", _i32),
+                ("reserved", _i32)]
 
 
 class MoeLayerWeights(ctypes.Structure):
     _fields_ = [("gate_w", _vp), ("gate_bias", _vp), ("w1", _vp), ("w3", _vp), ("w2", _vp),
-                ("wd", _vp), ("wu", _vp), ("ws1", _vp), ("ws3", _vp), ("ws2", _vp)]
+                ("wd", _vp), ("wu", _vp), ("ws1", _vp), ("ws3", _vp), ("ws2", _vp),
+                ("w1_scale", _vp), ("w3_scale", _vp)]
 
 
 class MoeLayerAux(ctypes.Structure):
     _fields_ = [("topk_ids", _vp), ("topk_w", _vp), ("counts", _vp), ("offsets", _vp),
                 ("row_token", _vp), ("token_row", _vp), ("x_perm", _vp), ("y_perm", _vp),
-                ("z", _vp), ("out_latent", _vp)]
+                ("z", _vp), ("out_latent", _vp), ("x_perm_scale", _vp)]
 
 
 def _load() -> ctypes.CDLL:
@@ -68,14 +71,16 @@ def _load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.argtypes = [P(MoeShape), ctypes.c_int]
     sz = ctypes.c_size_t
     lib.moe_route_topk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
-    lib.moe_dispatch_permute.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
-    lib.moe_grouped_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
+    lib.moe_dispatch_permute.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
+    lib.moe_grouped_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz,
+                                    _vp]
+    lib.moe_quantize_mxfp8.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, _vp]
     lib.moe_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, P(MoeShape),
                                 _vp, sz, _vp]
     lib.moe_layer_forward.argtypes = [P(MoeLayerWeights), _vp, _vp, _vp, ctypes.c_int,
                                       P(MoeShape), P(MoeLayerAux), P(_vp), _vp, sz, _vp]
     for f in ("moe_route_topk", "moe_dispatch_permute", "moe_grouped_ffn", "moe_combine",
-              "moe_layer_forward"):
+              "moe_layer_forward", "moe_quantize_mxfp8"):
         getattr(lib, f).restype = ctypes.c_int
     v = lib.moe_abi_version()
     if v != ABI_VERSION:
@@ -91,8 +96,9 @@ def status_string(status: int) -> str:
 
 
 def shape(T: int, H: int, E: int, k: int, I: int, L: int = 0, dtype: str = "bf16",
-          shared_I: int = 0, capacity: int = 0) -> MoeShape:
-    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, shared_I, capacity)
+          shared_I: int = 0, capacity: int = 0, dispatch: str = "dtype") -> MoeShape:
+    fmt = {"dtype": MOE_DISPATCH_DTYPE, "mxfp8": MOE_DISPATCH_MXFP8}[dispatch]
+    return MoeShape(T, H, E, k, I, L, MOE_BF16 if dtype == "bf16" else MOE_F32, shared_I, capacity, fmt, 0)
 
 
 def workspace_bytes(s: MoeShape, call: int) -> int:
@@ -132,16 +138,27 @@ def route_topk(x, gate_w, gate_bias, logits, topk_ids, topk_w, counts, offsets, 
 
 
 def dispatch_permute(x, topk_ids, offsets, x_perm, row_token, token_row, s: MoeShape, ws,
-                     stream=None):
+                     stream=None, x_perm_scale=None):
     _check("moe_dispatch_permute", lib.moe_dispatch_permute(
-        _p(x), _p(topk_ids), _p(offsets), _p(x_perm), _p(row_token), _p(token_row),
+        _p(x), _p(topk_ids), _p(offsets), _p(x_perm), _p(x_perm_scale), _p(row_token), _p(token_row),
         ctypes.byref(s), _p(ws), _nbytes(ws), _stream(stream)))
 
 
-def grouped_ffn(x_perm, offsets, w1, w3, w2, y_perm, s: MoeShape, ws, stream=None):
+def grouped_ffn(x_perm, offsets, w1, w3, w2, y_perm, s: MoeShape, ws, stream=None, x_perm_scale=None,
+                w1_scale=None, w3_scale=None):
     _check("moe_grouped_ffn", lib.moe_grouped_ffn(
-        _p(x_perm), _p(offsets), _p(w1), _p(w3), _p(w2), _p(y_perm), ctypes.byref(s), _p(ws),
-        _nbytes(ws), _stream(stream)))
+        _p(x_perm), _p(x_perm_scale), _p(offsets), _p(w1), _p(w1_scale), _p(w3), _p(w3_scale), _p(w2),
+        _p(y_perm), ctypes.byref(s), _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def quantize_mxfp8(src, q, scale, stream=None):
+    """MXFP8 codes and scales of a [rows x cols] bf16 (int16 bit tensor) or fp32 tensor."""
+    import torch
+    src_dtype = MOE_F32 if src.dtype == torch.float32 else MOE_BF16
+    cols = src.shape[-1]
+    rows = src.numel() // cols if cols else 0
+    _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(
+        _p(src), src_dtype, rows, cols, _p(q), _p(scale), _stream(stream)))
 
 
 def combine(y_perm, token_row, topk_w, out, out_dtype: int, flags: int, s: MoeShape, ws,
@@ -153,7 +170,7 @@ def combine(y_perm, token_row, topk_w, out, out_dtype: int, flags: int, s: MoeSh
 
 def layer_forward(weights: dict, x, logits, out, out_dtype: int, s: MoeShape, ws, aux: dict = None,
                   stage_events=None, stream=None):
-    """weights: gate_w, gate_bias, w1, w3, w2, wd, wu, ws1, ws3, ws2 (tensors or None);
+    """weights: gate_w, gate_bias, w1, w3, w2, wd, wu, ws1, ws3, ws2, w1_scale, w3_scale (tensors or None);
     aux: moe_layer_aux fields."""
     w = MoeLayerWeights(*[_p(weights.get(f)) for f, _ in MoeLayerWeights._fields_])
     a = MoeLayerAux(*[_p((aux or {}).get(f)) for f, _ in MoeLayerAux._fields_])

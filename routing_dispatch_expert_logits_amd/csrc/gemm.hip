@@ -247,13 +247,24 @@ typedef __attribute__((address_space(3))) void* las_ptr;
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 static_assert(waitcnt_vm(24) == 0x4F78 && waitcnt_vm(0) == 0x0F70, "s_waitcnt encoding");
 
-template <int BM, int BN, int NB, int EPI, int S, int MW = 4, int BK = 64, int G = 1>
+//
+// F8 = true: MXFP8 operands (E4M3 codes, one E8M0 scale per 32 elements along K,
+// mx.a / mx.b0 / mx.b1 the [rows x K/32] scale arrays).  The code matrices are
+// passed as 16-bit pairs with K = D / 2, so a K-step is still 128 bytes per row
+// and the loaders and LDS layout are those of the bf16 kernel.  The loader waves
+// also copy each stage's scales (4 bytes per row: the step's four blocks) into a
+// region after the B tiles with 4-byte LDS DMA.  The MFMA waves feed one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per fragment and K-step: lane l (g = l / 16)
+// supplies the 16-byte chunks g and 4 + g of its row's K-step (K elements
+// 16g..16g+15 and 64+16g..64+16g+15) and the E8M0 scale of block g of that step.
+template <int BM, int BN, int NB, int EPI, int S, int MW = 4, int BK = 64, int G = 1, bool F8 = false>
 __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ mtile_start, int E, int N, int K) {
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, MxScales mx) {
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile 128/256 x 128/256");
   static_assert(BK == 32 || BK == 64, "K-step 32 or 64");
+  static_assert(!F8 || BK == 64, "MXFP8 K-steps are 128 codes");
   constexpr int WM = BM / 64;                     // MFMA waves along M (64 rows each)
   constexpr int WN = MW / WM;                     // MFMA waves along N
   static_assert(WM * WN == MW && WN >= 1, "wave grid");
@@ -261,11 +272,16 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
   constexpr int CH = BK / 8;                      // 16-byte chunks per LDS row
   constexpr int RPQ = 64 / CH;                    // rows per DMA instruction
   constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
-  constexpr int STAGE = A_ELEMS + NB * B_ELEMS;   // bf16 elements per stage
+  constexpr int SC_BYTES = F8 ? (BM + NB * BN) * 4 : 0;        // MXFP8 scales per stage
+  constexpr int STAGE = A_ELEMS + NB * B_ELEMS + SC_BYTES / 2;  // 16-bit elements per stage
   constexpr int QA = BM / RPQ, QB = BN / RPQ;     // DMA instructions per A / B tile
   constexpr int NQ = QA + NB * QB;                // DMA instructions per stage
   constexpr int NQP = NQ / 2;                     // per loader wave
-  static_assert(S >= 2 && S <= 6 && (S - 2) * NQP <= 63, "outstanding loads fit vmcnt");
+  constexpr int SQA = F8 ? BM / 64 : 0, SQB = F8 ? BN / 64 : 0;  // 4-byte scale DMAs (64 rows each)
+  constexpr int NSP = (SQA + NB * SQB) / 2;       // scale DMAs per loader wave
+  static_assert((SQA + NB * SQB) % 2 == 0, "scale DMAs split over two loader waves");
+  constexpr int NQW = NQP + NSP;                  // vector-memory ops per stage per loader wave
+  static_assert(S >= 2 && S <= 6 && (S - 2) * NQW <= 63, "outstanding loads fit vmcnt");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
 
   TileCoord tc;
@@ -295,20 +311,48 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
         ldsoff[j] = A_ELEMS + nb * B_ELEMS + qq * 512;
       }
     }
+    // MXFP8 scales: lane i of DMA j copies the step's 4 scale bytes of row i of its
+    // 64-row group (scale rows are K / 16 bytes: K counts 16-bit pairs)
+    const uint8_t* ssrc[NSP > 0 ? NSP : 1];
+    int sldsoff[NSP > 0 ? NSP : 1];
+    if constexpr (F8) {
+      const int srow = K / 16;
+#pragma unroll
+      for (int j = 0; j < NSP; ++j) {
+        const int q = p * NSP + j;
+        if (q < SQA) {
+          const int r = q * 64 + lane;
+          ssrc[j] = mx.a + (size_t)(tc.row0 + min(r, tc.rows - 1)) * srow;
+          sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + q * 256;
+        } else {
+          const int nb = (q - SQA) / SQB, qq = (q - SQA) % SQB;
+          const int r = qq * 64 + lane;
+          ssrc[j] = (nb == 0 ? mx.b0 : mx.b1) + ((size_t)tc.e * N + min(tc.n0 + r, N - 1)) * srow;
+          sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + BM * 4 + nb * BN * 4 + qq * 256;
+        }
+      }
+    }
     auto issue = [&](int st) {
       const int base = (st % S) * STAGE;
 #pragma unroll
       for (int j = 0; j < NQP; ++j)
         __builtin_amdgcn_global_load_lds((gas_ptr)(src[j] + st * BK), (las_ptr)&lds[base + ldsoff[j]],
                                          16, 0, 0);
+      if constexpr (F8) {
+#pragma unroll
+        for (int j = 0; j < NSP; ++j)
+          __builtin_amdgcn_global_load_lds((gas_ptr)(ssrc[j] + st * 4),
+                                           (las_ptr)(reinterpret_cast<uint8_t*>(lds) + base * 2 + sldsoff[j]),
+                                           4, 0, 0);
+      }
     };
     // Up to S-1 stages in flight.  wait_behind(n): the oldest outstanding stage has
-    // landed once at most n later stages (n * NQP loads) are still in flight.
+    // landed once at most n later stages (n * NQW loads) are still in flight.
     auto wait_behind = [](int n) {
-      if (n >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NQP < 63 ? 4 * NQP : 63));
-      else if (n == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * NQP < 63 ? 3 * NQP : 63));
-      else if (n == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NQP < 63 ? 2 * NQP : 63));
-      else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQP));
+      if (n >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * NQW < 63 ? 4 * NQW : 63));
+      else if (n == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * NQW < 63 ? 3 * NQW : 63));
+      else if (n == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NQW < 63 ? 2 * NQW : 63));
+      else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQW));
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
     const int pre = min(S - 1, nsteps);               // stages issued before the loop
@@ -401,7 +445,55 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
   constexpr int kWavesPerSimd = (MW + 2 + 3) / 4;
   constexpr int kVgprBudget = (512 / kWavesPerSimd) & ~7;
   constexpr bool kDoubleBuffer = NM * 4 + 2 * NR * 4 + 40 <= kVgprBudget;
-  if constexpr (!kDoubleBuffer) {
+  if constexpr (F8) {
+    // per K-step: both chunks of every fragment, the fragments' block scales, one
+    // scaled MFMA per fragment pair
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    constexpr int SCB = (A_ELEMS + NB * B_ELEMS) * 2;  // scale region, bytes into the stage
+    const int g = lane >> 4;
+    int sa_off[FM], sb_off[NB][FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sa_off[fm] = SCB + (wm * TM + fm * 16 + (lane & 15)) * 4 + g;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        sb_off[nb][fn] = SCB + BM * 4 + nb * BN * 4 + (wn * TN + fn * 16 + (lane & 15)) * 4 + g;
+    __syncthreads();  // stage 0 has landed
+    for (int s = 0; s < nsteps; ++s) {
+      const uint16_t* base = lds + (s % S) * STAGE;
+      const uint8_t* base8 = reinterpret_cast<const uint8_t*>(base);
+      u32x4 a0[FM], a1[FM], b0[NB][FN], b1[NB][FN];
+      int sa[FM], sb[NB][FN];
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        a0[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[0][fm]);
+        a1[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[1][fm]);
+        sa[fm] = base8[sa_off[fm]];
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          b0[nb][fn] = *reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[0][fn]);
+          b1[nb][fn] = *reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[1][fn]);
+          sb[nb][fn] = base8[sb_off[nb][fn]];
+        }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[nb][fn], b1[nb][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) {
+            const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[fm], a1[fm], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[nb][fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[nb][fm][fn], 0, 0, 0,
+                                                                               sa[fm], 0, sb[nb][fn]);
+          }
+        }
+      __syncthreads();  // every MFMA wave has read stage s; stage s+1 has landed
+    }
+  } else if constexpr (!kDoubleBuffer) {
     __syncthreads();  // stage 0 has landed
     for (int s = 0; s < nsteps; ++s) {
       const uint16_t* base = lds + (s % S) * STAGE;
@@ -453,67 +545,111 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
       }
 }
 
-// ------------------------------------------------------------------ bf16 decode kernel
+// ------------------------------------------------------------------ decode kernel
 // For experts with a handful of rows: 16-row m-tiles, no LDS, every wave
 // streams its own 16*FN weight rows straight from HBM with two K-steps of loads
-// in flight.  Within a 64-wide K-step lane l carries k = 16*(l/16) .. +16 of
+// in flight.  bf16: within a 64-wide K-step lane l carries k = 16*(l/16) .. +16 of
 // both operands (two 8-element MFMA halves); the same permutation of k on A and
 // B leaves the sum unchanged and makes each weight row's 128 bytes one
-// contiguous read by 4 lanes.
+// contiguous read by 4 lanes.  F8 (MXFP8 codes passed as 16-bit pairs, K = D / 2):
+// a K-step is 128 codes, and lane l carries chunks g and 4 + g (g = l / 16) of it,
+// the layout of v_mfma_scale_f32_16x16x128_f8f6f4, plus the E8M0 scales of block g
+// of its A row and of each of its B rows.
 
 template <int NB, int FN>
 struct DecodeRegs {
   uint4 a[2];
   uint4 b[NB][FN][2];
+  int sa;
+  int sb[NB][FN];
 };
 
-template <int NB, int FN>
+template <int NB, int FN, bool F8>
 __device__ __forceinline__ void decode_load(DecodeRegs<NB, FN>& r, const uint16_t* pa,
-                                            const uint16_t* const (&pb)[NB][FN], int k0) {
+                                            const uint16_t* const (&pb)[NB][FN], int k0,
+                                            const uint8_t* psa, const uint8_t* const (&psb)[NB][FN]) {
+  constexpr int second = F8 ? 32 : 8;  // 16-bit offset of the lane's second chunk
   r.a[0] = *reinterpret_cast<const uint4*>(pa + k0);
-  r.a[1] = *reinterpret_cast<const uint4*>(pa + k0 + 8);
+  r.a[1] = *reinterpret_cast<const uint4*>(pa + k0 + second);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       r.b[nb][fn][0] = *reinterpret_cast<const uint4*>(pb[nb][fn] + k0);
-      r.b[nb][fn][1] = *reinterpret_cast<const uint4*>(pb[nb][fn] + k0 + 8);
+      r.b[nb][fn][1] = *reinterpret_cast<const uint4*>(pb[nb][fn] + k0 + second);
     }
-}
-
-template <int NB, int FN>
-__device__ __forceinline__ void decode_mma(f32x4 (&acc)[NB][FN], const DecodeRegs<NB, FN>& r) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bf16x8 a = as_bf16x8(r.a[h]);
+  if constexpr (F8) {
+    const int s4 = k0 / 16;  // 4 scale bytes per 64-pair K-step
+    r.sa = psa[s4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[nb][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(r.b[nb][fn][h]),
-                                                               acc[nb][fn], 0, 0, 0);
+      for (int fn = 0; fn < FN; ++fn) r.sb[nb][fn] = psb[nb][fn][s4];
   }
 }
 
-template <int NB, int FN, int EPI>
+template <int NB, int FN, bool F8>
+__device__ __forceinline__ void decode_mma(f32x4 (&acc)[NB][FN], const DecodeRegs<NB, FN>& r) {
+  if constexpr (F8) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(
+        __builtin_bit_cast(u32x4, r.a[0]), __builtin_bit_cast(u32x4, r.a[1]), 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const i32x8 b = __builtin_bit_cast(i32x8, __builtin_shufflevector(
+            __builtin_bit_cast(u32x4, r.b[nb][fn][0]), __builtin_bit_cast(u32x4, r.b[nb][fn][1]), 0, 1, 2, 3,
+            4, 5, 6, 7));
+        acc[nb][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[nb][fn], 0, 0, 0, r.sa, 0,
+                                                                       r.sb[nb][fn]);
+      }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const bf16x8 a = as_bf16x8(r.a[h]);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[nb][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(r.b[nb][fn][h]),
+                                                                 acc[nb][fn], 0, 0, 0);
+    }
+  }
+}
+
+template <int NB, int FN, int EPI, bool F8 = false>
 __global__ __launch_bounds__(256) void k_gemm_decode(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ mtile_start, int E, int N, int K, const int32_t* __restrict__ gather) {
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, const int32_t* __restrict__ gather,
+    MxScales mx) {
   constexpr int BM = 16, BN = 4 * 16 * FN;
   TileCoord tc;
   if (!decode_tile<BM, BN>(offsets, mtile_start, E, M, N, tc)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kl = (lane >> 4) * 16;
+  const int g = lane >> 4;
+  const int kl = F8 ? g * 8 : g * 16;
   // gather non-NULL: operand row r is A[gather[r]] (token rows read in permuted order)
   const int ar = tc.row0 + min(lane & 15, tc.rows - 1);
-  const uint16_t* pa = A + (size_t)(gather ? gather[ar] : ar) * K + kl;
+  const int arow = gather ? gather[ar] : ar;
+  const uint16_t* pa = A + (size_t)arow * K + kl;
   const uint16_t* pb[NB][FN];
+  const uint8_t* psa = nullptr;
+  const uint8_t* psb[NB][FN];
+  const int srow = K / 16;  // MXFP8 scale bytes per row
+  if constexpr (F8) psa = mx.a + (size_t)arow * srow + g;
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int gn = min(tc.n0 + wave * 16 * FN + fn * 16 + (lane & 15), N - 1);
     pb[0][fn] = B0 + ((size_t)tc.e * N + gn) * K + kl;
     if constexpr (NB > 1) pb[NB - 1][fn] = B1 + ((size_t)tc.e * N + gn) * K + kl;
+    psb[0][fn] = nullptr;
+    if constexpr (NB > 1) psb[NB - 1][fn] = nullptr;
+    if constexpr (F8) {
+      psb[0][fn] = mx.b0 + ((size_t)tc.e * N + gn) * srow + g;
+      if constexpr (NB > 1) psb[NB - 1][fn] = mx.b1 + ((size_t)tc.e * N + gn) * srow + g;
+    }
   }
   f32x4 acc[NB][FN];
 #pragma unroll
@@ -523,14 +659,14 @@ __global__ __launch_bounds__(256) void k_gemm_decode(
 
   DecodeRegs<NB, FN> r0, r1;
   const int steps = K / 64;
-  decode_load<NB, FN>(r0, pa, pb, 0);
-  if (steps > 1) decode_load<NB, FN>(r1, pa, pb, 64);
+  decode_load<NB, FN, F8>(r0, pa, pb, 0, psa, psb);
+  if (steps > 1) decode_load<NB, FN, F8>(r1, pa, pb, 64, psa, psb);
   for (int s = 0; s < steps; s += 2) {
-    decode_mma<NB, FN>(acc, r0);
-    if (s + 2 < steps) decode_load<NB, FN>(r0, pa, pb, (s + 2) * 64);
+    decode_mma<NB, FN, F8>(acc, r0);
+    if (s + 2 < steps) decode_load<NB, FN, F8>(r0, pa, pb, (s + 2) * 64, psa, psb);
     if (s + 1 < steps) {
-      decode_mma<NB, FN>(acc, r1);
-      if (s + 3 < steps) decode_load<NB, FN>(r1, pa, pb, (s + 3) * 64);
+      decode_mma<NB, FN, F8>(acc, r1);
+      if (s + 3 < steps) decode_load<NB, FN, F8>(r1, pa, pb, (s + 3) * 64, psa, psb);
     }
   }
 #pragma unroll
@@ -649,7 +785,7 @@ int max_mtiles(int M, int E, int bm) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K)
 #define MOE_LAUNCH_DEC(kern, grid)                                                                   \
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K, \
-                     static_cast<const int32_t*>(nullptr))
+                     static_cast<const int32_t*>(nullptr), MxScales{})
 
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
@@ -668,10 +804,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       const dim3 g(grid_for(ceil_div(M, 256), N, 128)), b(8 * 64 + 128);
       if (epi == EPI_BF16)
         hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
-                           offsets, mtile_start, E, N, K);
+                           offsets, mtile_start, E, N, K, MxScales{});
       else if (epi == EPI_F32)
         hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
-                           offsets, mtile_start, E, N, K);
+                           offsets, mtile_start, E, N, K, MxScales{});
       else
         return hipErrorInvalidValue;
       return hipGetLastError();
@@ -686,17 +822,17 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       if (epi == EPI_SWIGLU_BF16) {
         if (pairs)
           hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
-                             B0, B1, C, offsets, mtile_start, E, N, K);
+                             B0, B1, C, offsets, mtile_start, E, N, K, MxScales{});
         else
           hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), gb, bb, 0, st, A, M, B0,
-                             B1, C, offsets, mtile_start, E, N, K);
+                             B1, C, offsets, mtile_start, E, N, K, MxScales{});
       } else {
         if (pairs)
           hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
-                             B0, B1, C, offsets, mtile_start, E, N, K);
+                             B0, B1, C, offsets, mtile_start, E, N, K, MxScales{});
         else
           hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), gb, bb, 0, st, A, M, B0,
-                             B1, C, offsets, mtile_start, E, N, K);
+                             B1, C, offsets, mtile_start, E, N, K, MxScales{});
       }
       return hipGetLastError();
     }
@@ -705,10 +841,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       const int32_t* mt256 = mtile_start + E + 1;
       if (epi == EPI_BF16)
         hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
-                           offsets, mt256, E, N, K);
+                           offsets, mt256, E, N, K, MxScales{});
       else if (epi == EPI_F32)
         hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
-                           offsets, mt256, E, N, K);
+                           offsets, mt256, E, N, K, MxScales{});
       else
         return hipErrorInvalidValue;
       return hipGetLastError();
@@ -764,9 +900,34 @@ hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* 
   const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
   if (epi == EPI_SWIGLU_BF16)
     hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), dim3(g), dim3(256), 0, st, X, M, B0, B1, C,
-                       offsets, mtile_start, E, N, K, gather);
+                       offsets, mtile_start, E, N, K, gather, MxScales{});
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const uint8_t* B0, const uint8_t* B1,
+                                 uint16_t* C, const int32_t* offsets, const int32_t* mtile_start, int E,
+                                 int N, int D, MxScales mx, const int32_t* gather, hipStream_t st) {
+  if (D % 128) return hipErrorInvalidValue;
+  const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
+  const uint16_t* b0 = reinterpret_cast<const uint16_t*>(B0);
+  const uint16_t* b1 = reinterpret_cast<const uint16_t*>(B1);
+  const int K = D / 2;  // codes travel as 16-bit pairs
+  if (kind == GEMM_PREFILL) {
+    if (gather) return hipErrorInvalidValue;
+    const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128)), bb(8 * 64 + 128);
+    if (ceil_div(N, 128) >= 16)
+      hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2, true>), gb, bb, 0, st, a, M,
+                         b0, b1, C, offsets, mtile_start, E, N, K, mx);
+    else
+      hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 1, true>), gb, bb, 0, st, a, M,
+                         b0, b1, C, offsets, mtile_start, E, N, K, mx);
+  } else {
+    const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
+    hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16, true>), dim3(g), dim3(256), 0, st, a, M, b0, b1,
+                       C, offsets, mtile_start, E, N, K, gather, mx);
+  }
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ struct Dims {
   int Is;   // shared expert intermediate width, 0 = none
   int cap;  // rows kept per expert, 0 = no limit
   bool bf16;
+  bool mx;  // MXFP8 dispatch: x_perm holds E4M3 codes + E8M0 scales, W1 / W3 likewise
 };
 
 moe_status check_shape(const moe_shape* s, Dims& d) {
@@ -41,6 +42,7 @@ moe_status check_shape(const moe_shape* s, Dims& d) {
       s->capacity < 0)
     return MOE_ERR_INVALID_ARG;
   if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->dispatch != MOE_DISPATCH_DTYPE && s->dispatch != MOE_DISPATCH_MXFP8) return MOE_ERR_INVALID_ARG;
   if (s->k > s->E) return MOE_ERR_INVALID_ARG;
   if (s->E > kMaxE || s->k > kWave) return MOE_ERR_UNSUPPORTED;
   if (s->T > INT_MAX || s->H > INT_MAX || s->I > INT_MAX || s->L > INT_MAX) return MOE_ERR_UNSUPPORTED;
@@ -53,7 +55,9 @@ moe_status check_shape(const moe_shape* s, Dims& d) {
   d.cap = s->capacity >= s->T ? 0 : (int)s->capacity;
   d.bf16 = s->dtype == MOE_BF16;
   d.es = d.bf16 ? 2 : 4;
+  d.mx = s->dispatch == MOE_DISPATCH_MXFP8;
   if (d.Is && d.L) return MOE_ERR_UNSUPPORTED;  // shared expert on non-latent layers only
+  if (d.mx && (!d.bf16 || d.D % 128)) return MOE_ERR_UNSUPPORTED;  // bf16 layers, 128-code K-steps
   if (d.bf16) {
     if (d.D % 64 || d.I % 64 || (d.L && d.H % 64) || d.Is % 64) return MOE_ERR_UNSUPPORTED;
   } else {
@@ -101,7 +105,7 @@ CombWs comb_ws(const Dims& d) {
 
 struct LayerWs {
   size_t logits, ids, w, counts, offsets, row_token, token_row, bc, gpart, mtile, z, xperm, act, outl,
-      soffs, smtile, sact, sy, total;
+      soffs, smtile, sact, sy, xs, xq, xqs, total;
 };
 LayerWs layer_ws(const Dims& d) {
   Carve c; LayerWs w;
@@ -117,6 +121,10 @@ LayerWs layer_ws(const Dims& d) {
   w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
   w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
+  w.xs = c.take(d.mx ? (size_t)d.R * (d.D / kMxBlock) : 0);  // MXFP8 scales of x_perm
+  // MXFP8 decode-scale steps: the token rows quantised once, read through row_token
+  w.xq = c.take(d.mx ? (size_t)d.T * d.D : 0);
+  w.xqs = c.take(d.mx ? (size_t)d.T * (d.D / kMxBlock) : 0);
   w.act = c.take((size_t)d.R * d.I * d.es);
   w.outl = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   // shared expert: one group of T rows
@@ -131,6 +139,7 @@ LayerWs layer_ws(const Dims& d) {
 // The shared expert's FFN as a grouped FFN of one expert over all T rows.
 Dims shared_dims(const Dims& d) {
   Dims s = d;
+  s.mx = false;  // the shared expert's rows are not dispatched
   s.E = 1;
   s.k = 1;
   s.R = d.T;
@@ -169,9 +178,17 @@ moe_status gate_scores(const Dims& d, const void* x, const float* gate_w, const 
 
 moe_status expert_ffn(const Dims& d, const void* x_perm, const int32_t* offsets,
                       const int32_t* mtile, const void* w1, const void* w3, const void* w2,
-                      void* act, void* y_perm, hipStream_t st) {
+                      void* act, void* y_perm, hipStream_t st, MxScales mx = MxScales{}) {
   const GemmKind kind = expert_kind(d);
-  if (kind == GEMM_SIMT) {
+  if (d.mx) {
+    MOE_HIP(launch_gemm_mx_swiglu(kind, static_cast<const uint8_t*>(x_perm), d.R,
+                                  static_cast<const uint8_t*>(w1), static_cast<const uint8_t*>(w3),
+                                  static_cast<uint16_t*>(act), offsets, mtile, d.E, d.I, d.D, mx, nullptr,
+                                  st));
+    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                             static_cast<const uint16_t*>(w2), nullptr, y_perm, offsets, mtile,
+                             d.E, d.D, d.I, st));
+  } else if (kind == GEMM_SIMT) {
     MOE_HIP(launch_gemm_simt(false, EPI_SWIGLU_F32, x_perm, d.R, static_cast<const float*>(w1),
                              static_cast<const float*>(w3), act, offsets, mtile, d.E, d.I, d.D,
                              nullptr, st));
@@ -259,13 +276,13 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
 }
 
 moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const int32_t* offsets,
-                                void* x_perm, int32_t* row_token, int32_t* token_row,
+                                void* x_perm, uint8_t* x_perm_scale, int32_t* row_token, int32_t* token_row,
                                 const moe_shape* s, void* ws, size_t ws_bytes, void* stream) {
   Dims d;
   moe_status rc = check_shape(s, d);
   if (rc != MOE_OK) return rc;
   if (!al16(x) || !al16(topk_ids) || !al16(offsets) || !al16(x_perm) || !al16(row_token) ||
-      !al16(token_row))
+      !al16(token_row) || (d.mx ? !al16(x_perm_scale) : x_perm_scale != nullptr))
     return MOE_ERR_INVALID_ARG;
   const RouteWs w = route_ws(d, false);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
@@ -274,24 +291,41 @@ moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, const in
   MOE_HIP(launch_block_counts(topk_ids, d.T, d.E, d.k, bc, st));
   MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, nullptr, st));
   MOE_HIP(launch_permute(x, d.D * d.es / 16, topk_ids, d.T, d.E, d.k, d.cap, offsets, bc, x_perm,
-                         row_token, token_row, st));
+                         d.mx ? x_perm_scale : nullptr, row_token, token_row, st));
   return MOE_OK;
 }
 
-moe_status moe_grouped_ffn(const void* x_perm, const int32_t* offsets, const void* w1,
-                           const void* w3, const void* w2, void* y_perm, const moe_shape* s,
-                           void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_grouped_ffn(const void* x_perm, const uint8_t* x_perm_scale, const int32_t* offsets,
+                           const void* w1, const uint8_t* w1_scale, const void* w3, const uint8_t* w3_scale,
+                           const void* w2, void* y_perm, const moe_shape* s, void* ws, size_t ws_bytes,
+                           void* stream) {
   Dims d;
   moe_status rc = check_shape(s, d);
   if (rc != MOE_OK) return rc;
   if (!al16(x_perm) || !al16(offsets) || !al16(w1) || !al16(w3) || !al16(w2) || !al16(y_perm))
+    return MOE_ERR_INVALID_ARG;
+  if (d.mx ? (!al16(x_perm_scale) || !al16(w1_scale) || !al16(w3_scale))
+           : (x_perm_scale || w1_scale || w3_scale))
     return MOE_ERR_INVALID_ARG;
   const FfnWs w = ffn_ws(d);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* mtile = at<int32_t>(ws, w.mtile);
   MOE_HIP(launch_offsets(nullptr, offsets, d.E, nullptr, gemm_bm(expert_kind(d)), mtile, st));
-  return expert_ffn(d, x_perm, offsets, mtile, w1, w3, w2, at<void>(ws, w.act), y_perm, st);
+  return expert_ffn(d, x_perm, offsets, mtile, w1, w3, w2, at<void>(ws, w.act), y_perm, st,
+                    MxScales{x_perm_scale, w1_scale, w3_scale});
+}
+
+moe_status moe_quantize_mxfp8(const void* src, int src_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                              uint8_t* scale, void* stream) {
+  if (rows < 0 || cols < 1 || (src_dtype != MOE_F32 && src_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  if (cols % kMxBlock) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!al16(src) || !al16(q) || !al16(scale)) return MOE_ERR_INVALID_ARG;
+  if (rows > (int64_t)1 << 40 || cols > INT_MAX) return MOE_ERR_UNSUPPORTED;
+  MOE_HIP(launch_mx_quantize(src, src_dtype == MOE_BF16, (long)rows, (long)cols, q, scale,
+                             static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 moe_status moe_combine(const void* y_perm, const int32_t* token_row, const float* topk_w,
@@ -334,12 +368,15 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   if (!wt->gate_w && !logits) return MOE_ERR_INVALID_ARG;  // given logits are required
   if (d.L && (!al16(wt->wd) || !al16(wt->wu))) return MOE_ERR_INVALID_ARG;
   if (d.Is && (!al16(wt->ws1) || !al16(wt->ws3) || !al16(wt->ws2))) return MOE_ERR_INVALID_ARG;
+  if (d.mx ? (!al16(wt->w1_scale) || !al16(wt->w3_scale)) : (wt->w1_scale || wt->w3_scale))
+    return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (!d.bf16 && d.L && out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   moe_layer_aux none = {};
   moe_layer_aux& ax = aux ? *aux : none;
+  if (!d.mx && ax.x_perm_scale) return MOE_ERR_INVALID_ARG;
   const void* auxp[] = {ax.topk_ids, ax.topk_w, ax.counts, ax.offsets, ax.row_token,
-                        ax.token_row, ax.x_perm, ax.y_perm, ax.z, ax.out_latent};
+                        ax.token_row, ax.x_perm, ax.y_perm, ax.z, ax.out_latent, ax.x_perm_scale};
   for (const void* p : auxp)
     if (!al16_or_null(p)) return MOE_ERR_INVALID_ARG;
   const LayerWs w = layer_ws(d);
@@ -362,6 +399,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   void* yperm = ax.y_perm ? ax.y_perm : at<void>(ws, w.xperm);
   void* act = at<void>(ws, w.act);
   void* outl = d.L ? pick(ax.out_latent, w.outl) : nullptr;
+  uint8_t* xs = d.mx ? static_cast<uint8_t*>(pick(ax.x_perm_scale, w.xs)) : nullptr;
 
   auto ev = [&](int i) -> bool {
     return !stage_events || hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
@@ -384,14 +422,21 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   // Decode-scale steps (16-row expert tiles, T <= kSmallT): routing, counts, offsets,
   // tile tables and row metadata in one launch, and the gate/up GEMM reads its rows
   // straight from the token rows through row_token (no permuted copy unless the
-  // caller asks for it in aux.x_perm).
-  const bool small = kind == GEMM_DECODE && d.T <= kSmallT;
+  // caller asks for it in aux.x_perm).  With MXFP8 dispatch the token rows are
+  // quantised once and read the same way; a caller who asks for the permuted codes
+  // gets the general path.
+  const bool small = kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (ax.x_perm || ax.x_perm_scale));
+  uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
+  uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;
   if (small) {
     MOE_HIP(launch_route_small(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, counts,
                                offs, rtok, trow, d.cap, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
-    // rows [0, offsets[E]) are the kept ones
-    if (ax.x_perm) MOE_HIP(launch_unpermute(src, row16, rtok, d.R, offs + d.E, ax.x_perm, st));
+    if (d.mx) {
+      MOE_HIP(launch_mx_quantize(src, true, d.T, d.D, xq, xqs, st));
+    } else if (ax.x_perm) {  // rows [0, offsets[E]) are the kept ones
+      MOE_HIP(launch_unpermute(src, row16, rtok, d.R, offs + d.E, ax.x_perm, st));
+    }
   } else {
     // a2 + a3
     MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
@@ -399,11 +444,21 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
     // a4
-    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, rtok, trow, st));
+    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, xs, rtok, trow, st));
   }
   if (!ev(4)) return MOE_ERR_HIP;
   // a5
-  if (small) {
+  if (d.mx) {
+    const MxScales mx{small ? xqs : xs, wt->w1_scale, wt->w3_scale};
+    MOE_HIP(launch_gemm_mx_swiglu(kind, static_cast<const uint8_t*>(small ? xq : xperm), d.R,
+                                  static_cast<const uint8_t*>(wt->w1), static_cast<const uint8_t*>(wt->w3),
+                                  static_cast<uint16_t*>(act), offs, mtile, d.E, d.I, d.D, mx,
+                                  small ? rtok : nullptr, st));
+    if (!ev(5)) return MOE_ERR_HIP;
+    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
+                             d.E, d.D, d.I, st));
+  } else if (small) {
     MOE_HIP(launch_gemm_decode_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
                                       static_cast<const uint16_t*>(wt->w1),
                                       static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,

@@ -33,6 +33,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// 8 bf16 values of one 16-byte chunk, widened exactly to fp32.
+__device__ __forceinline__ void unpack_bf16x8(uint4 v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -103,6 +113,51 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---- MXFP8 (OCP MX: E4M3 elements, one E8M0 scale per 32 elements along K)
+
+constexpr int kMxBlock = 32;
+
+// E8M0 scale code of a block whose largest magnitude is amax (finite, >= 0):
+// 127 + floor(log2 amax) - 8, clamped at 0 (fp32 zeros and subnormals land there).
+__device__ __forceinline__ int mx_scale_code(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xffu);  // biased exponent
+  return e == 0 ? 0 : max(e - 8, 0);
+}
+
+// 2^-(code - 127) as an fp32 multiplier (code 0..246 gives a normal number).
+__device__ __forceinline__ float mx_inv_scale(int code) {
+  return __uint_as_float(static_cast<uint32_t>(254 - code) << 23);
+}
+
+// Four E4M3 codes (bytes 0..3 = a, b, c, d) of values already divided by the block
+// scale: clamped to +-448 first (the conversion rounds to nearest even but turns
+// magnitudes from 464 on into NaN), then converted by the hardware.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, 0, false)) & 0xffffu;
+  return lo | (hi << 16);
+}
+
+// MX-quantise 8 consecutive values of a 32-element block held by 4 adjacent lanes
+// (lanes 4j .. 4j+3 hold the block's elements 0-7, 8-15, 16-23, 24-31).  Every lane
+// of the group must be active.  Returns the 8 codes; *code = the block's E8M0 scale.
+__device__ __forceinline__ uint2 mx_quantize8(const float* f, int* code) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, kWave));
+  m = fmaxf(m, __shfl_xor(m, 2, kWave));
+  const int c = mx_scale_code(m);
+  const float inv = mx_inv_scale(c);
+  *code = c;
+  return make_uint2(e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                    e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
+}
 
 // Largest e in [0, E] with starts[e] <= q (starts non-decreasing, starts[0] = 0).
 __device__ __forceinline__ int upper_index(const int32_t* __restrict__ starts, int E, int q) {

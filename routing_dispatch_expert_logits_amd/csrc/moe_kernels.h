@@ -18,6 +18,13 @@ enum Epi {
 
 enum GemmKind { GEMM_PREFILL = 0, GEMM_DECODE = 1, GEMM_SIMT = 2 };
 
+// E8M0 scale arrays of MXFP8 GEMM operands ([rows x K/32] bytes; NULL for bf16 GEMMs).
+struct MxScales {
+  const uint8_t* a;
+  const uint8_t* b0;
+  const uint8_t* b1;
+};
+
 int gemm_bm(GemmKind kind);
 int max_mtiles(int M, int E, int bm);
 
@@ -34,9 +41,19 @@ hipError_t launch_expert_scan(int32_t* block_counts, int nb, int E, int cap, int
 hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int E,
                           int32_t* offsets_out, int bm, int32_t* mtile_start, hipStream_t st);
 // bases: per-block rows before each block (launch_expert_scan); offsets: segment starts.
+// x_scale non-NULL: MXFP8 dispatch of bf16 rows (x_perm gets E4M3 codes, x_scale the
+// [rows x D/32] E8M0 scales; row16 = D / 8 must be a multiple of 4).
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
-                          const int32_t* offsets, const int32_t* bases, void* x_perm,
+                          const int32_t* offsets, const int32_t* bases, void* x_perm, uint8_t* x_scale,
                           int32_t* row_token, int32_t* token_row, hipStream_t st);
+// MXFP8 quantisation of [rows x cols] bf16 or fp32 values (cols % 32 == 0).
+hipError_t launch_mx_quantize(const void* src, bool src_bf16, long rows, long cols, uint8_t* q,
+                              uint8_t* scale, hipStream_t st);
+// Expert gate/up GEMM on MXFP8 rows and weights (D % 128 == 0), bf16 SwiGLU output;
+// GEMM_DECODE may read its rows through gather (as launch_gemm_decode_gather).
+hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const uint8_t* B0, const uint8_t* B1,
+                                 uint16_t* C, const int32_t* offsets, const int32_t* mtile_start, int E,
+                                 int N, int D, MxScales mx, const int32_t* gather, hipStream_t st);
 // add: nullable [T x row16 x 16 B] addend of the input element type, added after the k terms.
 hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
                           const float* w, const void* add, int T, int k, void* out, bool out_f32,

@@ -26,12 +26,20 @@ constexpr int kCopyUnroll = 4;
 // column split lets small token counts still fill the GPU).  Only the
 // blockIdx.y == 0 workgroups write the metadata.  x / x_perm rows are row16
 // 16-byte units long.
+//
+// MX = true (MXFP8 dispatch of bf16 rows): each token's row is quantised once (8
+// elements per lane, the 4 lanes of a 32-element block adjacent) and its E4M3 codes
+// (x_perm as bytes, rows of row16 * 8 codes) and E8M0 scales (xs, row16 / 4 per row)
+// are copied to its destinations: the dispatch carries one byte per element plus
+// one scale byte per 32.  Column splits then fall on multiples of 4 chunks.
+template <bool MX>
 __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, int row16,
                                                  const int32_t* __restrict__ topk_ids, int T,
                                                  int E, int k, int tpw, int cap,
                                                  const int32_t* __restrict__ offsets,
                                                  const int32_t* __restrict__ bases,
                                                  u32x4* __restrict__ x_perm,
+                                                 uint8_t* __restrict__ xs,
                                                  int32_t* __restrict__ row_token,
                                                  int32_t* __restrict__ token_row) {
   __shared__ unsigned long long mask[kMaxE];
@@ -40,8 +48,10 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
   const int btok = block_tokens(T);
   const int blk = tok0 / btok;
   const int bt0 = blk * btok;
-  const int c0 = (int)((long)row16 * blockIdx.y / gridDim.y);
-  const int c1 = (int)((long)row16 * (blockIdx.y + 1) / gridDim.y);
+  const int c0 = MX ? 4 * (int)((long)(row16 / 4) * blockIdx.y / gridDim.y)
+                    : (int)((long)row16 * blockIdx.y / gridDim.y);
+  const int c1 = MX ? 4 * (int)((long)(row16 / 4) * (blockIdx.y + 1) / gridDim.y)
+                    : (int)((long)row16 * (blockIdx.y + 1) / gridDim.y);
   const bool meta = blockIdx.y == 0;
   for (int e = tid; e < E; e += 256) mask[e] = 0ull;
   __syncthreads();
@@ -67,21 +77,49 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
       }
     }
     const u32x4* src = x + (size_t)t * row16;
-    for (int cb = c0; cb < c1; cb += kWave * kCopyUnroll) {
-      u32x4 v[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = cb + u * kWave + lane;
-        if (c < c1) v[u] = src[c];
-      }
-      for (int j = 0; j < k; ++j) {
-        const int r = __shfl(row, j, kWave);
-        if (r < 0) continue;  // dropped (uniform over the wave)
-        u32x4* dst = x_perm + (size_t)r * row16;
+    if constexpr (!MX) {
+      for (int cb = c0; cb < c1; cb += kWave * kCopyUnroll) {
+        u32x4 v[kCopyUnroll];
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
           const int c = cb + u * kWave + lane;
-          if (c < c1) dst[c] = v[u];
+          if (c < c1) v[u] = src[c];
+        }
+        for (int j = 0; j < k; ++j) {
+          const int r = __shfl(row, j, kWave);
+          if (r < 0) continue;  // dropped (uniform over the wave)
+          u32x4* dst = x_perm + (size_t)r * row16;
+#pragma unroll
+          for (int u = 0; u < kCopyUnroll; ++u) {
+            const int c = cb + u * kWave + lane;
+            if (c < c1) dst[c] = v[u];
+          }
+        }
+      }
+    } else {
+      // wave-uniform trip count: the block-max shuffles need every lane of a group
+      uint2* q = reinterpret_cast<uint2*>(x_perm);
+      for (int cb = c0; cb < c1; cb += kWave * kCopyUnroll) {
+        uint2 cv[kCopyUnroll];
+        int sc[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int c = cb + u * kWave + lane;
+          float f[8];
+          unpack_bf16x8(__builtin_bit_cast(uint4, src[min(c, c1 - 1)]), f);
+          cv[u] = mx_quantize8(f, &sc[u]);
+        }
+        for (int j = 0; j < k; ++j) {
+          const int r = __shfl(row, j, kWave);
+          if (r < 0) continue;  // dropped (uniform over the wave)
+#pragma unroll
+          for (int u = 0; u < kCopyUnroll; ++u) {
+            const int c = cb + u * kWave + lane;
+            if (c < c1) {
+              q[(size_t)r * row16 + c] = cv[u];
+              if ((c & 3) == 0) xs[(size_t)r * (row16 / 4) + (c >> 2)] = static_cast<uint8_t>(sc[u]);
+            }
+          }
         }
       }
     }
@@ -89,7 +127,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
 }
 
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
-                          const int32_t* offsets, const int32_t* bases, void* x_perm,
+                          const int32_t* offsets, const int32_t* bases, void* x_perm, uint8_t* x_scale,
                           int32_t* row_token, int32_t* token_row, hipStream_t st) {
   // 4 tokens per wave for large T, 1 for small T (a workgroup's tokens always lie
   // in one ranking block); split columns until ~1024 workgroups
@@ -97,9 +135,16 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
   const int gx = ceil_div(T, 4 * tpw);
   int cs = 1;
   while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
-  hipLaunchKernelGGL(k_permute, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
-                     ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), row_token,
-                     token_row);
+  if (x_scale) {  // MXFP8 dispatch of bf16 rows: row16 bf16 chunks -> row16 * 8 code bytes
+    if (row16 % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_permute<true>, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
+                       ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), x_scale,
+                       row_token, token_row);
+  } else {
+    hipLaunchKernelGGL(k_permute<false>, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
+                       ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), nullptr,
+                       row_token, token_row);
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ def host(t: torch.Tensor, bf16: bool = False) -> np.ndarray:
 
 
 def empty(shape, kind: str) -> torch.Tensor:
-    dt = {"f32": torch.float32, "bf16": torch.int16, "i32": torch.int32}[kind]
+    dt = {"f32": torch.float32, "bf16": torch.int16, "i32": torch.int32, "u8": torch.uint8}[kind]
     return torch.empty(shape, dtype=dt, device=DEV)
 
 
@@ -35,7 +35,8 @@ def ws(s: B.MoeShape, call: int) -> torch.Tensor:
 
 
 def shape_of(cfg) -> B.MoeShape:
-    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
+    return B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity,
+                   cfg.dispatch)
 
 
 def act_kind(cfg) -> str:

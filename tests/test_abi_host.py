@@ -104,19 +104,37 @@ def test_route_rejects_bad_arguments_on_host():
     bad = B.shape(64, 128, 8, 2, 256)
     bad.dtype = 7
     assert _route(bad) == B.MOE_ERR_INVALID_ARG
+    bad = B.shape(64, 128, 8, 2, 256)
+    bad.dispatch = 5
+    assert _route(bad) == B.MOE_ERR_INVALID_ARG
+    assert _route(B.shape(64, 128, 8, 2, 256, dtype="f32", dispatch="mxfp8")) == B.MOE_ERR_UNSUPPORTED
+    assert _route(B.shape(64, 192, 8, 2, 256, dispatch="mxfp8")) == B.MOE_ERR_UNSUPPORTED  # D % 128
+    assert _route(B.shape(64, 256, 8, 2, 256, dispatch="mxfp8"), ws_bytes=0) == B.MOE_ERR_WORKSPACE  # accepted
 
 
 def test_other_calls_reject_bad_arguments_on_host():
     s = B.shape(64, 128, 8, 2, 256)
     L = B.lib
-    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(s), FAKE, 1 << 20,
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, ctypes.byref(s), FAKE, 1 << 20,
                                   None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 0,
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(s), FAKE, 0,
                                   None) == B.MOE_ERR_WORKSPACE
-    assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.byref(s), FAKE, 1 << 30,
-                             None) == B.MOE_ERR_INVALID_ARG
-    assert L.moe_grouped_ffn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 8,
+    # a scale buffer is MXFP8-only
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(s), FAKE, 1 << 20,
+                                  None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn(FAKE, None, FAKE, FAKE, None, FAKE, None, None, FAKE, ctypes.byref(s), FAKE,
+                             1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_grouped_ffn(FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, ctypes.byref(s), FAKE, 8,
                              None) == B.MOE_ERR_WORKSPACE
+    mx = B.shape(64, 128, 8, 2, 256, dispatch="mxfp8")
+    assert L.moe_grouped_ffn(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(mx), FAKE,
+                             1 << 30, None) == B.MOE_ERR_INVALID_ARG            # MXFP8 rows need scales
+    assert L.moe_dispatch_permute(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(mx), FAKE, 1 << 20,
+                                  None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mxfp8(FAKE, B.MOE_BF16, 4, 48, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_mxfp8(FAKE, 9, 4, 64, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mxfp8(FAKE, B.MOE_BF16, 4, 64, FAKE + 4, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mxfp8(None, B.MOE_BF16, 0, 64, None, None, None) == B.MOE_OK   # nothing to do
     assert L.moe_combine(FAKE, FAKE, FAKE, None, FAKE, 5, 0, ctypes.byref(s), FAKE, 1 << 30,
                          None) == B.MOE_ERR_INVALID_ARG                     # out dtype
     assert L.moe_combine(FAKE, FAKE, FAKE, None, FAKE, 0, 3, ctypes.byref(s), FAKE, 1 << 30,

@@ -37,6 +37,7 @@ class MoEConfig:
     const_logits: bool = False         # every router logit equal (all-tie routing)
     shared_I: int = 0                  # shared expert intermediate width (0 = none)
     capacity: int = 0                  # rows kept per expert (0 = no limit, nothing dropped)
+    dispatch: str = "dtype"            # "dtype" or "mxfp8" (E4M3 rows + E8M0 scales per 32)
 
     @property
     def D(self) -> int:
