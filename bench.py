@@ -314,6 +314,11 @@ def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cm
         return out
 
     copy_bytes = copy_mib << 20
+    mx = config.endswith("_mxfp8")   # the MXFP8 kernels carry a trailing "true" template argument
+
+    def dominant(name):
+        return any(p in name for p in DOMINANT_KERNEL_PATTERNS) and (("true>" in name) == mx)
+
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rs = rows(path, counter)
@@ -321,8 +326,8 @@ def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cm
         big = max(copies)
         cal = [v for v in copies if v > 0.9 * big]
         scale = copy_bytes / (1024.0 * sum(cal) / len(cal))
-        gemm = [v for n, v in rs if any(p in n for p in DOMINANT_KERNEL_PATTERNS)]
-        kname = next(n for n, v in rs if any(p in n for p in DOMINANT_KERNEL_PATTERNS))
+        gemm = [v for n, v in rs if dominant(n)]
+        kname = next(n for n, v in rs if dominant(n))
         res[counter] = {"kib_per_launch": sum(gemm) / len(gemm), "launches": len(gemm),
                         "copy_kib": sum(cal) / len(cal), "scale": scale, "kernel": kname.split("(")[0]}
     hbm = (res["FETCH_SIZE"]["kib_per_launch"] * 1024 * res["FETCH_SIZE"]["scale"] +

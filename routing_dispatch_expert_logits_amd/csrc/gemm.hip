@@ -463,14 +463,10 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
     for (int s = 0; s < nsteps; ++s) {
       const uint16_t* base = lds + (s % S) * STAGE;
       const uint8_t* base8 = reinterpret_cast<const uint8_t*>(base);
+      // B fragments and all scales first, then A fragment by fragment, and the MFMAs
+      // fragment-row by fragment-row, so each row's MFMAs wait only for their own A
       u32x4 a0[FM], a1[FM], b0[NB][FN], b1[NB][FN];
       int sa[FM], sb[NB][FN];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        a0[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[0][fm]);
-        a1[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[1][fm]);
-        sa[fm] = base8[sa_off[fm]];
-      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -480,17 +476,24 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
           sb[nb][fn] = base8[sb_off[nb][fn]];
         }
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int fm = 0; fm < FM; ++fm) sa[fm] = base8[sa_off[fm]];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[nb][fn], b1[nb][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int fm = 0; fm < FM; ++fm) {
+        a0[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[0][fm]);
+        a1[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[1][fm]);
+      }
 #pragma unroll
-          for (int fm = 0; fm < FM; ++fm) {
-            const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[fm], a1[fm], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int fm = 0; fm < FM; ++fm) {
+        const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[fm], a1[fm], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[nb][fn], b1[nb][fn], 0, 1, 2, 3, 4, 5, 6, 7));
             acc[nb][fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[nb][fm][fn], 0, 0, 0,
                                                                                sa[fm], 0, sb[nb][fn]);
           }
-        }
+      }
       __syncthreads();  // every MFMA wave has read stage s; stage s+1 has landed
     }
   } else if constexpr (!kDoubleBuffer) {
