@@ -286,3 +286,77 @@ def test_layer_mx_equals_separate_calls(name):
     # bf16 output = RNE of the fp32 output
     d = run_layer_mx(cfg, inp, with_aux=False, out_dtype=B.MOE_BF16)
     np.testing.assert_array_equal(d["out"], _bf16_bits(a["out"]))
+
+
+# ------------------------------------------------------------------ full size, sampled tokens
+
+FULL_MX = ["qwen3_30b_a3b_shaped", "k3_shaped_decode", "k3_shaped_decode_t8"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL_MX)
+def test_layer_full_size_mx_sampled(name):
+    """The full-size layer with MXFP8 dispatch in the launch configuration bench.py
+    times: W1 / W3 codes of the sampled tokens' experts bit-exact against the oracle's
+    conversion, and the fp32 output of sampled tokens within the derived bound."""
+    from workloads import FULL_CONFIGS
+    cfg = _mx(FULL_CONFIGS[name])
+    print(f"\n[{name}] generating inputs", flush=True)
+    inp = gen.layer_inputs(cfg)
+    T, E, k, D, I = cfg.T, cfg.E, cfg.k, cfg.D, cfg.I
+    assert not cfg.L and not cfg.shared_I
+    s = shape_of(cfg)
+    w = {n: dev(inp[n]) for n in ("gate_w", "w2") if n in inp}
+    for n in ("w1", "w3"):
+        q, sc = empty((E, I, D), "u8"), empty((E, I, D // 32), "u8")
+        B.quantize_mxfp8(dev(inp[n]), q, sc)
+        w[n], w[n + "_scale"] = q, sc
+    if "bias" in inp:
+        w["gate_bias"] = dev(inp["bias"])
+    logits = dev(inp["logits"]) if "logits" in inp else empty((T, E), "f32")
+    ids = empty((T, k), "i32")
+    out32 = empty((T, cfg.H), "f32")
+    print(f"[{name}] running the layer", flush=True)
+    B.layer_forward(w, dev(inp["x"]), logits, out32, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER), {"topk_ids": ids})
+    torch.cuda.synchronize()
+    o32, gids = host(out32), host(ids)
+    rng = np.random.default_rng(cfg.seed + 1)
+    tok = np.sort(rng.choice(T, size=min(12, T), replace=False))
+    if "logits" in inp:
+        scores = oracle.router_scores(inp["logits"][tok], inp.get("bias"))
+        keep = np.ones(len(tok), dtype=bool)
+    else:
+        lg_ref = oracle.gate_logits(inp["x"][tok], inp["gate_w"], inp.get("bias"))
+        rms_l = float(np.sqrt(np.mean(lg_ref ** 2)))
+        scores = lg_ref.astype(np.float32)
+        srt = -np.sort(-lg_ref, axis=1)
+        keep = (srt[:, k - 1] - srt[:, k]) > 2e-5 * rms_l
+    r = oracle.route(scores, k, E)
+    np.testing.assert_array_equal(np.sort(gids[tok][keep], 1), np.sort(r["ids"][keep], 1))
+    tk, ids_k, wts_k = tok[keep], r["ids"][keep], r["weights"][keep]
+    xq, xs = M.mx_quantize(oracle.decode(inp["x"][tk]))
+    need = sorted(set(int(e) for e in ids_k.ravel()))
+    print(f"[{name}] oracle on {len(tk)} sampled tokens, {len(need)} experts", flush=True)
+    y, dy = {}, {}
+    for e in need:
+        wq = [M.mx_quantize(oracle.decode(inp[n][e])) for n in ("w1", "w3")]
+        for n, (q, sc) in zip(("w1", "w3"), wq):   # the conversion kernel at full size
+            np.testing.assert_array_equal(host(w[n + "_scale"][e]), sc)
+            np.testing.assert_array_equal(host(w[n][e]), q)
+        rows = [i for i in range(len(tk)) if e in ids_k[i]]
+        ye, p = M.expert_ffn_rows_mx(xq[rows], xs[rows], wq[0][0], wq[0][1], wq[1][0], wq[1][1],
+                                     inp["w2"][e], parts=True)
+        de = y_bound(ye, [(e, 0, len(rows), p)], {e: inp["w2"][e]})
+        for j, i in enumerate(rows):
+            y[(i, e)], dy[(i, e)] = ye[j], de[j]
+    ref = np.zeros((len(tk), cfg.H))
+    dout = np.zeros((len(tk), cfg.H))
+    for i in range(len(tk)):
+        for j in range(k):
+            e = int(ids_k[i, j])
+            ref[i] += wts_k[i, j] * y[(i, e)]
+            dout[i] += wts_k[i, j] * dy[(i, e)]
+    dout += 2.0 ** -20 * np.abs(ref) + 1e-30
+    ratio = float(np.max(np.abs(o32[tk] - ref) / dout))
+    print(f"[{name}] worst |d out| / bound = {ratio:.3f}", flush=True)
+    assert ratio <= 1.0
