@@ -92,6 +92,33 @@ def test_route_many_tokens_wide(E, k):
     _check_route(cfg, lg, None)
 
 
+@pytest.mark.parametrize("E,k,cap", [(256, 8, 0), (64, 4, 6000)])
+def test_route_and_dispatch_max_tokens(E, k, cap):
+    """131072 tokens (8192 ranking blocks, a million assignments): routing, the
+    permutation and the permuted rows bit-exact, with and without an expert capacity
+    that drops rows of the hot experts."""
+    T, H = 1 << 17, 64
+    r = np.random.default_rng(E + k)
+    lg = (r.standard_normal((T, E)) - 0.6 * np.log1p(np.arange(E))).astype(np.float32)  # skewed
+    cfg = PARITY_CONFIGS["all_ties"].with_(T=T, E=E, k=k, H=H, capacity=cap)
+    ref = _check_route(cfg, lg, None)
+    rt, tr = oracle.permutation(ref["ids"], E, cap)
+    if cap:
+        assert ref["routed_counts"].max() > cap        # something is dropped
+    x = gen.draw(cfg, gen.TAG_X, 0, (T, H), 1.0)
+    s = shape_of(cfg)
+    R = T * k
+    xp = empty((R, H), "bf16")
+    row_token, token_row = empty((R,), "i32"), empty((T, k), "i32")
+    B.dispatch_permute(dev(x), dev(ref["ids"].astype(np.int32)), dev(ref["offsets"].astype(np.int32)),
+                       xp, row_token, token_row, s, ws(s, B.MOE_CALL_DISPATCH))
+    torch.cuda.synchronize()
+    n = len(rt)
+    np.testing.assert_array_equal(host(row_token)[:n], rt)
+    np.testing.assert_array_equal(host(token_row), tr)
+    np.testing.assert_array_equal(host(xp, True)[:n], x[rt])
+
+
 @pytest.mark.parametrize("cfg", [c for c in CFGS if c.gate == "computed"],
                          ids=[c.name for c in CFGS if c.gate == "computed"])
 def test_gate_logits(cfg):
