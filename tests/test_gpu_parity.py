@@ -431,3 +431,40 @@ def test_layer_output_equals_separate_calls(name):
         bf = cfg.dtype == "bf16"
         ref_sh = oracle.shared_expert_ffn(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"], bf)
         _check_y(cfg, host(ysh, bf), ref_sh)
+
+
+def test_concurrent_layers_on_two_streams():
+    """Calls are re-entrant across distinct workspaces: two different layers launched
+    concurrently on two streams (default priority) give the bits of serial runs."""
+    cfgs = [PARITY_CONFIGS["small_bf16_zipf"], PARITY_CONFIGS["small_bf16_decode"].with_(dispatch="mxfp8")]
+    setups = []
+    for cfg in cfgs:
+        inp = gen.layer_inputs(cfg)
+        s = shape_of(cfg)
+        w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2") if n in inp}
+        if cfg.dispatch == "mxfp8":
+            for n in ("w1", "w3"):
+                q, sc = empty((cfg.E, cfg.I, cfg.D), "u8"), empty((cfg.E, cfg.I, cfg.D // 32), "u8")
+                B.quantize_mxfp8(w[n], q, sc)
+                w[n], w[n + "_scale"] = q, sc
+        if "bias" in inp:
+            w["gate_bias"] = dev(inp["bias"])
+        logits = dev(inp["logits"]) if "logits" in inp else empty((cfg.T, cfg.E), "f32")
+        setups.append((cfg, s, w, dev(inp["x"]), logits))
+    torch.cuda.synchronize()
+
+    def run(i, stream, reps):
+        cfg, s, w, x, logits = setups[i]
+        out = empty((cfg.T, cfg.H), "f32")
+        wsp = ws(s, B.MOE_CALL_LAYER)
+        for _ in range(reps):
+            B.layer_forward(w, x, logits, out, B.MOE_F32, s, wsp, stream=stream)
+        return out
+
+    serial = [host(run(i, None, 1)) for i in range(2)]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [run(0, s1, 20), run(1, s2, 20)]
+    torch.cuda.synchronize()
+    for i in range(2):
+        np.testing.assert_array_equal(host(outs[i]), serial[i])
