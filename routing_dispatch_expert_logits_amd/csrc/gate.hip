@@ -48,9 +48,18 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
                                               float* __restrict__ logits, int T, int E, int H,
                                               int Hs) {
   const int NT = ceil_div(E, kGBN);
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so workgroup
+  // b runs on XCD b % 8; giving each XCD a contiguous run of (token block, expert
+  // block) pairs keeps the NT workgroups that read one token block on one XCD and
+  // its rows in that XCD's L2 (dealt in plain order, every token block is fetched
+  // into several XCDs' L2s from HBM)
+  const int total = ceil_div(T, kGBM) * NT;
+  const int per_xcd = ceil_div(total, 8);
+  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || L >= total) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int m0 = (blockIdx.x / NT) * kGBM + (wave >> 1) * kGTM;
-  const int n0 = (blockIdx.x % NT) * kGBN + (wave & 1) * kGTN;
+  const int m0 = (L / NT) * kGBM + (wave >> 1) * kGTM;
+  const int n0 = (L % NT) * kGBN + (wave & 1) * kGTN;
   if (m0 >= T || n0 >= E) return;  // no barriers or LDS: a wave with no logits leaves
   const int kbeg = blockIdx.y * Hs;
   if (gridDim.y > 1) {
@@ -153,7 +162,7 @@ hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float*
                             float* partial, int T, int E, int H, hipStream_t st) {
   const int S = gate_splits(T, E, H);
   const int Hs = H / S;
-  const dim3 g(ceil_div(T, kGBM) * ceil_div(E, kGBN), S), b(256);
+  const dim3 g(ceil_div(ceil_div(T, kGBM) * ceil_div(E, kGBN), 8) * 8, S), b(256);
   hipLaunchKernelGGL(k_gate, g, b, 0, st, x, gate_w, bias, S > 1 ? partial : logits, T, E, H, Hs);
   if (S > 1) {
     const size_t n = (size_t)T * E;
