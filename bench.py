@@ -375,7 +375,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share of the layer only; --gpus {args.gpus} is not "
-              "supported (no collectives between GPUs in this build).", file=sys.stderr)
+              "supported (the library runs one GPU's share and has no collectives between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
