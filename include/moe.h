@@ -3,14 +3,16 @@
  * on AMD Instinct MI355X (gfx950).
  *
  * The calls follow the pipeline of the WideEP explainer page (Kimi K3), section
- * "The router writes a network schedule": the source computes gating scores and
- * top-k expert ids; a dispatcher counts destinations, allocates slots, permutes
- * token activations into destination-contiguous rows and attaches routing
- * metadata; the receiver groups rows by expert and runs the expert matrix
- * multiplies; the combine reverses the route and the source unpermutes and
+ * "The router writes a network schedule": the source scores each token against the
+ * experts and picks its top-k; a dispatcher tallies the rows bound for each
+ * destination, reserves their places, copies the token rows there in destination
+ * order and attaches routing metadata; the receiver groups rows by expert and runs
+ * the expert matrix multiplies; the combine sends results back and the source puts
+ * rows back in token order and
  * applies the routing weights.  On one GPU every assignment is local, so the
  * "transfer" is the permutation itself (same page, table of communication
- * paths, row "Same GPU": no fabric hop, still permute and HBM traffic).
+ * paths, row "Same GPU": nothing crosses a link, but the rows are still permuted and
+ * still cost HBM traffic).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -22,7 +24,7 @@
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream).  They never read device memory on the host and never
  *   synchronise: static grids, GPU-resident counts and offsets (same page,
- *   table row "CPU control path": static shapes, GPU-resident metadata).
+ *   table row "CPU control path": fixed shapes, metadata that stays on the device).
  *   Calls are re-entrant across distinct workspaces; two calls that share a
  *   workspace or outputs must be ordered by the caller.
  * - Element types: activations, expert weights, projections and the permuted
@@ -52,10 +54,11 @@
  *
  * MXFP8 dispatch (moe_shape.dispatch = MOE_DISPATCH_MXFP8; value-changing)
  * -------------------------------------------------------------------------
- * "Top-k multiplies traffic. Locality subtracts it." (WideEP explainer): a runtime
- * may quantise the outbound activation, carry scales, compute in another format
- * and return at higher precision; the comparison must count the conversion
- * kernels, the scale metadata and the accuracy impact.  Quantisation is a
+ * "Top-k multiplies traffic. Locality subtracts it." (WideEP explainer): the rows a
+ * device sends may travel in a narrower number format with their scale factors
+ * alongside, the expert math may run in that format, and results come back wide;
+ * an honest comparison includes the format-conversion work, the bytes of the
+ * scales and the change in the numbers.  Quantisation is a
  * value-changing optimisation ("Three Parameter Counts...", table of "Which
  * optimizations need a task-level gate").  The format is OCP MX "MXFP8-E4M3", the
  * one gfx950's scaled matrix instructions take: E4M3 codes (1 sign, 4 exponent
@@ -155,8 +158,8 @@ MOE_API int moe_abi_version(void);
  * Gate scores + top-k selection + per-expert counts and offsets (steps a1-a3).
  *
  * Passage: WideEP explainer, "The router writes a network schedule" (the source
- * computes gating scores and top-k expert ids; the dispatcher counts
- * destinations and allocates slots) and "Sparse compute. Dense availability."
+ * scores tokens against experts and picks each token's top-k; the dispatcher
+ * tallies rows per destination and reserves their places) and "Sparse compute. Dense availability."
  * (k of E experts per token).
  *
  * x        [T x H] activations (dtype); read only when gate_w != NULL.
@@ -213,9 +216,9 @@ MOE_API moe_status moe_dispatch_permute(const void* x, const int32_t* topk_ids, 
  * Passage: WideEP explainer, "The router writes a network schedule" (expert
  * matrix multiplies on the grouped rows) and "Sparse compute. Dense
  * availability." (fewer, fatter grouped GEMMs); "Three Parameter Counts...",
- * table of "Which optimizations need a task-level gate" (a grouped GEMM runs
- * several expert matrices in one launch with differing row counts and creates
- * no work for an expert that received no token).
+ * table of "Which optimizations need a task-level gate" (one grouped launch covers
+ * many experts' matrices whatever their row counts, and an expert without rows
+ * gets no work).
  *
  * x_perm [T*k x D] (dtype), offsets [E+1] int32.
  * w1, w3 [E x I x D], w2 [E x D x I] (dtype).  Weights of experts with no rows

@@ -9,8 +9,8 @@ input generator in ``workloads/``.
 It is a plain, slow, obviously correct restatement of what the layer
 computes, in float64 numpy, one step per function, in the order of the
 pipeline described on the WideEP explainer page ("The router writes a network
-schedule"): gating scores and top-k expert ids at the source, counts per
-destination and slot allocation, a permutation of activations into
+schedule"): scoring and top-k selection at the source, a tally per destination
+and the reservation of places, a permutation of activations into
 destination-contiguous rows with routing metadata, grouping by expert and the
 expert matrix multiplies, and the combine that undoes the permutation and
 applies the routing weights.
@@ -166,8 +166,8 @@ def expert_counts(ids: np.ndarray, E: int) -> np.ndarray:
 
     Counts are assignments, not unique tokens: a top-k token adds k rows ("Three
     Parameter Counts...", section "What the utilization dashboard smooths
-    away"); the dispatcher counts destinations ("The router writes a network
-    schedule").
+    away"); the dispatcher tallies the rows per destination ("The router writes a
+    network schedule").
     """
     counts = np.zeros(E, dtype=np.int64)
     for e in range(E):
@@ -270,8 +270,8 @@ def grouped_expert_ffn(x_perm: np.ndarray, offsets: np.ndarray, w1: np.ndarray, 
 
     The receiver groups rows by local expert and runs the expert matrix
     multiplies (WideEP explainer, "The router writes a network schedule"); a
-    grouped GEMM creates no work for an expert that received no token ("Three
-    Parameter Counts...", "Which optimizations need a task-level gate").
+    grouped GEMM gives an expert without rows nothing to do ("Three Parameter
+    Counts...", "Which optimizations need a task-level gate").
     """
     E = len(offsets) - 1
     D = w2.shape[1]
@@ -287,8 +287,8 @@ def shared_expert_ffn(x: np.ndarray, ws1: np.ndarray, ws3: np.ndarray, ws2: np.n
                       bf16: bool) -> np.ndarray:
     """The shared expert: a SwiGLU FFN that every token passes through, whatever
     the router picked ("Three Parameter Counts...", "What the utilization dashboard
-    smooths away": DeepSeekMoE-style shared experts run regardless of the router
-    score; it is one of the non-expert weights every rank replicates,
+    smooths away": shared experts of the DeepSeekMoE kind process every token
+    whatever the router decides; it is one of the non-expert weights every rank replicates,
     research-vault claim IX2-0406).  The pages give no formula; it is read as an
     expert of the routed experts' form (and rounding points) with its own
     intermediate width, on all T rows of the full-width state.  ws1, ws3 are
@@ -482,7 +482,7 @@ def token_outputs(inp: Dict[str, np.ndarray], tokens: np.ndarray, ids: np.ndarra
 
 
 def load_skew(counts: np.ndarray, T: int, k: int) -> float:
-    """Max expert load divided by mean expert load (mean = T*k/E).
+    """The largest per-expert load over the mean per-expert load (mean = T*k/E).
 
     "Three Parameter Counts...", "What the utilization dashboard smooths away".
     """

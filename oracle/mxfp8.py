@@ -3,10 +3,11 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import, call or run anything here; the product path never does.
 
-What the pages fix: a runtime may quantise the outbound activation, carry scales,
-compute in another format and return at higher precision, and a fair comparison
-counts the conversion kernels, the scale metadata and the accuracy impact ("Top-k
-multiplies traffic. Locality subtracts it.", WideEP explainer); quantising
+What the pages fix: the rows a device sends may travel in a narrower number format
+with their scale factors alongside, the expert math may run in that format and the
+results come back wide, and a fair comparison includes the conversion work, the
+bytes of the scales and the change in the numbers ("Top-k multiplies traffic.
+Locality subtracts it.", WideEP explainer); quantising
 activations or weights is value-changing ("Three Parameter Counts...", table of
 "Which optimizations need a task-level gate").
 

@@ -1,7 +1,7 @@
 // Permutation of token rows into expert-contiguous rows + routing metadata (step a4).
 //
-// The dispatcher permutes token activations into destination-contiguous
-// buffers and attaches routing metadata; the receiver groups rows by expert
+// The dispatcher copies token rows into buffers ordered by destination and adds
+// routing metadata; the receiver groups rows by expert
 // (WideEP explainer (Kimi K3), "The router writes a network schedule").  On
 // one GPU the destination is the expert itself, so one permutation does both.
 // The buffer holds exactly T*k*D elements: the dispatch payload T x k x H x B
