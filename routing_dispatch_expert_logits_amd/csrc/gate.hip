@@ -26,27 +26,33 @@ __device__ __forceinline__ void split3(f32x8 w, bf16x8& hi, bf16x8& mid, bf16x8&
   lo = __builtin_convertvector(r1 - __builtin_convertvector(mid, f32x8), bf16x8);
 }
 
-// Workgroup: 4 waves as 2 (tokens) x 2 (experts); a wave owns a 64 x 32 block of
-// logits, a workgroup 128 x 64.  No LDS: every lane loads its own MFMA operand
-// fragments (8 consecutive k of one X row, 8 consecutive k of one Wg row), two
-// 32-wide K-steps ahead of their use; the waves of a workgroup that share rows or
-// experts read the same lines at about the same time, so the repeats hit in L1.
-constexpr int kGTM = 64, kGTN = 32, kGBM = 2 * kGTM, kGBN = 2 * kGTN;
+// Workgroup: 4 waves as 2 (tokens) x 2 (experts); a wave owns a 64 x TN block of
+// logits (TN = 32 or 64), a workgroup 128 x 2 TN.  No LDS: every lane loads its own
+// MFMA operand fragments (8 consecutive k of one X row, 8 consecutive k of one Wg
+// row), two 32-wide K-steps ahead of their use; the waves of a workgroup that share
+// rows or experts read the same lines at about the same time, so the repeats hit
+// in L1.  The kernel is bound by the rate at which a CU can have such loads in
+// flight, so the wider tile (a third fewer bytes per MFMA) is faster wherever its
+// K slices stay long (gate_plan).
+constexpr int kGTM = 64, kGBM = 2 * kGTM;
 
+template <int TN>
 struct GateFrag {
-  u32x4 a[4];      // X rows m0 + 16 fm + l % 16
-  f32x4 b[2][2];   // Wg rows n0 + 16 fn + l % 16, two halves of 4 k
+  u32x4 a[4];            // X rows m0 + 16 fm + l % 16
+  f32x4 b[TN / 16][2];   // Wg rows n0 + 16 fn + l % 16, two halves of 4 k
 };
 
 // blockIdx.y selects a K slice [y * Hs, (y + 1) * Hs), Hs a multiple of 64
 // (split-K).  With one slice the result plus bias goes to logits; with several,
 // slice y writes its fp32 partial to logits + y * T * E and k_gate_reduce adds
 // the slices in a fixed order.
+template <int TN>
 __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
                                               const float* __restrict__ Wg,
                                               const float* __restrict__ bias,
                                               float* __restrict__ logits, int T, int E, int H,
                                               int Hs) {
+  constexpr int kGFN = TN / 16, kGBN = 2 * TN;
   const int NT = ceil_div(E, kGBN);
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, so workgroup
   // b runs on XCD b % 8; giving each XCD a contiguous run of (token block, expert
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
   if ((int)(blockIdx.x >> 3) >= per_xcd || L >= total) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m0 = (L / NT) * kGBM + (wave >> 1) * kGTM;
-  const int n0 = (L % NT) * kGBN + (wave & 1) * kGTN;
+  const int n0 = (L % NT) * kGBN + (wave & 1) * TN;
   if (m0 >= T || n0 >= E) return;  // no barriers or LDS: a wave with no logits leaves
   const int kbeg = blockIdx.y * Hs;
   if (gridDim.y > 1) {
@@ -68,32 +74,32 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
   }
   const int kl = (lane >> 4) * 8;
   const uint16_t* pa[4];
-  const float* pb[2];
+  const float* pb[kGFN];
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm) pa[fm] = X + (size_t)min(m0 + fm * 16 + (lane & 15), T - 1) * H + kbeg + kl;
 #pragma unroll
-  for (int fn = 0; fn < 2; ++fn) pb[fn] = Wg + (size_t)min(n0 + fn * 16 + (lane & 15), E - 1) * H + kbeg + kl;
+  for (int fn = 0; fn < kGFN; ++fn) pb[fn] = Wg + (size_t)min(n0 + fn * 16 + (lane & 15), E - 1) * H + kbeg + kl;
 
-  auto load = [&](GateFrag& f, int k) {
+  auto load = [&](GateFrag<TN>& f, int k) {
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) f.a[fm] = *reinterpret_cast<const u32x4*>(pa[fm] + k);
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
+    for (int fn = 0; fn < kGFN; ++fn) {
       f.b[fn][0] = *reinterpret_cast<const f32x4*>(pb[fn] + k);
       f.b[fn][1] = *reinterpret_cast<const f32x4*>(pb[fn] + k + 4);
     }
   };
-  f32x4 acc[3][4][2];
+  f32x4 acc[3][4][kGFN];
 #pragma unroll
   for (int j = 0; j < 3; ++j)
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-      for (int fn = 0; fn < 2; ++fn) acc[j][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto step = [&](const GateFrag& f) {
-    bf16x8 bh[2], bm[2], bl[2];
+      for (int fn = 0; fn < kGFN; ++fn) acc[j][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](const GateFrag<TN>& f) {
+    bf16x8 bh[kGFN], bm[kGFN], bl[kGFN];
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn) {
+    for (int fn = 0; fn < kGFN; ++fn) {
       const f32x8 w = {f.b[fn][0][0], f.b[fn][0][1], f.b[fn][0][2], f.b[fn][0][3],
                        f.b[fn][1][0], f.b[fn][1][1], f.b[fn][1][2], f.b[fn][1][3]};
       split3(w, bh[fn], bm[fn], bl[fn]);
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
     for (int fm = 0; fm < 4; ++fm) {
       const bf16x8 a = as_bf16x8(f.a[fm]);
 #pragma unroll
-      for (int fn = 0; fn < 2; ++fn) {
+      for (int fn = 0; fn < kGFN; ++fn) {
         acc[0][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh[fn], acc[0][fm][fn], 0, 0, 0);
         acc[1][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bm[fn], acc[1][fm][fn], 0, 0, 0);
         acc[2][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl[fn], acc[2][fm][fn], 0, 0, 0);
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
   };
   // two K-steps in flight; past the end of the slice the loads repeat its last
   // step (in bounds, never consumed)
-  GateFrag f0, f1;
+  GateFrag<TN> f0, f1;
   load(f0, 0);
   load(f1, 32);
   for (int k = 0; k < Hs; k += 64) {
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gate(const uint16_t* __restrict__ X,
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < 2; ++fn)
+    for (int fn = 0; fn < kGFN; ++fn)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = m0 + fm * 16 + (lane >> 4) * 4 + i;
@@ -149,21 +155,34 @@ __global__ __launch_bounds__(256) void k_gate_reduce(const float* __restrict__ p
   logits[i] = v;
 }
 
-int gate_splits(int T, int E, int H) {
-  // split K until about 1024 waves run (each K slice a multiple of 64); a 2048-wave
-  // target measured slower on the Qwen3-, DeepSeek-R1-shaped and latent layers
-  const int waves = ceil_div(T, kGBM) * ceil_div(E, kGBN) * 4;
-  int s = 1;
-  while (waves * s < 1024 && s < 8 && H % (64 * s * 2) == 0) s *= 2;
-  return s;
+GatePlan gate_plan(int T, int E, int H) {
+  // split K until about 1024 waves run (each K slice a multiple of 64; a 2048-wave
+  // target measured slower on the Qwen3-, DeepSeek-R1-shaped and latent layers);
+  // the 64-wide tile when its slices stay at least 1024 long (measured: 18 % faster
+  // on the DeepSeek-R1-shaped and latent gates, 6 % slower on the Qwen3-shaped one,
+  // whose 128 experts would need 8 slices of 256)
+  auto splits = [&](int tn) {
+    const int waves = ceil_div(T, kGBM) * ceil_div(E, 2 * tn) * 4;
+    int s = 1;
+    while (waves * s < 1024 && s < 8 && H % (64 * s * 2) == 0) s *= 2;
+    return s;
+  };
+  const int s64 = splits(64);
+  if (H / s64 >= 1024) return GatePlan{64, s64};
+  return GatePlan{32, splits(32)};
 }
 
 hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
                             float* partial, int T, int E, int H, hipStream_t st) {
-  const int S = gate_splits(T, E, H);
+  const GatePlan p = gate_plan(T, E, H);
+  const int S = p.splits;
   const int Hs = H / S;
-  const dim3 g(ceil_div(ceil_div(T, kGBM) * ceil_div(E, kGBN), 8) * 8, S), b(256);
-  hipLaunchKernelGGL(k_gate, g, b, 0, st, x, gate_w, bias, S > 1 ? partial : logits, T, E, H, Hs);
+  const dim3 g(ceil_div(ceil_div(T, kGBM) * ceil_div(E, 2 * p.tn), 8) * 8, S), b(256);
+  float* dst = S > 1 ? partial : logits;
+  if (p.tn == 64)
+    hipLaunchKernelGGL(k_gate<64>, g, b, 0, st, x, gate_w, bias, dst, T, E, H, Hs);
+  else
+    hipLaunchKernelGGL(k_gate<32>, g, b, 0, st, x, gate_w, bias, dst, T, E, H, Hs);
   if (S > 1) {
     const size_t n = (size_t)T * E;
     hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial, S,

@@ -160,7 +160,7 @@ P* at(void* ws, size_t off) {
 
 size_t gate_partial_bytes(const Dims& d) {
   if (!d.bf16) return 0;
-  const int s = gate_splits(d.T, d.E, d.H);
+  const int s = gate_plan(d.T, d.E, d.H).splits;
   return s > 1 ? (size_t)s * d.T * d.E * 4 : 0;
 }
 

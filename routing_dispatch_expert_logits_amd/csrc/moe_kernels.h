@@ -85,8 +85,12 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st);
 // Router logits = X gate_w^T + bias, X bf16, gate_w fp32 (split-bf16 MFMA, fp32 accuracy); H % 64 == 0.
-// partial: gate_splits(T, E, H) * T * E floats of scratch (unused when that is 1).
-int gate_splits(int T, int E, int H);
+// The gate kernel's tile width (32 or 64 experts per wave) and split-K count for a shape.
+struct GatePlan {
+  int tn, splits;
+};
+GatePlan gate_plan(int T, int E, int H);
+// partial: gate_plan(T, E, H).splits * T * E floats of scratch (unused when that is 1).
 hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
                             float* partial, int T, int E, int H, hipStream_t st);
 // fp32 SIMT GEMM (A fp32 or bf16, B fp32).

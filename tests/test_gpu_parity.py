@@ -119,8 +119,16 @@ def test_route_and_dispatch_max_tokens(E, k, cap):
     np.testing.assert_array_equal(host(xp, True)[:n], x[rt])
 
 
-@pytest.mark.parametrize("cfg", [c for c in CFGS if c.gate == "computed"],
-                         ids=[c.name for c in CFGS if c.gate == "computed"])
+# Gates that take the 64-expert-wide wave tile (long K slices): ragged T and E, with
+# split-K over 8 slices and with a bias
+WIDE_GATES = [MoEConfig(name="gate64_ragged", T=130, H=8192, E=200, k=4, I=64, seed=51, gate="computed",
+                        gate_std=None),
+              MoEConfig(name="gate64_bias", T=70, H=8192, E=96, k=6, I=64, seed=52, gate="computed",
+                        gate_std=None, zipf_s=1.1, zipf_alpha=1.0)]
+
+
+@pytest.mark.parametrize("cfg", [c for c in CFGS if c.gate == "computed"] + WIDE_GATES,
+                         ids=[c.name for c in CFGS if c.gate == "computed"] + [c.name for c in WIDE_GATES])
 def test_gate_logits(cfg):
     inp = gen.layer_inputs(cfg, with_experts=False)
     s = shape_of(cfg)
