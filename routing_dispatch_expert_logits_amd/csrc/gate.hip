@@ -173,9 +173,11 @@ GatePlan gate_plan(int T, int E, int H) {
 }
 
 hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
-                            float* partial, int T, int E, int H, hipStream_t st) {
+                            float* partial, int T, int E, int H, hipStream_t st, bool defer_reduce,
+                            int* splits) {
   const GatePlan p = gate_plan(T, E, H);
   const int S = p.splits;
+  if (splits) *splits = S;
   const int Hs = H / S;
   const dim3 g(ceil_div(ceil_div(T, kGBM) * ceil_div(E, 2 * p.tn), 8) * 8, S), b(256);
   float* dst = S > 1 ? partial : logits;
@@ -183,7 +185,7 @@ hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float*
     hipLaunchKernelGGL(k_gate<64>, g, b, 0, st, x, gate_w, bias, dst, T, E, H, Hs);
   else
     hipLaunchKernelGGL(k_gate<32>, g, b, 0, st, x, gate_w, bias, dst, T, E, H, Hs);
-  if (S > 1) {
+  if (S > 1 && !defer_reduce) {  // deferred: the top-k kernel sums the slices as it reads them
     const size_t n = (size_t)T * E;
     hipLaunchKernelGGL(k_gate_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, partial, S,
                        bias, logits, T, E);

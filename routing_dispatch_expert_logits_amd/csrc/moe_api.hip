@@ -164,16 +164,29 @@ size_t gate_partial_bytes(const Dims& d) {
   return s > 1 ? (size_t)s * d.T * d.E * 4 : 0;
 }
 
+// a1, and where a2 then reads the scores (ScoreSrc): with the gate's output split
+// over K the top-k kernel sums the slices and writes the logits itself (one launch
+// and one pass over T x E fewer than a separate reduce).
 moe_status gate_scores(const Dims& d, const void* x, const float* gate_w, const float* bias,
-                       float* logits, float* partial, hipStream_t st) {
+                       float* logits, float* partial, hipStream_t st, ScoreSrc* src) {
+  int S = 1;
   if (d.bf16) {
     MOE_HIP(launch_gate_bf16(static_cast<const uint16_t*>(x), gate_w, bias, logits, partial, d.T, d.E,
-                             d.H, st));
+                             d.H, st, true, &S));
   } else {
     MOE_HIP(launch_gemm_simt(false, EPI_F32_BIAS, x, d.T, gate_w, nullptr, logits, nullptr, nullptr,
                              1, d.E, d.H, bias, st));
   }
+  if (S > 1)
+    *src = ScoreSrc{nullptr, partial, S, (size_t)d.T * d.E, bias, logits};
+  else  // the gate wrote logits with the bias in them
+    *src = ScoreSrc{logits, nullptr, 1, 0, nullptr, nullptr};
   return MOE_OK;
+}
+
+// Given router logits: read as they are, the bias (nullable) added on the fly.
+ScoreSrc given_scores(const float* logits, const float* bias) {
+  return ScoreSrc{logits, nullptr, 1, 0, bias, nullptr};
 }
 
 moe_status expert_ffn(const Dims& d, const void* x_perm, const int32_t* offsets,
@@ -264,12 +277,13 @@ moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_
   const RouteWs w = route_ws(d, gate_w != nullptr);
   if (!ws || ws_bytes < w.total || !al16(ws)) return MOE_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  ScoreSrc src = given_scores(logits, gate_bias);
   if (gate_w) {
-    rc = gate_scores(d, x, gate_w, gate_bias, logits, at<float>(ws, w.gpart), st);
+    rc = gate_scores(d, x, gate_w, gate_bias, logits, at<float>(ws, w.gpart), st, &src);
     if (rc != MOE_OK) return rc;
   }
   int32_t* bc = at<int32_t>(ws, w.bc);
-  MOE_HIP(launch_topk(logits, gate_w ? nullptr : gate_bias, d.T, d.E, d.k, topk_ids, topk_w, bc, st));
+  MOE_HIP(launch_topk(src, d.T, d.E, d.k, topk_ids, topk_w, bc, st));
   MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, counts, st));
   MOE_HIP(launch_offsets(counts, nullptr, d.E, offsets, 0, nullptr, st));
   return MOE_OK;
@@ -412,8 +426,9 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     if (rc != MOE_OK) return rc;
   }
   if (!ev(1)) return MOE_ERR_HIP;
+  ScoreSrc scores = given_scores(lg, wt->gate_bias);
   if (wt->gate_w) {  // a1: router logits on the full-width state
-    rc = gate_scores(d, x, wt->gate_w, wt->gate_bias, lg, at<float>(ws, w.gpart), st);
+    rc = gate_scores(d, x, wt->gate_w, wt->gate_bias, lg, at<float>(ws, w.gpart), st, &scores);
     if (rc != MOE_OK) return rc;
   }
   if (!ev(2)) return MOE_ERR_HIP;
@@ -429,7 +444,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
   uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;
   if (small) {
-    MOE_HIP(launch_route_small(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, counts,
+    MOE_HIP(launch_route_small(scores, d.T, d.E, d.k, ids, tw, counts,
                                offs, rtok, trow, d.cap, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
     if (d.mx) {
@@ -439,7 +454,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     }
   } else {
     // a2 + a3
-    MOE_HIP(launch_topk(lg, wt->gate_w ? nullptr : wt->gate_bias, d.T, d.E, d.k, ids, tw, bc, st));
+    MOE_HIP(launch_topk(scores, d.T, d.E, d.k, ids, tw, bc, st));
     MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, counts, st));
     MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;

@@ -28,8 +28,20 @@ struct MxScales {
 int gemm_bm(GemmKind kind);
 int max_mtiles(int M, int E, int bm);
 
-hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
-                       float* w, int32_t* block_counts, hipStream_t st);
+// Where the top-k kernels read each token's E scores: a scores row [T x E], plus an
+// optional bias added on the fly; or, with parts non-NULL, the gate's S split-K partial
+// rows (slice p at parts + p * stride) summed in ascending p, plus the bias, and that
+// sum also written to logits_out (the same bits k_gate_reduce would write).
+struct ScoreSrc {
+  const float* scores;
+  const float* parts;
+  int S;
+  size_t stride;
+  const float* bias;
+  float* logits_out;
+};
+hipError_t launch_topk(const ScoreSrc& src, int T, int E, int k, int32_t* ids, float* w,
+                       int32_t* block_counts, hipStream_t st);
 hipError_t launch_block_counts(const int32_t* ids, int T, int E, int k, int32_t* block_counts,
                                hipStream_t st);
 // block_counts[b][e] -> rows of e in blocks before b; counts_out[e] = total (if non-NULL).
@@ -66,7 +78,7 @@ hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, co
                                   bool out_f32, hipStream_t st);
 // Decode-scale routing (T <= kSmallT) in one launch: ids, weights, counts, offsets, the m-tile
 // tables (bm > 0) and row_token / token_row, as the large-T kernels produce them.
-hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
+hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
                              int32_t* token_row, int cap, int bm, int32_t* mtile_start,
                              hipStream_t st);
@@ -91,8 +103,11 @@ struct GatePlan {
 };
 GatePlan gate_plan(int T, int E, int H);
 // partial: gate_plan(T, E, H).splits * T * E floats of scratch (unused when that is 1).
+// *splits (nullable) receives that count.  With defer_reduce and more than one slice the
+// slices stay in partial and logits are written by the top-k kernel (ScoreSrc.parts).
 hipError_t launch_gate_bf16(const uint16_t* x, const float* gate_w, const float* bias, float* logits,
-                            float* partial, int T, int E, int H, hipStream_t st);
+                            float* partial, int T, int E, int H, hipStream_t st, bool defer_reduce,
+                            int* splits);
 // fp32 SIMT GEMM (A fp32 or bf16, B fp32).
 hipError_t launch_gemm_simt(bool a_bf16, int epi, const void* A, int M, const float* B0,
                             const float* B1, void* C, const int32_t* offsets,

@@ -27,21 +27,38 @@ namespace moe {
 // wave-wide largest key, then the lowest expert index holding it (so equal scores
 // go to the lower index), and removes that entry; both reductions are DPP row
 // butterflies plus readlane.
+// The token's scores come from src (see ScoreSrc): a scores row plus an optional
+// bias formed on the fly, or the gate's split-K partial rows summed in ascending
+// slice order plus the bias, the sum then written out as the token's logits row
+// (the arithmetic of k_gate_reduce, so the logits are the same bits).
 template <int SLOTS>
-__device__ __forceinline__ void rank_token(const float* __restrict__ row,
-                                           const float* __restrict__ bias, int E, int k, int lane,
+__device__ __forceinline__ void rank_token(const ScoreSrc& src, size_t row0, int E, int k, int lane,
                                            int& my_e, float& my_w) {
   // every load is issued unconditionally (lanes past E read the last score and
   // are masked afterwards) so they overlap instead of each waiting in a branch
   float v[SLOTS];
+  const float* first = src.parts ? src.parts : src.scores;
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) v[s] = row[min(lane + s * kWave, E - 1)];
-  if (bias) {
+  for (int s = 0; s < SLOTS; ++s) v[s] = first[row0 + min(lane + s * kWave, E - 1)];
+  for (int p = 1; p < src.S; ++p) {
+    float q[SLOTS];
+    const float* part = src.parts + (size_t)p * src.stride + row0;
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) q[s] = part[min(lane + s * kWave, E - 1)];
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s) v[s] += q[s];
+  }
+  if (src.bias) {
     float b[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) b[s] = bias[min(lane + s * kWave, E - 1)];
+    for (int s = 0; s < SLOTS; ++s) b[s] = src.bias[min(lane + s * kWave, E - 1)];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) v[s] += b[s];
+  }
+  if (src.logits_out) {
+#pragma unroll
+    for (int s = 0; s < SLOTS; ++s)
+      if (lane + s * kWave < E) src.logits_out[row0 + lane + s * kWave] = v[s];
   }
   uint32_t key[SLOTS];
 #pragma unroll
@@ -79,8 +96,7 @@ __device__ __forceinline__ void rank_token(const float* __restrict__ row,
 // expert for the block are gathered in LDS (order-independent) and written to
 // block_counts[block][e].
 template <int SLOTS>
-__global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_in,
-                                               const float* __restrict__ bias, int T, int E, int k,
+__global__ __launch_bounds__(1024) void k_topk(ScoreSrc src, int T, int E, int k,
                                                int32_t* __restrict__ topk_ids,
                                                float* __restrict__ topk_w,
                                                int32_t* __restrict__ block_counts) {
@@ -94,7 +110,7 @@ __global__ __launch_bounds__(1024) void k_topk(const float* __restrict__ scores_
   if (t < T) {
     int my_e;
     float my_w;
-    rank_token<SLOTS>(scores_in + (size_t)t * E, bias, E, k, lane, my_e, my_w);
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, my_e, my_w);
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_e;
       topk_w[(size_t)t * k + lane] = my_w;
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
 // dropped (token_row = -1) and counts are min(count, cap).
 template <int SLOTS>
 __global__ __launch_bounds__(1024) void k_route_small(
-    const float* __restrict__ scores_in, const float* __restrict__ bias, int T, int E, int k,
+    ScoreSrc src, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
     int cap, int bm, int32_t* __restrict__ mtile_start) {
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
   for (int t = wave; t < T; t += 16) {
     int my_e;
     float my_w;
-    rank_token<SLOTS>(scores_in + (size_t)t * E, bias, E, k, lane, my_e, my_w);
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, my_e, my_w);
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_e;
       topk_w[(size_t)t * k + lane] = my_w;
@@ -317,16 +333,16 @@ __global__ void k_single_group(int T, int32_t* __restrict__ offsets, int bm,
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
-                       float* w, int32_t* block_counts, hipStream_t st) {
+hipError_t launch_topk(const ScoreSrc& src, int T, int E, int k, int32_t* ids, float* w,
+                       int32_t* block_counts, hipStream_t st) {
   const int nb = ceil_div(T, block_tokens(T));
   const int slots = ceil_div(E, kWave);
   dim3 g(nb), b(1024);
-  if (slots <= 1) hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 2) hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 4) hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else if (slots <= 8) hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
-  else hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, scores, bias, T, E, k, ids, w, block_counts);
+  if (slots <= 1) hipLaunchKernelGGL(k_topk<1>, g, b, 0, st, src, T, E, k, ids, w, block_counts);
+  else if (slots <= 2) hipLaunchKernelGGL(k_topk<2>, g, b, 0, st, src, T, E, k, ids, w, block_counts);
+  else if (slots <= 4) hipLaunchKernelGGL(k_topk<4>, g, b, 0, st, src, T, E, k, ids, w, block_counts);
+  else if (slots <= 8) hipLaunchKernelGGL(k_topk<8>, g, b, 0, st, src, T, E, k, ids, w, block_counts);
+  else hipLaunchKernelGGL(k_topk<16>, g, b, 0, st, src, T, E, k, ids, w, block_counts);
   return hipGetLastError();
 }
 
@@ -351,7 +367,7 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
   return hipGetLastError();
 }
 
-hipError_t launch_route_small(const float* scores, const float* bias, int T, int E, int k, int32_t* ids,
+hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
                              int32_t* token_row, int cap, int bm, int32_t* mtile_start,
                              hipStream_t st) {
@@ -359,7 +375,7 @@ hipError_t launch_route_small(const float* scores, const float* bias, int T, int
   const int slots = ceil_div(E, kWave);
   dim3 g(1), b(1024);
 #define MOE_RS(SL)                                                                                   \
-  hipLaunchKernelGGL((k_route_small<SL>), g, b, 0, st, scores, bias, T, E, k, ids, w, counts, offsets, \
+  hipLaunchKernelGGL((k_route_small<SL>), g, b, 0, st, src, T, E, k, ids, w, counts, offsets, \
                      row_token, token_row, cap, bm, mtile_start)
   if (slots <= 1) MOE_RS(1);
   else if (slots <= 2) MOE_RS(2);
