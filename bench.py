@@ -277,24 +277,22 @@ def cpu_baseline(cfg, inp, target_s):
 
 def gate_up_kernel(cfg):
     """Name of the kernel moe_grouped_ffn picks for the expert gate/up GEMM (the
-    library's choice: 128-row warp-specialised MFMA tiles when the mean rows per
-    expert reach 48, n-tiles in pairs when there are 16 or more of them, 16-row
-    weight-streaming tiles below 48 rows, SIMT for fp32)."""
+    library's choice: the persistent wave-specialised kernel on 128-row MFMA tiles
+    when the mean rows per expert reach 48, 16-row weight-streaming tiles below 48
+    rows, SIMT for fp32)."""
     if cfg.dtype != "bf16":
         return "k_gemm_simt<SwiGLU> (expert gate/up GEMM, fp32)"
     mx = cfg.dispatch == "mxfp8"
     if cfg.R >= 48 * cfg.E:
         if mx:
-            g = "2" if -(-cfg.I // 128) >= 16 else "1"
-            return f"k_gemm_ws<128,128,2,SwiGLU,3,8,64,{g},MXFP8> (expert gate/up GEMM, MXFP8)"
-        g = ",64,2" if -(-cfg.I // 128) >= 16 else ""
-        return f"k_gemm_ws<128,128,2,SwiGLU,3,8{g}> (expert gate/up GEMM)"
+            return "k_gemm_wsp<128,128,2,SwiGLU,3,8,MXFP8> (expert gate/up GEMM, MXFP8, persistent)"
+        return "k_gemm_wsp<128,128,2,SwiGLU,3,8> (expert gate/up GEMM, persistent)"
     if mx:
         return "k_gemm_decode<2,2,SwiGLU,MXFP8> (expert gate/up GEMM, MXFP8)"
     return "k_gemm_decode<2,2,SwiGLU> (expert gate/up GEMM)"
 
 
-DOMINANT_KERNEL_PATTERNS = ("k_gemm_prefill<128, 128, 2,", "k_gemm_ws<128, 128, 2,", "k_gemm_decode<2, 2,")
+DOMINANT_KERNEL_PATTERNS = ("k_gemm_prefill<128, 128, 2,", "k_gemm_wsp<128, 128, 2,", "k_gemm_ws<128, 128, 2,", "k_gemm_decode<2, 2,")
 
 
 def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cmd):

@@ -28,6 +28,34 @@ struct TileCoord {
   int e, row0, rows, n0;
 };
 
+// Logical tile L of a grouped GEMM (L < mtile_start[E] * ceil(N / BN)).
+template <int BM, int BN, int G>
+__device__ __forceinline__ TileCoord grouped_tile(const int32_t* __restrict__ offsets,
+                                                  const int32_t* __restrict__ mtile_start, int E, int N,
+                                                  int L) {
+  const int NT = ceil_div(N, BN);
+  const int e = upper_index(mtile_start, E, L / NT);
+  const int mt0 = mtile_start[e];
+  const int mte = mtile_start[e + 1] - mt0;
+  const int local = L - mt0 * NT;
+  int n_idx, m_idx;
+  if constexpr (G == 1) {
+    n_idx = local / mte;
+    m_idx = local - n_idx * mte;
+  } else {
+    const int grp = local / (G * mte), r = local - grp * (G * mte);
+    const int ng = min(G, NT - grp * G);  // n-tiles in this group
+    m_idx = r / ng;
+    n_idx = grp * G + (r - m_idx * ng);
+  }
+  TileCoord tc;
+  tc.e = e;
+  tc.row0 = offsets[e] + m_idx * BM;
+  tc.rows = min(BM, offsets[e + 1] - tc.row0);
+  tc.n0 = n_idx * BN;
+  return tc;
+}
+
 // Returns false when this workgroup has no tile.  Within an expert, tiles run in
 // groups of G consecutive n-tiles; inside a group the m-tile index is outer, so
 // the G tiles reading one m-tile's rows are adjacent and each weight panel is
@@ -45,24 +73,7 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
   const int L = xcd * per_xcd + slot;
   if (L >= total) return false;
   if (offsets) {
-    const int e = upper_index(mtile_start, E, L / NT);
-    const int mt0 = mtile_start[e];
-    const int mte = mtile_start[e + 1] - mt0;
-    const int local = L - mt0 * NT;
-    int n_idx, m_idx;
-    if constexpr (G == 1) {
-      n_idx = local / mte;
-      m_idx = local - n_idx * mte;
-    } else {
-      const int grp = local / (G * mte), r = local - grp * (G * mte);
-      const int ng = min(G, NT - grp * G);  // n-tiles in this group
-      m_idx = r / ng;
-      n_idx = grp * G + (r - m_idx * ng);
-    }
-    tc.e = e;
-    tc.row0 = offsets[e] + m_idx * BM;
-    tc.rows = min(BM, offsets[e + 1] - tc.row0);
-    tc.n0 = n_idx * BN;
+    tc = grouped_tile<BM, BN, G>(offsets, mtile_start, E, N, L);
   } else {
     const int n_idx = L / total_mt, m_idx = L - n_idx * total_mt;
     tc.e = 0;
@@ -73,7 +84,14 @@ __device__ __forceinline__ bool decode_tile(const int32_t* __restrict__ offsets,
   return true;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
+// SiLU(g) * u = g * u / (1 + e^-g), with e^-g = 2^(-g log2 e) from the hardware exp2 and
+// the hardware reciprocal (each within about one fp32 ulp, far below the bf16 rounding
+// of the intermediate).  A very negative g overflows e^-g to inf and its reciprocal to
+// 0, so the product is 0, as SiLU tends to.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.f + e) * u;
+}
 
 template <int EPI>
 __device__ __forceinline__ void epi_store(void* C, size_t idx, float v0, float v1, const float* bias,
@@ -548,6 +566,362 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
       }
 }
 
+// ------------------------------------------------------------------ persistent variant
+// k_gemm_wsp: the wave-specialised kernel as a persistent kernel for the expert
+// gate/up GEMMs.  One workgroup per CU; workgroup i runs on XCD i % 8 and takes the
+// tiles of that XCD's contiguous chunk of logical tiles one at a time, in order, from
+// the chunk's claim counter (claim[i % 8], an agent-scope atomic).  So the 32 CUs of
+// an XCD work through its chunk in the order the hardware would have dispatched
+// one-tile workgroups (the tiles sharing an expert's weights run together), a CU
+// that runs slow simply takes fewer tiles, and there is no per-tile dispatch, launch
+// or pipeline fill: the loader waves run ahead across tile boundaries, so the next
+// tile's first stages are in flight while the MFMA waves store the previous one.
+// Each workgroup decodes its XCD's chunk once into an LDS table.  Tiles, K-steps,
+// LDS layout and MFMA order are those of k_gemm_ws, so the results are the same
+// bits.  The claim counters must be zero at launch: the m-tile table kernels
+// (k_offsets, k_route_small, k_single_group) clear them.
+
+// Chunk entries an LDS table can hold (4 bytes each: expert | m-tile << 10 | n-tile << 22).
+template <bool F8>
+constexpr int wsp_table_cap() { return F8 ? 2816 : 3840; }
+constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0) (vmcnt, expcnt not waited)
+
+// Whether the persistent kernel takes a GEMM of at most `tiles` 128 x 128 tiles with K
+// 16-bit columns: the XCD chunk fits the LDS table, tile coordinates fit the entry,
+// and a tile has at least 3 K-steps (the claim of the next tile is published one
+// K-step after it is issued and read two K-steps before the tile ends).
+template <bool F8>
+static inline bool wsp_fits(long tiles, int E, int N, int K) {
+  return (tiles + 7) / 8 <= wsp_table_cap<F8>() && E <= 1024 && ceil_div(N, 128) <= 1024 && K % 64 == 0 &&
+         K / 64 >= 3;
+}
+
+template <int BM, int BN, int NB, int EPI, int S, int MW = 8, bool F8 = false>
+__global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
+    const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, MxScales mx, int32_t* __restrict__ claim) {
+  constexpr int BK = 64;
+  constexpr int WM = BM / 64, WN = MW / WM;
+  static_assert(WM * WN == MW && WN >= 1, "wave grid");
+  constexpr int TM = 64, TN = BN / WN, FM = 4, FN = TN / 16;
+  constexpr int CH = BK / 8, RPQ = 64 / CH;
+  constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
+  constexpr int SC_BYTES = F8 ? (BM + NB * BN) * 4 : 0;
+  constexpr int STAGE = A_ELEMS + NB * B_ELEMS + SC_BYTES / 2;
+  constexpr int QA = BM / RPQ, QB = BN / RPQ, NQ = QA + NB * QB, NQP = NQ / 2;
+  constexpr int SQA = F8 ? BM / 64 : 0, SQB = F8 ? BN / 64 : 0;
+  constexpr int NSP = (SQA + NB * SQB) / 2;
+  static_assert((SQA + NB * SQB) % 2 == 0, "scale DMAs split over two loader waves");
+  constexpr int NQW = NQP + NSP;  // vector-memory ops per stage per loader wave
+  static_assert(S == 3 && NQW <= 63, "three stages: one stage in flight behind the one landing");
+  constexpr int CAP = wsp_table_cap<F8>();
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
+  __shared__ uint32_t table[CAP];
+  __shared__ int claimed[4];  // chunk index of tile ti of this workgroup at [ti % 4], -1 past the end
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NT = ceil_div(N, BN);
+  const int total = mtile_start[E] * NT;
+  const int per_xcd = ceil_div(total, 8);
+  const int xcd = blockIdx.x & 7;
+  const int lo = xcd * per_xcd, chunk = max(0, min(per_xcd, total - lo));  // chunk <= CAP by wsp_fits
+  if (chunk == 0) return;
+  // the chunk's tiles in logical order (expert-major, then n-tile, then m-tile)
+  for (int e = tid; e < E; e += MW * 64 + 128) {
+    const int mt0 = mtile_start[e], mte = mtile_start[e + 1] - mt0;
+    const int b = max(0, lo - mt0 * NT), f = min(mte * NT, lo + chunk - mt0 * NT);
+    for (int local = b; local < f; ++local) {
+      const int n = local / mte, m = local - n * mte;
+      table[mt0 * NT + local - lo] = (uint32_t)e | ((uint32_t)m << 10) | ((uint32_t)n << 22);
+    }
+  }
+  if (tid == 0) {
+    const int t = atomicAdd(&claim[xcd], 1);
+    claimed[0] = t < chunk ? t : -1;
+  }
+  __syncthreads();
+  if (claimed[0] < 0) return;  // the same value for every wave
+  const int nsteps = K / BK;
+
+  // tile t of the chunk: expert, first row, rows, first column (wave-uniform)
+#define MOE_WSP_COORDS(t, e, r0, rows, n0)                                                     \
+  {                                                                                            \
+    const uint32_t v_ = table[t];                                                              \
+    e = __builtin_amdgcn_readfirstlane((int)(v_ & 1023u));                                     \
+    const int m_ = __builtin_amdgcn_readfirstlane((int)((v_ >> 10) & 4095u));                  \
+    n0 = __builtin_amdgcn_readfirstlane((int)(v_ >> 22)) * BN;                                 \
+    r0 = offsets[e] + m_ * BM;                                                                 \
+    rows = min(BM, offsets[e + 1] - r0);                                                       \
+  }
+
+  if (wave >= MW) {
+    // ---------------- loader waves
+    const int p = wave - MW;
+    const uint16_t* src[NQP];
+    int ldsoff[NQP];
+    const uint8_t* ssrc[NSP > 0 ? NSP : 1];
+    int sldsoff[NSP > 0 ? NSP : 1];
+#define MOE_WSP_SET_TILE(t)                                                                           \
+  {                                                                                                   \
+    int t_e, t_r0, t_rows, t_n0;                                                                      \
+    MOE_WSP_COORDS(t, t_e, t_r0, t_rows, t_n0)                                                        \
+    _Pragma("unroll") for (int j = 0; j < NQP; ++j) {                                                 \
+      const int q = p * NQP + j;                                                                      \
+      if (q < QA) {                                                                                   \
+        const int r = q * RPQ + lane / CH;                                                            \
+        const int cc = (lane % CH) ^ swz<BK>(r);                                                      \
+        src[j] = A + (size_t)(t_r0 + min(r, t_rows - 1)) * K + cc * 8;                                \
+        ldsoff[j] = q * 512;                                                                          \
+      } else {                                                                                        \
+        const int nb = (q - QA) / QB, qq = (q - QA) % QB;                                             \
+        const int r = qq * RPQ + lane / CH;                                                           \
+        const int cc = (lane % CH) ^ swz<BK>(r);                                                      \
+        src[j] = (nb == 0 ? B0 : B1) + ((size_t)t_e * N + min(t_n0 + r, N - 1)) * K + cc * 8;         \
+        ldsoff[j] = A_ELEMS + nb * B_ELEMS + qq * 512;                                                \
+      }                                                                                               \
+    }                                                                                                 \
+    if constexpr (F8) {                                                                               \
+      const int srow = K / 16;                                                                        \
+      _Pragma("unroll") for (int j = 0; j < NSP; ++j) {                                               \
+        const int q = p * NSP + j;                                                                    \
+        if (q < SQA) {                                                                                \
+          const int r = q * 64 + lane;                                                                \
+          ssrc[j] = mx.a + (size_t)(t_r0 + min(r, t_rows - 1)) * srow;                                \
+          sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + q * 256;                                        \
+        } else {                                                                                      \
+          const int nb = (q - SQA) / SQB, qq = (q - SQA) % SQB;                                       \
+          const int r = qq * 64 + lane;                                                               \
+          ssrc[j] = (nb == 0 ? mx.b0 : mx.b1) + ((size_t)t_e * N + min(t_n0 + r, N - 1)) * srow;      \
+          sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + BM * 4 + nb * BN * 4 + qq * 256;                \
+        }                                                                                             \
+      }                                                                                               \
+    }                                                                                                 \
+  }
+#define MOE_WSP_ISSUE(slot)                                                                           \
+  {                                                                                                   \
+    const int base = (slot) * STAGE;                                                                  \
+    _Pragma("unroll") for (int j = 0; j < NQP; ++j)                                                   \
+      __builtin_amdgcn_global_load_lds((gas_ptr)(src[j] + ist * BK), (las_ptr)&lds[base + ldsoff[j]], 16, 0, 0); \
+    if constexpr (F8) {                                                                               \
+      _Pragma("unroll") for (int j = 0; j < NSP; ++j)                                                 \
+        __builtin_amdgcn_global_load_lds((gas_ptr)(ssrc[j] + ist * 4),                                \
+                                         (las_ptr)(reinterpret_cast<uint8_t*>(lds) + base * 2 + sldsoff[j]), 4, 0, 0); \
+    }                                                                                                 \
+    ++ist;                                                                                            \
+  }
+    int it = 0, ist = 0;    // tile (ring index) and K-step of the next stage to issue
+    int fslot = 0;          // its LDS ring slot
+    bool more = true;       // whether tile `it` still has stages to issue
+    bool published = true;  // whether the claim for tile it + 1 is in claimed[]
+    int tnext = 0;          // that claim (loader wave 0, lane 0)
+    MOE_WSP_SET_TILE(claimed[0])
+    if (p == 0 && lane == 0) tnext = atomicAdd(&claim[xcd], 1);
+    published = false;
+    for (int f = 0; f < S - 1; ++f) {  // nsteps >= 3: both stages belong to the first tile
+      MOE_WSP_ISSUE(fslot)
+      fslot = fslot + 1 == S ? 0 : fslot + 1;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQW));  // stage 0 landed
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    for (int ti = 0;; ++ti) {
+      if (claimed[ti & 3] < 0) break;
+      for (int st = 0; st < nsteps; ++st) {
+        // the stage S-1 ahead: this tile's, or the first stages of the next claimed tile
+        if (more && ist == nsteps) {
+          const int tn = claimed[(it + 1) & 3];
+          if (tn >= 0) {
+            ++it;
+            ist = 0;
+            MOE_WSP_SET_TILE(tn)
+            if (p == 0 && lane == 0) tnext = atomicAdd(&claim[xcd], 1);
+            published = false;
+          } else {
+            more = false;
+          }
+        }
+        if (more) {
+          MOE_WSP_ISSUE(fslot)
+          fslot = fslot + 1 == S ? 0 : fslot + 1;
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(NQW));  // the stage consumed next has landed
+        } else {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        }
+        // the claim went out before the last two stages, so the wait above completed it
+        if (p == 0 && !published && ist >= 2) {
+          const int v = __builtin_amdgcn_readfirstlane(tnext);
+          if (lane == 0) claimed[(it + 1) & 3] = v < chunk ? v : -1;
+          published = true;
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
+#undef MOE_WSP_ISSUE
+#undef MOE_WSP_SET_TILE
+    return;
+  }
+
+  // ---------------- MFMA waves
+  const int wm = wave / WN, wn = wave % WN;
+  f32x4 acc[NB][FM][FN];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[nb][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int aoffs[2][FM], boffs[2][FN];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = h * 4 + (lane >> 4);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = wm * TM + fm * 16 + (lane & 15);
+      aoffs[h][fm] = r * BK + ((c ^ swz<BK>(r)) << 3);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int r = wn * TN + fn * 16 + (lane & 15);
+      boffs[h][fn] = A_ELEMS + r * BK + ((c ^ swz<BK>(r)) << 3);
+    }
+  }
+  struct Ops {
+    bf16x8 a[FM];
+    bf16x8 b[NB][FN];
+  };
+  constexpr int NR = FM + NB * FN, NM = NB * FN * FM;
+  auto rd = [&](Ops& o, const uint16_t* base, int h) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) o.a[fm] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoffs[h][fm]));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        o.b[nb][fn] = as_bf16x8(*reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[h][fn]));
+  };
+  auto mma = [&](const Ops& o) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+          acc[nb][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.a[fm], o.b[nb][fn], acc[nb][fm][fn], 0, 0, 0);
+  };
+  auto interleave = [] {
+#pragma unroll
+    for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+  };
+  // this wave's reads of the current stage are done; the loaders' next stage has landed
+  auto barrier = [] {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto f8_step = [&](const uint16_t* base) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    constexpr int SCB = (A_ELEMS + NB * B_ELEMS) * 2;
+    const int g = lane >> 4;
+    const uint8_t* base8 = reinterpret_cast<const uint8_t*>(base);
+    u32x4 a0[FM], a1[FM], b0[NB][FN], b1[NB][FN];
+    int sa[FM], sb[NB][FN];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        b0[nb][fn] = *reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[0][fn]);
+        b1[nb][fn] = *reinterpret_cast<const u32x4*>(base + nb * B_ELEMS + boffs[1][fn]);
+        sb[nb][fn] = base8[SCB + BM * 4 + nb * BN * 4 + (wn * TN + fn * 16 + (lane & 15)) * 4 + g];
+      }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) sa[fm] = base8[SCB + (wm * TM + fm * 16 + (lane & 15)) * 4 + g];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      a0[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[0][fm]);
+      a1[fm] = *reinterpret_cast<const u32x4*>(base + aoffs[1][fm]);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0[fm], a1[fm], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b0[nb][fn], b1[nb][fn], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[nb][fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[nb][fm][fn], 0, 0, 0,
+                                                                             sa[fm], 0, sb[nb][fn]);
+        }
+    }
+  };
+
+  Ops o0, o1;
+  barrier();  // stage 0 has landed
+  int cs = 0;  // ring slot of the stage the next K-step consumes
+  auto next_slot = [](int x) { return x + 1 == S ? 0 : x + 1; };
+  for (int ti = 0;; ++ti) {
+    const int t = __builtin_amdgcn_readfirstlane(claimed[ti & 3]);
+    if (t < 0) break;
+    int t_e, t_r0, t_rows, t_n0;
+    MOE_WSP_COORDS(t, t_e, t_r0, t_rows, t_n0)
+    (void)t_e;
+    if (wm * TM >= t_rows) {  // no valid rows for this wave: keep the barrier cadence
+      for (int st = 0; st < nsteps; ++st) {
+        barrier();
+        cs = next_slot(cs);
+      }
+      continue;
+    }
+    if constexpr (F8) {
+      for (int st = 0; st < nsteps; ++st) {
+        f8_step(lds + cs * STAGE);
+        barrier();
+        cs = next_slot(cs);
+      }
+    } else {
+      // operands double-buffered in registers: the next 32-wide substep's LDS reads
+      // are interleaved with the current substep's MFMAs
+      rd(o0, lds + cs * STAGE, 0);
+      for (int st = 0; st < nsteps - 1; ++st) {
+        rd(o1, lds + cs * STAGE, 1);
+        mma(o0);
+        interleave();
+        barrier();
+        cs = next_slot(cs);
+        rd(o0, lds + cs * STAGE, 0);
+        mma(o1);
+        interleave();
+      }
+      rd(o1, lds + cs * STAGE, 1);
+      mma(o0);
+      interleave();
+      barrier();
+      cs = next_slot(cs);
+      mma(o1);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = wm * TM + fm * 16 + (lane >> 4) * 4 + i;
+          const int c = t_n0 + wn * TN + fn * 16 + (lane & 15);
+          if (r < t_rows && c < N)
+            epi_store<EPI>(C, (size_t)(t_r0 + r) * N + c, acc[0][fm][fn][i],
+                           NB > 1 ? acc[NB - 1][fm][fn][i] : 0.f, nullptr, c);
+          acc[0][fm][fn][i] = 0.f;
+          if constexpr (NB > 1) acc[NB - 1][fm][fn][i] = 0.f;
+        }
+  }
+#undef MOE_WSP_COORDS
+}
+
 // ------------------------------------------------------------------ decode kernel
 // For experts with a handful of rows: 16-row m-tiles, no LDS, every wave
 // streams its own 16*FN weight rows straight from HBM with two K-steps of loads
@@ -797,8 +1171,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
   if (kind == GEMM_PREFILL) {
     // Kernel per GEMM, measured on MI355X with the real per-expert row counts of the
     // Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped and latent layers (one box, one run):
-    //  - expert gate/up: wave-specialised LDS-DMA kernel, 128 x 128 tiles, 8 MFMA
-    //    waves (best or within 1 % on all three);
+    //  - expert gate/up: the persistent wave-specialised LDS-DMA kernel, 128 x 128
+    //    tiles, 8 MFMA waves (against one workgroup per tile: Qwen3-shaped 303 -> 271 us,
+    //    R1-shaped 4.66 -> 4.45 ms, latent equal; against 256-row tiles with every wave
+    //    loading, faster on both of the first two);
     //  - expert down: register-staged tile kernel at three waves per SIMD, or (K >= 2048,
     //    measured in the whole layer) the wave-specialised kernel with 256 x 128 tiles;
     //  - dense latent projections (one group): wave-specialised kernel with
@@ -817,10 +1193,21 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
     }
     const int g = grid_for(max_mtiles(M, E, 128), N, 128);
     if (swiglu) {
-      // with 16 or more n-tiles per expert, n-tiles run in pairs so the two tiles
-      // reading one m-tile's rows are adjacent (DeepSeek-R1- and latent-shaped
-      // layers); with fewer, plain n-major order measured faster (Qwen3-shaped)
-      const dim3 gb(g), bb(8 * 64 + 128);
+      const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
+      const dim3 bb(8 * 64 + 128);
+      if (wsp_fits<false>(tiles, E, N, K)) {
+        // persistent wave-specialised kernel (256 workgroups, one per CU)
+        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
+        if (epi == EPI_SWIGLU_BF16)
+          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
+                             C, offsets, mtile_start, E, N, K, MxScales{}, claim);
+        else
+          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
+                             C, offsets, mtile_start, E, N, K, MxScales{}, claim);
+        return hipGetLastError();
+      }
+      // one workgroup per tile; n-tiles in pairs when there are 16 or more of them
+      const dim3 gb(g);
       const bool pairs = ceil_div(N, 128) >= 16;
       if (epi == EPI_SWIGLU_BF16) {
         if (pairs)
@@ -919,13 +1306,21 @@ hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const u
   const int K = D / 2;  // codes travel as 16-bit pairs
   if (kind == GEMM_PREFILL) {
     if (gather) return hipErrorInvalidValue;
-    const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128)), bb(8 * 64 + 128);
-    if (ceil_div(N, 128) >= 16)
-      hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2, true>), gb, bb, 0, st, a, M,
-                         b0, b1, C, offsets, mtile_start, E, N, K, mx);
-    else
-      hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 1, true>), gb, bb, 0, st, a, M,
-                         b0, b1, C, offsets, mtile_start, E, N, K, mx);
+    const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
+    const dim3 bb(8 * 64 + 128);
+    if (wsp_fits<true>(tiles, E, N, K)) {
+      int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
+      hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, true>), dim3(256), bb, 0, st, a, M, b0, b1,
+                         C, offsets, mtile_start, E, N, K, mx, claim);
+    } else {
+      const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128));
+      if (ceil_div(N, 128) >= 16)
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2, true>), gb, bb, 0, st, a, M,
+                           b0, b1, C, offsets, mtile_start, E, N, K, mx);
+      else
+        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 1, true>), gb, bb, 0, st, a, M,
+                           b0, b1, C, offsets, mtile_start, E, N, K, mx);
+    }
   } else {
     const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
     hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16, true>), dim3(g), dim3(256), 0, st, a, M, b0, b1,

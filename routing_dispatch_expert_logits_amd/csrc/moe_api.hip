@@ -89,7 +89,7 @@ RouteWs route_ws(const Dims& d, bool with_gate) {
 struct FfnWs { size_t mtile, act, total; };
 FfnWs ffn_ws(const Dims& d) {
   Carve c; FfnWs w;
-  w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
+  w.mtile = c.take(mtile_table_bytes(d.E));  // tables for two tile heights + claim counters
   w.act = c.take((size_t)d.R * d.I * d.es);
   w.total = c.cur;
   return w;
@@ -118,7 +118,7 @@ LayerWs layer_ws(const Dims& d) {
   w.token_row = c.take((size_t)d.R * 4);
   w.bc = c.take((size_t)d.nb * d.E * 4);
   w.gpart = c.take(gate_partial_bytes(d));
-  w.mtile = c.take((size_t)(d.E + 1) * 2 * 4);  // tables for two tile heights
+  w.mtile = c.take(mtile_table_bytes(d.E));  // tables for two tile heights + claim counters
   w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   w.xperm = c.take((size_t)d.R * d.D * d.es);  // later reused for y_perm
   w.xs = c.take(d.mx ? (size_t)d.R * (d.D / kMxBlock) : 0);  // MXFP8 scales of x_perm
@@ -129,7 +129,7 @@ LayerWs layer_ws(const Dims& d) {
   w.outl = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
   // shared expert: one group of T rows
   w.soffs = c.take(d.Is ? 2 * 4 : 0);
-  w.smtile = c.take(d.Is ? 2 * 2 * 4 : 0);
+  w.smtile = c.take(d.Is ? mtile_table_bytes(1) : 0);
   w.sact = c.take((size_t)d.T * d.Is * d.es);
   w.sy = c.take(d.Is ? (size_t)d.T * d.H * d.es : 0);
   w.total = c.cur;

@@ -245,6 +245,7 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
       if (t < E) tab[t] = st;
       if (t == E - 1) tab[E] = st + mt;
     }
+    if (t < kClaimSlots) mtile_start[2 * (E + 1) + t] = 0;
   }
 }
 
@@ -305,6 +306,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
       if (tid < E) tab[tid] = st;
       if (tid == E - 1) tab[E] = st + mt;
     }
+    if (tid < kClaimSlots) mtile_start[2 * (E + 1) + tid] = 0;
   }
   __syncthreads();
   for (int a = tid; a < T * k; a += 1024) {
@@ -322,6 +324,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
 // One group of T rows (the shared expert's GEMMs run as a single expert).
 __global__ void k_single_group(int T, int32_t* __restrict__ offsets, int bm,
                                int32_t* __restrict__ mtile_start) {
+  if (threadIdx.x < kClaimSlots) mtile_start[4 + threadIdx.x] = 0;
   if (threadIdx.x != 0) return;
   offsets[0] = 0;
   offsets[1] = T;

@@ -44,8 +44,8 @@ def test_stage_bytes_follow_kept_rows():
 
 
 def test_kernel_labels():
-    assert "k_gemm_ws<128,128,2,SwiGLU,3,8>" in bench.gate_up_kernel(FULL_CONFIGS["qwen3_30b_a3b_shaped"])
-    assert ",64,2>" in bench.gate_up_kernel(FULL_CONFIGS["deepseek_r1_shaped"])      # paired n-tiles
+    assert "k_gemm_wsp<128,128,2,SwiGLU,3,8>" in bench.gate_up_kernel(FULL_CONFIGS["qwen3_30b_a3b_shaped"])
+    assert "k_gemm_wsp<128,128,2,SwiGLU,3,8>" in bench.gate_up_kernel(FULL_CONFIGS["deepseek_r1_shaped"])
     assert "k_gemm_decode" in bench.gate_up_kernel(FULL_CONFIGS["k3_shaped_decode"])
     assert "MXFP8" in bench.gate_up_kernel(FULL_CONFIGS["qwen3_30b_a3b_shaped"].with_(dispatch="mxfp8"))
     assert "simt" in bench.gate_up_kernel(FULL_CONFIGS["tiny_f32"])
