@@ -1176,7 +1176,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
     //    R1-shaped 4.66 -> 4.45 ms, latent equal; against 256-row tiles with every wave
     //    loading, faster on both of the first two);
     //  - expert down: register-staged tile kernel at three waves per SIMD, or (K >= 2048,
-    //    measured in the whole layer) the wave-specialised kernel with 256 x 128 tiles;
+    //    measured in the whole layer) the persistent wave-specialised kernel with
+    //    256 x 128 tiles (R1-shaped 2.61 -> 2.46 ms against one workgroup per tile,
+    //    latent-shaped equal; on the Qwen3-shaped down GEMM, K = 768, it took 220 us
+    //    against the register-staged kernel's 196 us);
     //  - dense latent projections (one group): wave-specialised kernel with
     //    256 x 128 tiles (one tile row per 256 tokens fills 256 CUs in one pass).
     if (!offsets) {
@@ -1227,8 +1230,20 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       return hipGetLastError();
     }
     if (K >= 2048) {  // down GEMM with a long K: 256-row tiles (second m-tile table)
-      const dim3 gb(grid_for(max_mtiles(M, E, 256), N, 128)), bb(8 * 64 + 128);
       const int32_t* mt256 = mtile_start + E + 1;
+      const long tiles = (long)max_mtiles(M, E, 256) * ceil_div(N, 128);
+      const dim3 bb(8 * 64 + 128);
+      if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
+        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
+        if (epi == EPI_BF16)
+          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
+                             offsets, mt256, E, N, K, MxScales{}, claim);
+        else
+          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
+                             offsets, mt256, E, N, K, MxScales{}, claim);
+        return hipGetLastError();
+      }
+      const dim3 gb(grid_for(max_mtiles(M, E, 256), N, 128));
       if (epi == EPI_BF16)
         hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
                            offsets, mt256, E, N, K, MxScales{});

@@ -19,9 +19,10 @@ enum Epi {
 enum GemmKind { GEMM_PREFILL = 0, GEMM_DECODE = 1, GEMM_SIMT = 2 };
 
 // An m-tile table buffer holds the tables for two tile heights, (E + 1) ints each,
-// followed by kClaimSlots tile-claim counters of the persistent expert GEMM (one per
-// XCD), which the kernels that write the tables set to zero.
-constexpr int kClaimSlots = 8;
+// followed by kClaimSlots tile-claim counters of the persistent expert GEMMs (one per
+// XCD for the gate/up GEMM, then one per XCD for the down GEMM), which the kernels
+// that write the tables set to zero.
+constexpr int kClaimSlots = 16;
 inline size_t mtile_table_bytes(int E) { return ((size_t)(E + 1) * 2 + kClaimSlots) * 4; }
 
 // E8M0 scale arrays of MXFP8 GEMM operands ([rows x K/32] bytes; NULL for bf16 GEMMs).
