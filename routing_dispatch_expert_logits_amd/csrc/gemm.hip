@@ -568,15 +568,17 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 
 // ------------------------------------------------------------------ persistent variant
 // k_gemm_wsp: the wave-specialised kernel as a persistent kernel for the expert
-// gate/up GEMMs.  One workgroup per CU; workgroup i runs on XCD i % 8 and takes the
-// tiles of that XCD's contiguous chunk of logical tiles one at a time, in order, from
-// the chunk's claim counter (claim[i % 8], an agent-scope atomic).  So the 32 CUs of
-// an XCD work through its chunk in the order the hardware would have dispatched
+// GEMMs.  One workgroup per CU; workgroup i runs on XCD i % 8 and takes the tiles
+// of that XCD's contiguous chunk of logical tiles one at a time, in order, from the
+// chunk's claim counter (claim[i % 8], an agent-scope atomic).  So the 32 CUs of an
+// XCD work through its chunk in the order the hardware would have dispatched
 // one-tile workgroups (the tiles sharing an expert's weights run together), a CU
 // that runs slow simply takes fewer tiles, and there is no per-tile dispatch, launch
 // or pipeline fill: the loader waves run ahead across tile boundaries, so the next
 // tile's first stages are in flight while the MFMA waves store the previous one.
-// Each workgroup decodes its XCD's chunk once into an LDS table.  Tiles, K-steps,
+// Each workgroup decodes the tile coordinates once into an LDS table: every tile
+// when they fit, and then a workgroup whose chunk is done takes tiles left in
+// other XCDs' chunks; else its own chunk.  Tiles, K-steps,
 // LDS layout and MFMA order are those of k_gemm_ws, so the results are the same
 // bits.  The claim counters must be zero at launch: the m-tile table kernels
 // (k_offsets, k_route_small, k_single_group) clear them.
@@ -618,7 +620,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
   constexpr int CAP = wsp_table_cap<F8>();
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
   __shared__ uint32_t table[CAP];
-  __shared__ int claimed[4];  // chunk index of tile ti of this workgroup at [ti % 4], -1 past the end
+  __shared__ int claimed[4];  // logical index of tile ti of this workgroup at [ti % 4], -1 past the end
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NT = ceil_div(N, BN);
@@ -626,28 +628,67 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
   const int per_xcd = ceil_div(total, 8);
   const int xcd = blockIdx.x & 7;
   const int lo = xcd * per_xcd, chunk = max(0, min(per_xcd, total - lo));  // chunk <= CAP by wsp_fits
-  if (chunk == 0) return;
-  // the chunk's tiles in logical order (expert-major, then n-tile, then m-tile)
+  if (total == 0) return;
+  // With every tile in the table, a workgroup whose XCD chunk is done takes tiles
+  // from the chunk with the most left (the XCDs finish a few percent apart);
+  // otherwise the table holds this XCD's chunk only.
+  const bool all = total <= CAP;
+  const int tlo = all ? 0 : lo, tcount = all ? total : chunk;
+  // table[L - tlo] for logical tile L in logical order (expert-major, then n-tile, then m-tile)
   for (int e = tid; e < E; e += MW * 64 + 128) {
     const int mt0 = mtile_start[e], mte = mtile_start[e + 1] - mt0;
-    const int b = max(0, lo - mt0 * NT), f = min(mte * NT, lo + chunk - mt0 * NT);
+    const int b = max(0, tlo - mt0 * NT), f = min(mte * NT, tlo + tcount - mt0 * NT);
     for (int local = b; local < f; ++local) {
       const int n = local / mte, m = local - n * mte;
-      table[mt0 * NT + local - lo] = (uint32_t)e | ((uint32_t)m << 10) | ((uint32_t)n << 22);
+      table[mt0 * NT + local - tlo] = (uint32_t)e | ((uint32_t)m << 10) | ((uint32_t)n << 22);
     }
   }
-  if (tid == 0) {
-    const int t = atomicAdd(&claim[xcd], 1);
-    claimed[0] = t < chunk ? t : -1;
+  // The logical tile for a claim `own` made on this XCD's counter, or -1 when no tile is
+  // left.  Run by a whole wave.  Each failed steal meets a counter already past its
+  // chunk, which every later agent-scope load of it shows, so the loop ends after at
+  // most 9 rounds.
+  auto take = [&](int own) -> int {
+    if (own < chunk) return lo + own;
+    if (!all) return -1;
+    for (int round = 0; round < 16; ++round) {
+      int left = -1;
+      if (lane < 8) {
+        const int c = __hip_atomic_load(&claim[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        left = max(0, min(per_xcd, total - lane * per_xcd)) - c;
+      }
+      int best = left, who = lane;
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const int l2 = __shfl_xor(best, o), w2 = __shfl_xor(who, o);
+        if (l2 > best || (l2 == best && w2 < who)) {
+          best = l2;
+          who = w2;
+        }
+      }
+      best = __builtin_amdgcn_readfirstlane(best);
+      who = __builtin_amdgcn_readfirstlane(who);
+      if (best <= 0) return -1;
+      int t = 0;
+      if (lane == 0) t = atomicAdd(&claim[who], 1);
+      t = __builtin_amdgcn_readfirstlane(t);
+      if (t < max(0, min(per_xcd, total - who * per_xcd))) return who * per_xcd + t;
+    }
+    return -1;
+  };
+  if (wave == 0) {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(&claim[xcd], 1);
+    const int L = take(__builtin_amdgcn_readfirstlane(t));
+    if (lane == 0) claimed[0] = L;
   }
   __syncthreads();
   if (claimed[0] < 0) return;  // the same value for every wave
   const int nsteps = K / BK;
 
-  // tile t of the chunk: expert, first row, rows, first column (wave-uniform)
-#define MOE_WSP_COORDS(t, e, r0, rows, n0)                                                     \
+  // logical tile L: expert, first row, rows, first column (wave-uniform)
+#define MOE_WSP_COORDS(L, e, r0, rows, n0)                                                     \
   {                                                                                            \
-    const uint32_t v_ = table[t];                                                              \
+    const uint32_t v_ = table[(L) - tlo];                                                      \
     e = __builtin_amdgcn_readfirstlane((int)(v_ & 1023u));                                     \
     const int m_ = __builtin_amdgcn_readfirstlane((int)((v_ >> 10) & 4095u));                  \
     n0 = __builtin_amdgcn_readfirstlane((int)(v_ >> 22)) * BN;                                 \
@@ -750,8 +791,8 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
         }
         // the claim went out before the last two stages, so the wait above completed it
         if (p == 0 && !published && ist >= 2) {
-          const int v = __builtin_amdgcn_readfirstlane(tnext);
-          if (lane == 0) claimed[(it + 1) & 3] = v < chunk ? v : -1;
+          const int L = take(__builtin_amdgcn_readfirstlane(tnext));
+          if (lane == 0) claimed[(it + 1) & 3] = L;
           published = true;
         }
         __builtin_amdgcn_s_barrier();
