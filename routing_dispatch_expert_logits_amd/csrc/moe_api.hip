@@ -416,7 +416,8 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   uint8_t* xs = d.mx ? static_cast<uint8_t*>(pick(ax.x_perm_scale, w.xs)) : nullptr;
 
   auto ev = [&](int i) -> bool {
-    return !stage_events || hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
+    return !stage_events || !stage_events[i] ||
+           hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
   };
   const GemmKind kind = expert_kind(d);
 

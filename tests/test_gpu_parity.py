@@ -396,6 +396,37 @@ def test_layer_matches_separate_calls_and_is_deterministic(name):
     np.testing.assert_array_equal(offs, a["offsets"])
 
 
+def test_stage_events_skip_null_entries():
+    """A stage-event array may leave entries NULL: only the others are recorded, and the
+    layer's results do not depend on which are."""
+    from bench import HipEvents
+    cfg = PARITY_CONFIGS["small_bf16_zipf"]
+    inp = gen.layer_inputs(cfg)
+    s = shape_of(cfg)
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2")}
+    x = dev(inp["x"])
+    outs = []
+    hip = HipEvents()
+    full = hip.create(B.MOE_NUM_STAGE_EVENTS)
+    pair = hip.create(2)
+    g = B.STAGE_NAMES.index("gemm_gate_up")
+    some = [None] * B.MOE_NUM_STAGE_EVENTS
+    some[g], some[g + 1] = pair
+    stream = torch.cuda.current_stream().cuda_stream
+    for evs in (None, full, some):
+        logits = empty((cfg.T, cfg.E), "f32")
+        out = empty((cfg.T, cfg.H), "f32")
+        B.layer_forward(w, x, logits, out, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER), stage_events=evs, stream=stream)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    np.testing.assert_array_equal(outs[0], outs[2])
+    assert hip.elapsed_ms(pair[0], pair[1]) > 0
+    assert hip.elapsed_ms(full[0], full[-1]) >= hip.elapsed_ms(full[g], full[g + 1]) > 0
+    hip.destroy(full)
+    hip.destroy(pair)
+
+
 @pytest.mark.parametrize("name", ["shared_expert", "shared_expert_decode", "shared_expert_f32",
                                   "small_bf16_decode", "single_token", "many_empty",
                                   "capacity_prefill", "capacity_decode", "capacity_f32"])
