@@ -54,11 +54,17 @@ def log(msg):
 
 
 class HipEvents:
-    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded.
+
+    The events are timing-only: created with hipEventDisableSystemFence, so recording
+    one does not write back and invalidate the caches (which slows the kernel that
+    follows); every read of them comes after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -68,8 +74,8 @@ class HipEvents:
         evs = []
         for _ in range(n):
             h = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(h))
-            assert rc == 0, f"hipEventCreate failed: {rc}"
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+            assert rc == 0, f"hipEventCreateWithFlags failed: {rc}"
             evs.append(h.value)
         return evs
 
@@ -442,9 +448,8 @@ def main(argv=None):
     names = B.STAGE_NAMES
     # The timed steps record only the two events around the expert gate/up GEMM (the
     # dominant kernel the roofline object describes): every event record puts a few
-    # microseconds between the kernels either side of it, nine of them about 35 us per
-    # Qwen3-shaped layer.  The per-stage breakdown comes from a separate pass with
-    # every stage event, after the timed region.
+    # microseconds between the kernels either side of it.  The per-stage breakdown comes
+    # from a separate pass with every stage event, after the timed region.
     g = names.index("gemm_gate_up")
     gev = [hip.create(2) for _ in range(args.steps)]
     tev = []
