@@ -24,8 +24,12 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
+# -amdgpu-atomic-optimizer-strategy=None: the optimizer turns a one-lane atomic with a
+# uniform address (the persistent GEMM's tile claim) into a combine that waits for the
+# result at once, which drains the claiming loader wave's LDS DMA stages.
 DEVICE_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                 "-Wall", "-Wno-unused-function", "-fvisibility=hidden",
                 "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

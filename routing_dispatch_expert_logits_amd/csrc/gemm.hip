@@ -602,7 +602,8 @@ template <int BM, int BN, int NB, int EPI, int S, int MW = 8, bool F8 = false>
 __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ mtile_start, int E, int N, int K, MxScales mx, int32_t* __restrict__ claim) {
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, MxScales mx, int32_t* __restrict__ claim,
+    const int32_t* __restrict__ gather) {
   constexpr int BK = 64;
   constexpr int WM = BM / 64, WN = MW / WM;
   static_assert(WM * WN == MW && WN >= 1, "wave grid");
@@ -703,6 +704,27 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     int ldsoff[NQP];
     const uint8_t* ssrc[NSP > 0 ? NSP : 1];
     int sldsoff[NSP > 0 ? NSP : 1];
+    // gathered A rows (gather != NULL): the token row of each row this wave loads, for
+    // the tile set up next; read one K-step before it is needed, ahead of that step's
+    // DMAs, so the step's own vmcnt wait completes the loads
+    int gidx[NQP], sgidx[NSP > 0 ? NSP : 1];
+#define MOE_WSP_GATHER(t)                                                                             \
+  {                                                                                                   \
+    int g_e, g_r0, g_rows, g_n0;                                                                      \
+    MOE_WSP_COORDS(t, g_e, g_r0, g_rows, g_n0)                                                        \
+    (void)g_e;                                                                                        \
+    (void)g_n0;                                                                                       \
+    _Pragma("unroll") for (int j = 0; j < NQP; ++j) {                                                 \
+      const int q = p * NQP + j;                                                                      \
+      if (q < QA) gidx[j] = gather[g_r0 + min(q * RPQ + lane / CH, g_rows - 1)];                      \
+    }                                                                                                 \
+    if constexpr (F8) {                                                                               \
+      _Pragma("unroll") for (int j = 0; j < NSP; ++j) {                                               \
+        const int q = p * NSP + j;                                                                    \
+        if (q < SQA) sgidx[j] = gather[g_r0 + min(q * 64 + lane, g_rows - 1)];                        \
+      }                                                                                               \
+    }                                                                                                 \
+  }
 #define MOE_WSP_SET_TILE(t)                                                                           \
   {                                                                                                   \
     int t_e, t_r0, t_rows, t_n0;                                                                      \
@@ -712,7 +734,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
       if (q < QA) {                                                                                   \
         const int r = q * RPQ + lane / CH;                                                            \
         const int cc = (lane % CH) ^ swz<BK>(r);                                                      \
-        src[j] = A + (size_t)(t_r0 + min(r, t_rows - 1)) * K + cc * 8;                                \
+        src[j] = A + (size_t)(gather ? gidx[j] : t_r0 + min(r, t_rows - 1)) * K + cc * 8;             \
         ldsoff[j] = q * 512;                                                                          \
       } else {                                                                                        \
         const int nb = (q - QA) / QB, qq = (q - QA) % QB;                                             \
@@ -728,7 +750,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
         const int q = p * NSP + j;                                                                    \
         if (q < SQA) {                                                                                \
           const int r = q * 64 + lane;                                                                \
-          ssrc[j] = mx.a + (size_t)(t_r0 + min(r, t_rows - 1)) * srow;                                \
+          ssrc[j] = mx.a + (size_t)(gather ? sgidx[j] : t_r0 + min(r, t_rows - 1)) * srow;            \
           sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + q * 256;                                        \
         } else {                                                                                      \
           const int nb = (q - SQA) / SQB, qq = (q - SQA) % SQB;                                       \
@@ -756,6 +778,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     bool more = true;       // whether tile `it` still has stages to issue
     bool published = true;  // whether the claim for tile it + 1 is in claimed[]
     int tnext = 0;          // that claim (loader wave 0, lane 0)
+    if (gather) MOE_WSP_GATHER(claimed[0])
     MOE_WSP_SET_TILE(claimed[0])
     if (p == 0 && lane == 0) tnext = atomicAdd(&claim[xcd], 1);
     published = false;
@@ -769,6 +792,12 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     for (int ti = 0;; ++ti) {
       if (claimed[ti & 3] < 0) break;
       for (int st = 0; st < nsteps; ++st) {
+        // next tile's token rows, one step before its first stage (nsteps >= 4: the claim
+        // was published at least one barrier earlier)
+        if (gather && more && ist == nsteps - 1) {
+          const int tg = claimed[(it + 1) & 3];
+          if (tg >= 0) MOE_WSP_GATHER(tg)
+        }
         // the stage S-1 ahead: this tile's, or the first stages of the next claimed tile
         if (more && ist == nsteps) {
           const int tn = claimed[(it + 1) & 3];
@@ -801,6 +830,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     }
 #undef MOE_WSP_ISSUE
 #undef MOE_WSP_SET_TILE
+#undef MOE_WSP_GATHER
     return;
   }
 
@@ -1205,6 +1235,29 @@ int max_mtiles(int M, int E, int bm) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K, \
                      static_cast<const int32_t*>(nullptr), MxScales{})
 
+bool gemm_gather_ok(int M, int E, int N, int K, bool mx) {
+  const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
+  return (mx ? wsp_fits<true>(tiles, E, N, K) : wsp_fits<false>(tiles, E, N, K)) && K / 64 >= 4;
+}
+
+hipError_t launch_gemm_prefill_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
+                                      const uint16_t* B0, const uint16_t* B1, void* C,
+                                      const int32_t* offsets, const int32_t* mtile_start, int E, int N,
+                                      int K, hipStream_t st) {
+  if (!gather || !gemm_gather_ok(M, E, N, K, false)) return hipErrorInvalidValue;
+  int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
+  const dim3 bb(8 * 64 + 128);
+  if (epi == EPI_SWIGLU_BF16)
+    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), bb, 0, st, X, M, B0, B1, C,
+                       offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
+  else if (epi == EPI_SWIGLU_F32)
+    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), bb, 0, st, X, M, B0, B1, C,
+                       offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, const uint16_t* B0,
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st) {
@@ -1244,10 +1297,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
         int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
         if (epi == EPI_SWIGLU_BF16)
           hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
-                             C, offsets, mtile_start, E, N, K, MxScales{}, claim);
+                             C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
         else
           hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
-                             C, offsets, mtile_start, E, N, K, MxScales{}, claim);
+                             C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
         return hipGetLastError();
       }
       // one workgroup per tile; n-tiles in pairs when there are 16 or more of them
@@ -1278,10 +1331,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
         int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
         if (epi == EPI_BF16)
           hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
-                             offsets, mt256, E, N, K, MxScales{}, claim);
+                             offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
         else
           hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
-                             offsets, mt256, E, N, K, MxScales{}, claim);
+                             offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
         return hipGetLastError();
       }
       const dim3 gb(grid_for(max_mtiles(M, E, 256), N, 128));
@@ -1361,13 +1414,13 @@ hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const u
   const uint16_t* b1 = reinterpret_cast<const uint16_t*>(B1);
   const int K = D / 2;  // codes travel as 16-bit pairs
   if (kind == GEMM_PREFILL) {
-    if (gather) return hipErrorInvalidValue;
     const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
     const dim3 bb(8 * 64 + 128);
+    if (gather && !gemm_gather_ok(M, E, N, K, true)) return hipErrorInvalidValue;
     if (wsp_fits<true>(tiles, E, N, K)) {
       int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
       hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, true>), dim3(256), bb, 0, st, a, M, b0, b1,
-                         C, offsets, mtile_start, E, N, K, mx, claim);
+                         C, offsets, mtile_start, E, N, K, mx, claim, gather);
     } else {
       const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128));
       if (ceil_div(N, 128) >= 16)

@@ -442,6 +442,15 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   // quantised once and read the same way; a caller who asks for the permuted codes
   // gets the general path.
   const bool small = kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (ax.x_perm || ax.x_perm_scale));
+  // Larger steps: unless the caller asks for the permuted rows, the permutation writes
+  // only the row metadata and the gate/up GEMM reads the token rows through row_token
+  // (decode-sized tiles always can; the persistent prefill kernel when its tile table
+  // fits).  The GEMM sees the same rows in the same order, so the results are the same
+  // bits as with the permuted copy.
+  const bool gath = !small && d.bf16 && !ax.x_perm && !(d.mx && ax.x_perm_scale) &&
+                    (kind == GEMM_DECODE ||
+                     (kind == GEMM_PREFILL && gemm_gather_ok(d.R, d.E, d.I, d.mx ? d.D / 2 : d.D, d.mx)));
+  const bool rows_from_tokens = small || gath;
   uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
   uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;
   if (small) {
@@ -460,25 +469,36 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
     // a4
-    MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, xs, rtok, trow, st));
+    if (gath) {
+      if (d.mx) MOE_HIP(launch_mx_quantize(src, true, d.T, d.D, xq, xqs, st));  // token rows, once
+      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, nullptr, nullptr, rtok, trow, st));
+    } else {
+      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, xs, rtok, trow, st));
+    }
   }
   if (!ev(4)) return MOE_ERR_HIP;
   // a5
   if (d.mx) {
-    const MxScales mx{small ? xqs : xs, wt->w1_scale, wt->w3_scale};
-    MOE_HIP(launch_gemm_mx_swiglu(kind, static_cast<const uint8_t*>(small ? xq : xperm), d.R,
+    const MxScales mx{rows_from_tokens ? xqs : xs, wt->w1_scale, wt->w3_scale};
+    MOE_HIP(launch_gemm_mx_swiglu(kind, static_cast<const uint8_t*>(rows_from_tokens ? xq : xperm), d.R,
                                   static_cast<const uint8_t*>(wt->w1), static_cast<const uint8_t*>(wt->w3),
                                   static_cast<uint16_t*>(act), offs, mtile, d.E, d.I, d.D, mx,
-                                  small ? rtok : nullptr, st));
+                                  rows_from_tokens ? rtok : nullptr, st));
     if (!ev(5)) return MOE_ERR_HIP;
     MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
                              static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
                              d.E, d.D, d.I, st));
-  } else if (small) {
-    MOE_HIP(launch_gemm_decode_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
-                                      static_cast<const uint16_t*>(wt->w1),
-                                      static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,
-                                      d.D, st));
+  } else if (rows_from_tokens) {
+    if (kind == GEMM_DECODE)
+      MOE_HIP(launch_gemm_decode_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
+                                        static_cast<const uint16_t*>(wt->w1),
+                                        static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,
+                                        d.D, st));
+    else
+      MOE_HIP(launch_gemm_prefill_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
+                                         static_cast<const uint16_t*>(wt->w1),
+                                         static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,
+                                         d.D, st));
     if (!ev(5)) return MOE_ERR_HIP;
     MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
                              static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,

@@ -69,7 +69,8 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
 hipError_t launch_mx_quantize(const void* src, bool src_bf16, long rows, long cols, uint8_t* q,
                               uint8_t* scale, hipStream_t st);
 // Expert gate/up GEMM on MXFP8 rows and weights (D % 128 == 0), bf16 SwiGLU output;
-// GEMM_DECODE may read its rows through gather (as launch_gemm_decode_gather).
+// GEMM_DECODE may read its rows through gather (as launch_gemm_decode_gather), and so
+// may GEMM_PREFILL when gemm_gather_ok(M, E, N, D / 2, true).
 hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const uint8_t* B0, const uint8_t* B1,
                                  uint16_t* C, const int32_t* offsets, const int32_t* mtile_start, int E,
                                  int N, int D, MxScales mx, const int32_t* gather, hipStream_t st);
@@ -91,6 +92,16 @@ hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t*
                              hipStream_t st);
 // Decode GEMM whose A rows are read through an index: row r of the operand is X[gather[r]]
 // (the expert gate/up GEMM reading the token rows directly instead of a permuted copy).
+// Whether the persistent prefill gate/up GEMM can read its rows through a gather
+// index (row r of the grouped GEMM = row gather[r] of X): the tile table fits and K
+// (16-bit columns; MXFP8 codes count in pairs) has at least 4 K-steps.
+bool gemm_gather_ok(int M, int E, int N, int K, bool mx);
+// Prefill gate/up GEMM (SwiGLU epilogue) on rows gathered from X through `gather`
+// (row_token); requires gemm_gather_ok(M, E, N, K, false).
+hipError_t launch_gemm_prefill_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
+                                      const uint16_t* B0, const uint16_t* B1, void* C,
+                                      const int32_t* offsets, const int32_t* mtile_start, int E, int N,
+                                      int K, hipStream_t st);
 hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
                                      const uint16_t* B0, const uint16_t* B1, void* C,
                                      const int32_t* offsets, const int32_t* mtile_start, int E, int N,

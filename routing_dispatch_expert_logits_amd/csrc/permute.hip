@@ -21,6 +21,9 @@ namespace moe {
 
 constexpr int kCopyUnroll = 4;
 
+// With x_perm == NULL only the metadata is written (row_token, token_row): the
+// fused layer's persistent gate/up GEMM then gathers the token rows itself.
+//
 // Workgroup (blockIdx.x, blockIdx.y): 4 waves x tpw tokens starting at
 // blockIdx.x * 4 * tpw, columns [c0, c1) of their rows (16-byte units; the
 // column split lets small token counts still fill the GPU).  Only the
@@ -76,6 +79,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
         if (row >= 0) row_token[row] = t;
       }
     }
+    if (!x_perm) continue;  // metadata only: the GEMM reads the token rows through row_token
     const u32x4* src = x + (size_t)t * row16;
     if constexpr (!MX) {
       for (int cb = c0; cb < c1; cb += kWave * kCopyUnroll) {
@@ -134,7 +138,7 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
   const int tpw = T >= 4096 ? 4 : 1;
   const int gx = ceil_div(T, 4 * tpw);
   int cs = 1;
-  while (gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
+  while (x_perm && gx * cs < 1024 && row16 / (cs * 2) >= kWave) cs *= 2;
   if (x_scale) {  // MXFP8 dispatch of bf16 rows: row16 bf16 chunks -> row16 * 8 code bytes
     if (row16 % 4) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_permute<true>, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,

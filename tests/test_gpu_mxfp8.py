@@ -296,6 +296,29 @@ def test_layer_mx_equals_separate_calls(name):
     np.testing.assert_array_equal(d["out"], _bf16_bits(a["out"]))
 
 
+# MXFP8 layers whose gate/up GEMM reads the token rows through row_token when the caller
+# does not ask for the permuted codes: persistent prefill tiles (D / 2 >= 256 16-bit
+# columns) and decode-scale tiles above 64 tokens
+MX_GATHER = [MoEConfig(name="mx_gather_prefill", T=300, H=512, E=16, k=4, I=192, seed=43,
+                       gate="computed", gate_std=0.05, dispatch="mxfp8"),
+             MoEConfig(name="mx_gather_prefill_ragged", T=517, H=640, E=24, k=6, I=320, seed=44,
+                       gate="drawn", dispatch="mxfp8"),
+             MoEConfig(name="mx_gather_decode", T=100, H=512, E=64, k=4, I=128, seed=45,
+                       gate="drawn", dispatch="mxfp8")]
+
+
+@pytest.mark.parametrize("cfg", MX_GATHER, ids=[c.name for c in MX_GATHER])
+def test_layer_mx_gathered_rows(cfg):
+    """Without aux x_perm the layer quantises the token rows once and gathers them; the
+    output bits equal those of the layer that writes the permuted codes, which the oracle
+    bounds."""
+    inp = gen.layer_inputs(cfg)
+    a = run_layer_mx(cfg, inp)
+    b = run_layer_mx(cfg, inp, with_aux=False)
+    np.testing.assert_array_equal(b["out"], a["out"])
+    check_layer_mx(cfg)
+
+
 # ------------------------------------------------------------------ full size, sampled tokens
 
 FULL_MX = ["qwen3_30b_a3b_shaped", "k3_shaped_decode", "k3_shaped_decode_t8"]

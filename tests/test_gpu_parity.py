@@ -396,6 +396,37 @@ def test_layer_matches_separate_calls_and_is_deterministic(name):
     np.testing.assert_array_equal(offs, a["offsets"])
 
 
+GATHER_CFGS = ["small_bf16_zipf", "small_bf16_uniform", "wide_experts", "shared_expert", "capacity_prefill",
+               "all_ties"]
+
+
+@pytest.mark.parametrize("name", GATHER_CFGS)
+def test_layer_gathered_rows_equal_permuted_copy(name):
+    """Without aux x_perm the fused layer writes only the row metadata and its gate/up
+    GEMM reads the token rows through row_token (persistent prefill tiles, or decode
+    tiles above 64 tokens); the output bits equal those of the layer that writes the
+    permuted copy, and its routing metadata is the same."""
+    cfg = PARITY_CONFIGS[name]
+    inp = gen.layer_inputs(cfg)
+    a = run_layer(cfg, inp)
+    b = run_layer(cfg, inp, with_aux=False)
+    np.testing.assert_array_equal(b["out"], a["out"])
+    s = shape_of(cfg)
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "ws1", "ws3", "ws2") if n in inp}
+    if "bias" in inp:
+        w["gate_bias"] = dev(inp["bias"])
+    logits = dev(inp["logits"]) if "logits" in inp else empty((cfg.T, cfg.E), "f32")
+    aux = {"row_token": empty((cfg.R,), "i32"), "token_row": empty((cfg.T, cfg.k), "i32"),
+           "offsets": empty((cfg.E + 1,), "i32")}
+    out = empty((cfg.T, cfg.H), "f32")
+    B.layer_forward(w, dev(inp["x"]), logits, out, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER), aux)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), a["out"])
+    n = int(a["offsets"][-1])
+    np.testing.assert_array_equal(host(aux["row_token"])[:n], a["row_token"][:n])
+    np.testing.assert_array_equal(host(aux["token_row"]), a["token_row"])
+
+
 def test_stage_events_skip_null_entries():
     """A stage-event array may leave entries NULL: only the others are recorded, and the
     layer's results do not depend on which are."""
