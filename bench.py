@@ -94,11 +94,31 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def rows_from_tokens(cfg):
+    """Whether moe_layer_forward (called without aux x_perm, as here) feeds the gate/up
+    GEMM the token rows through row_token instead of a permuted copy: every bf16 layer
+    on decode-sized tiles, and on the persistent 128-row tiles when the library's
+    condition holds (the XCD chunk of tiles fits the LDS table, at least 4 K-steps)."""
+    if cfg.dtype != "bf16":
+        return False
+    if cfg.R < 48 * cfg.E:
+        return True                                   # decode-sized tiles
+    mx = cfg.dispatch == "mxfp8"
+    K = cfg.D // 2 if mx else cfg.D                   # 16-bit columns (MXFP8 codes in pairs)
+    tiles = (cfg.R // 128 + min(cfg.E, cfg.R) + 1) * -(-cfg.I // 128)
+    cap = 2816 if mx else 3840
+    return (-(-tiles // 8) <= cap and cfg.E <= 1024 and -(-cfg.I // 128) <= 1024
+            and K % 64 == 0 and K // 64 >= 4)
+
+
 def stage_bytes_flops(cfg, counts):
     """Algorithmic HBM bytes and FLOPs per stage for one layer forward.
 
     b = element bytes of activations/weights; touched = experts with >= 1 row; the
     row count R is the rows kept (all T*k unless an expert capacity drops some).
+    When the gate/up GEMM reads the token rows through row_token (rows_from_tokens),
+    the permutation writes only the metadata and the GEMM's row bytes are those of
+    the T token rows (MXFP8: the quantised token rows, converted once per token).
     """
     T, H, E, k, I, L, D = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.D
     R = int(sum(counts))
@@ -110,14 +130,17 @@ def stage_bytes_flops(cfg, counts):
     st["gate"] = ((T * H * b + E * H * 4 + T * E * 4, 2 * T * H * E) if cfg.gate == "computed"
                   else (0, 0))
     st["route"] = (T * E * 4 + 8 * R + (2 * E + 1) * 4, 0)
+    gath = rows_from_tokens(cfg)
     if cfg.dispatch == "mxfp8":
         # rows and W1 / W3 as one code byte per element plus one scale byte per 32
         q = D * 33 // 32
-        st["permute"] = (T * D * b + R * q + 12 * R, 0)
-        st["gemm_gate_up"] = (touched * 2 * q * I + R * q + R * I * b, 4 * R * D * I)
+        rows_q = T * q if gath else R * q
+        st["permute"] = (T * D * b + rows_q + 12 * R, 0)
+        st["gemm_gate_up"] = (touched * 2 * q * I + rows_q + R * I * b, 4 * R * D * I)
     else:
-        st["permute"] = (T * D * b + R * D * b + 12 * R, 0)
-        st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
+        st["permute"] = ((12 * R, 0) if gath else (T * D * b + R * D * b + 12 * R, 0))
+        rows_b = (T if gath else R) * D * b
+        st["gemm_gate_up"] = (touched * 2 * D * I * b + rows_b + R * I * b, 4 * R * D * I)
     st["gemm_down"] = (touched * D * I * b + R * I * b + R * D * b, 2 * R * D * I)
     Is = cfg.shared_I
     st["shared_expert"] = ((T * H * b + 3 * Is * H * b + 2 * T * Is * b + T * H * b, 6 * T * H * Is)

@@ -17,20 +17,30 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def test_stage_bytes_bf16_and_mxfp8():
+    """The Qwen3-shaped layer gathers its token rows (metadata-only permutation, T rows
+    read by the gate/up GEMM); a layer whose rows are only 2 K-steps wide keeps the
+    permuted copy."""
     cfg = FULL_CONFIGS["qwen3_30b_a3b_shaped"]
     T, H, E, k, I, D, R = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.D, cfg.R
     counts = np.full(E, R // E)
+    assert bench.rows_from_tokens(cfg)
     st, touched = bench.stage_bytes_flops(cfg, counts)
     assert touched == E
-    assert st["permute"] == (T * D * 2 + R * D * 2 + 12 * R, 0)
-    assert st["gemm_gate_up"] == (E * 2 * D * I * 2 + R * D * 2 + R * I * 2, 4 * R * D * I)
+    assert st["permute"] == (12 * R, 0)
+    assert st["gemm_gate_up"] == (E * 2 * D * I * 2 + T * D * 2 + R * I * 2, 4 * R * D * I)
     assert st["gemm_down"][1] == 2 * R * D * I
     mx = cfg.with_(dispatch="mxfp8")
     st8, _ = bench.stage_bytes_flops(mx, counts)
     q = D * 33 // 32                       # one code byte per element + one scale byte per 32
-    assert st8["permute"] == (T * D * 2 + R * q + 12 * R, 0)
-    assert st8["gemm_gate_up"] == (E * 2 * q * I + R * q + R * I * 2, 4 * R * D * I)
+    assert st8["permute"] == (T * D * 2 + T * q + 12 * R, 0)
+    assert st8["gemm_gate_up"] == (E * 2 * q * I + T * q + R * I * 2, 4 * R * D * I)
     assert st8["gemm_down"] == st["gemm_down"] and st8["combine"] == st["combine"]
+    narrow = cfg.with_(H=128)
+    assert not bench.rows_from_tokens(narrow)
+    stn, _ = bench.stage_bytes_flops(narrow, counts)
+    assert stn["permute"] == (T * 128 * 2 + R * 128 * 2 + 12 * R, 0)
+    assert bench.rows_from_tokens(FULL_CONFIGS["k3_shaped_decode"])        # decode-sized tiles
+    assert not bench.rows_from_tokens(FULL_CONFIGS["tiny_f32"])
 
 
 def test_stage_bytes_follow_kept_rows():
