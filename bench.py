@@ -106,7 +106,7 @@ def rows_from_tokens(cfg):
     mx = cfg.dispatch == "mxfp8"
     K = cfg.D // 2 if mx else cfg.D                   # 16-bit columns (MXFP8 codes in pairs)
     tiles = (cfg.R // 128 + min(cfg.E, cfg.R) + 1) * -(-cfg.I // 128)
-    cap = 2816 if mx else 3840
+    cap = 2624 if mx else 3520
     return (-(-tiles // 8) <= cap and cfg.E <= 1024 and -(-cfg.I // 128) <= 1024
             and K % 64 == 0 and K // 64 >= 4)
 

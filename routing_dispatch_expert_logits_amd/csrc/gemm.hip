@@ -575,7 +575,10 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 // one-tile workgroups (the tiles sharing an expert's weights run together), a CU
 // that runs slow simply takes fewer tiles, and there is no per-tile dispatch, launch
 // or pipeline fill: the loader waves run ahead across tile boundaries, so the next
-// tile's first stages are in flight while the MFMA waves store the previous one.
+// tile's first stages are in flight while the MFMA waves store the previous one.  An
+// eleventh wave makes the claims (and, for gathered rows, DMAs the next tile's token
+// row indices into LDS), so the loader waves never wait on anything but their own
+// LDS DMA: a claim's result in a loader wave would make the compiler drain its DMA.
 // Each workgroup decodes the tile coordinates once into an LDS table: every tile
 // when they fit, and then a workgroup whose chunk is done takes tiles left in
 // other XCDs' chunks; else its own chunk.  Tiles, K-steps,
@@ -585,21 +588,21 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 
 // Chunk entries an LDS table can hold (4 bytes each: expert | m-tile << 10 | n-tile << 22).
 template <bool F8>
-constexpr int wsp_table_cap() { return F8 ? 2816 : 3840; }
+constexpr int wsp_table_cap() { return F8 ? 2624 : 3520; }
 constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0) (vmcnt, expcnt not waited)
 
 // Whether the persistent kernel takes a GEMM of at most `tiles` 128 x 128 tiles with K
 // 16-bit columns: the XCD chunk fits the LDS table, tile coordinates fit the entry,
-// and a tile has at least 3 K-steps (the claim of the next tile is published one
-// K-step after it is issued and read two K-steps before the tile ends).
+// and a tile has at least 4 K-steps (the scheduler wave publishes the next tile's
+// claim by K-step nsteps - 4, the loader waves read it at K-step nsteps - 2).
 template <bool F8>
 static inline bool wsp_fits(long tiles, int E, int N, int K) {
   return (tiles + 7) / 8 <= wsp_table_cap<F8>() && E <= 1024 && ceil_div(N, 128) <= 1024 && K % 64 == 0 &&
-         K / 64 >= 3;
+         K / 64 >= 4;
 }
 
 template <int BM, int BN, int NB, int EPI, int S, int MW = 8, bool F8 = false>
-__global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
+__global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
     const uint16_t* __restrict__ A, int M, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ C, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ mtile_start, int E, int N, int K, MxScales mx, int32_t* __restrict__ claim,
@@ -619,9 +622,11 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
   constexpr int NQW = NQP + NSP;  // vector-memory ops per stage per loader wave
   static_assert(S == 3 && NQW <= 63, "three stages: one stage in flight behind the one landing");
   constexpr int CAP = wsp_table_cap<F8>();
+  constexpr int NTHR = MW * 64 + 192;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
   __shared__ uint32_t table[CAP];
-  __shared__ int claimed[4];  // logical index of tile ti of this workgroup at [ti % 4], -1 past the end
+  __shared__ int claimed[4];       // logical index of tile ti of this workgroup at [ti % 4], -1 past the end
+  __shared__ int32_t grow[2][BM];  // gathered rows: token row of each tile row, tile ti at [ti % 2]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NT = ceil_div(N, BN);
@@ -636,7 +641,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
   const bool all = total <= CAP;
   const int tlo = all ? 0 : lo, tcount = all ? total : chunk;
   // table[L - tlo] for logical tile L in logical order (expert-major, then n-tile, then m-tile)
-  for (int e = tid; e < E; e += MW * 64 + 128) {
+  for (int e = tid; e < E; e += NTHR) {
     const int mt0 = mtile_start[e], mte = mtile_start[e + 1] - mt0;
     const int b = max(0, tlo - mt0 * NT), f = min(mte * NT, tlo + tcount - mt0 * NT);
     for (int local = b; local < f; ++local) {
@@ -644,46 +649,7 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
       table[mt0 * NT + local - tlo] = (uint32_t)e | ((uint32_t)m << 10) | ((uint32_t)n << 22);
     }
   }
-  // The logical tile for a claim `own` made on this XCD's counter, or -1 when no tile is
-  // left.  Run by a whole wave.  Each failed steal meets a counter already past its
-  // chunk, which every later agent-scope load of it shows, so the loop ends after at
-  // most 9 rounds.
-  auto take = [&](int own) -> int {
-    if (own < chunk) return lo + own;
-    if (!all) return -1;
-    for (int round = 0; round < 16; ++round) {
-      int left = -1;
-      if (lane < 8) {
-        const int c = __hip_atomic_load(&claim[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        left = max(0, min(per_xcd, total - lane * per_xcd)) - c;
-      }
-      int best = left, who = lane;
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        const int l2 = __shfl_xor(best, o), w2 = __shfl_xor(who, o);
-        if (l2 > best || (l2 == best && w2 < who)) {
-          best = l2;
-          who = w2;
-        }
-      }
-      best = __builtin_amdgcn_readfirstlane(best);
-      who = __builtin_amdgcn_readfirstlane(who);
-      if (best <= 0) return -1;
-      int t = 0;
-      if (lane == 0) t = atomicAdd(&claim[who], 1);
-      t = __builtin_amdgcn_readfirstlane(t);
-      if (t < max(0, min(per_xcd, total - who * per_xcd))) return who * per_xcd + t;
-    }
-    return -1;
-  };
-  if (wave == 0) {
-    int t = 0;
-    if (lane == 0) t = atomicAdd(&claim[xcd], 1);
-    const int L = take(__builtin_amdgcn_readfirstlane(t));
-    if (lane == 0) claimed[0] = L;
-  }
   __syncthreads();
-  if (claimed[0] < 0) return;  // the same value for every wave
   const int nsteps = K / BK;
 
   // logical tile L: expert, first row, rows, first column (wave-uniform)
@@ -697,35 +663,94 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     rows = min(BM, offsets[e + 1] - r0);                                                       \
   }
 
+  if (wave == MW + 2) {
+    // ---------------- scheduler wave: tile claims, and the token rows of gathered tiles.
+    // Its vmcnt waits for the claim's result are its own: the loader waves never wait
+    // on anything but their LDS DMA.
+    // The logical tile for a claim `own` made on this XCD's counter, or -1 when no tile
+    // is left.  Each failed steal meets a counter already past its chunk, which every
+    // later agent-scope load of it shows, so the loop ends after at most 9 rounds.
+    auto take = [&](int own) -> int {
+      if (own < chunk) return lo + own;
+      if (!all) return -1;
+      for (int round = 0; round < 16; ++round) {
+        int left = -1;
+        if (lane < 8) {
+          const int c = __hip_atomic_load(&claim[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          left = max(0, min(per_xcd, total - lane * per_xcd)) - c;
+        }
+        int best = left, who = lane;
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+          const int l2 = __shfl_xor(best, o), w2 = __shfl_xor(who, o);
+          if (l2 > best || (l2 == best && w2 < who)) {
+            best = l2;
+            who = w2;
+          }
+        }
+        best = __builtin_amdgcn_readfirstlane(best);
+        who = __builtin_amdgcn_readfirstlane(who);
+        if (best <= 0) return -1;
+        int t = 0;
+        if (lane == 0) t = atomicAdd(&claim[who], 1);
+        t = __builtin_amdgcn_readfirstlane(t);
+        if (t < max(0, min(per_xcd, total - who * per_xcd))) return who * per_xcd + t;
+      }
+      return -1;
+    };
+    // publish tile ti's claim and (gathered rows) DMA its token-row indices into grow
+    auto publish = [&](int ti, int L) {
+      if (lane == 0) claimed[ti & 3] = L;
+      if (gather && L >= 0) {
+        int g_e, g_r0, g_rows, g_n0;
+        MOE_WSP_COORDS(L, g_e, g_r0, g_rows, g_n0)
+        (void)g_e;
+        (void)g_n0;
+#pragma unroll
+        for (int h = 0; h < BM / 64; ++h)
+          __builtin_amdgcn_global_load_lds((gas_ptr)(gather + g_r0 + min(h * 64 + lane, g_rows - 1)),
+                                           (las_ptr)&grow[ti & 1][h * 64], 4, 0, 0);
+      }
+    };
+    {
+      int t = 0;
+      if (lane == 0) t = atomicAdd(&claim[xcd], 1);
+      publish(0, take(__builtin_amdgcn_readfirstlane(t)));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __syncthreads();  // the first tile's claim and token rows are in LDS
+    if (claimed[0] < 0) return;
+    // The next tile's claim goes out at K-step 0 of a tile and is published at K-step P
+    // (its DMA done by P + 1); the loader waves read it when they start the next tile's
+    // stages, at K-step nsteps - 2 (nsteps >= 4), the MFMA waves at the tile's start.
+    const int P = min(2, nsteps - 4);
+    __builtin_amdgcn_s_barrier();  // stage 0 has landed (the loaders' barrier)
+    asm volatile("" ::: "memory");
+    int pend = 0;
+    for (int ti = 0;; ++ti) {
+      if (claimed[ti & 3] < 0) break;
+      for (int st = 0; st < nsteps; ++st) {
+        if (st == 0 && lane == 0) pend = atomicAdd(&claim[xcd], 1);
+        if (st == P) publish(ti + 1, take(__builtin_amdgcn_readfirstlane(pend)));
+        if (st == P + 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the row-index DMA landed
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // claimed[] written
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    }
+    return;
+  }
+  __syncthreads();  // the first tile's claim (and token rows) are in LDS
+  if (claimed[0] < 0) return;  // the same value for every wave
+
   if (wave >= MW) {
-    // ---------------- loader waves
+    // ---------------- loader waves: stage f of the flattened (tile, K-step) sequence
     const int p = wave - MW;
     const uint16_t* src[NQP];
     int ldsoff[NQP];
     const uint8_t* ssrc[NSP > 0 ? NSP : 1];
     int sldsoff[NSP > 0 ? NSP : 1];
-    // gathered A rows (gather != NULL): the token row of each row this wave loads, for
-    // the tile set up next; read one K-step before it is needed, ahead of that step's
-    // DMAs, so the step's own vmcnt wait completes the loads
-    int gidx[NQP], sgidx[NSP > 0 ? NSP : 1];
-#define MOE_WSP_GATHER(t)                                                                             \
-  {                                                                                                   \
-    int g_e, g_r0, g_rows, g_n0;                                                                      \
-    MOE_WSP_COORDS(t, g_e, g_r0, g_rows, g_n0)                                                        \
-    (void)g_e;                                                                                        \
-    (void)g_n0;                                                                                       \
-    _Pragma("unroll") for (int j = 0; j < NQP; ++j) {                                                 \
-      const int q = p * NQP + j;                                                                      \
-      if (q < QA) gidx[j] = gather[g_r0 + min(q * RPQ + lane / CH, g_rows - 1)];                      \
-    }                                                                                                 \
-    if constexpr (F8) {                                                                               \
-      _Pragma("unroll") for (int j = 0; j < NSP; ++j) {                                               \
-        const int q = p * NSP + j;                                                                    \
-        if (q < SQA) sgidx[j] = gather[g_r0 + min(q * 64 + lane, g_rows - 1)];                        \
-      }                                                                                               \
-    }                                                                                                 \
-  }
-#define MOE_WSP_SET_TILE(t)                                                                           \
+#define MOE_WSP_SET_TILE(t, ti)                                                                       \
   {                                                                                                   \
     int t_e, t_r0, t_rows, t_n0;                                                                      \
     MOE_WSP_COORDS(t, t_e, t_r0, t_rows, t_n0)                                                        \
@@ -734,7 +759,8 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
       if (q < QA) {                                                                                   \
         const int r = q * RPQ + lane / CH;                                                            \
         const int cc = (lane % CH) ^ swz<BK>(r);                                                      \
-        src[j] = A + (size_t)(gather ? gidx[j] : t_r0 + min(r, t_rows - 1)) * K + cc * 8;             \
+        const int row = gather ? grow[(ti) & 1][r] : t_r0 + min(r, t_rows - 1);                       \
+        src[j] = A + (size_t)row * K + cc * 8;                                                        \
         ldsoff[j] = q * 512;                                                                          \
       } else {                                                                                        \
         const int nb = (q - QA) / QB, qq = (q - QA) % QB;                                             \
@@ -750,7 +776,8 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
         const int q = p * NSP + j;                                                                    \
         if (q < SQA) {                                                                                \
           const int r = q * 64 + lane;                                                                \
-          ssrc[j] = mx.a + (size_t)(gather ? sgidx[j] : t_r0 + min(r, t_rows - 1)) * srow;            \
+          const int row = gather ? grow[(ti) & 1][r] : t_r0 + min(r, t_rows - 1);                     \
+          ssrc[j] = mx.a + (size_t)row * srow;                                                        \
           sldsoff[j] = (A_ELEMS + NB * B_ELEMS) * 2 + q * 256;                                        \
         } else {                                                                                      \
           const int nb = (q - SQA) / SQB, qq = (q - SQA) % SQB;                                       \
@@ -773,16 +800,11 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     }                                                                                                 \
     ++ist;                                                                                            \
   }
-    int it = 0, ist = 0;    // tile (ring index) and K-step of the next stage to issue
-    int fslot = 0;          // its LDS ring slot
-    bool more = true;       // whether tile `it` still has stages to issue
-    bool published = true;  // whether the claim for tile it + 1 is in claimed[]
-    int tnext = 0;          // that claim (loader wave 0, lane 0)
-    if (gather) MOE_WSP_GATHER(claimed[0])
-    MOE_WSP_SET_TILE(claimed[0])
-    if (p == 0 && lane == 0) tnext = atomicAdd(&claim[xcd], 1);
-    published = false;
-    for (int f = 0; f < S - 1; ++f) {  // nsteps >= 3: both stages belong to the first tile
+    int it = 0, ist = 0;  // tile and K-step of the next stage to issue
+    int fslot = 0;        // its LDS ring slot
+    bool more = true;     // whether tile `it` still has stages to issue
+    MOE_WSP_SET_TILE(claimed[0], 0)
+    for (int f = 0; f < S - 1; ++f) {  // nsteps >= 4: both stages belong to the first tile
       MOE_WSP_ISSUE(fslot)
       fslot = fslot + 1 == S ? 0 : fslot + 1;
     }
@@ -792,21 +814,13 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
     for (int ti = 0;; ++ti) {
       if (claimed[ti & 3] < 0) break;
       for (int st = 0; st < nsteps; ++st) {
-        // next tile's token rows, one step before its first stage (nsteps >= 4: the claim
-        // was published at least one barrier earlier)
-        if (gather && more && ist == nsteps - 1) {
-          const int tg = claimed[(it + 1) & 3];
-          if (tg >= 0) MOE_WSP_GATHER(tg)
-        }
         // the stage S-1 ahead: this tile's, or the first stages of the next claimed tile
         if (more && ist == nsteps) {
           const int tn = claimed[(it + 1) & 3];
           if (tn >= 0) {
             ++it;
             ist = 0;
-            MOE_WSP_SET_TILE(tn)
-            if (p == 0 && lane == 0) tnext = atomicAdd(&claim[xcd], 1);
-            published = false;
+            MOE_WSP_SET_TILE(tn, it)
           } else {
             more = false;
           }
@@ -818,19 +832,12 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_wsp(
         } else {
           __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
-        // the claim went out before the last two stages, so the wait above completed it
-        if (p == 0 && !published && ist >= 2) {
-          const int L = take(__builtin_amdgcn_readfirstlane(tnext));
-          if (lane == 0) claimed[(it + 1) & 3] = L;
-          published = true;
-        }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
     }
 #undef MOE_WSP_ISSUE
 #undef MOE_WSP_SET_TILE
-#undef MOE_WSP_GATHER
     return;
   }
 
@@ -1237,7 +1244,7 @@ int max_mtiles(int M, int E, int bm) {
 
 bool gemm_gather_ok(int M, int E, int N, int K, bool mx) {
   const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
-  return (mx ? wsp_fits<true>(tiles, E, N, K) : wsp_fits<false>(tiles, E, N, K)) && K / 64 >= 4;
+  return mx ? wsp_fits<true>(tiles, E, N, K) : wsp_fits<false>(tiles, E, N, K);
 }
 
 hipError_t launch_gemm_prefill_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
@@ -1248,10 +1255,10 @@ hipError_t launch_gemm_prefill_gather(int epi, const uint16_t* X, const int32_t*
   int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
   const dim3 bb(8 * 64 + 128);
   if (epi == EPI_SWIGLU_BF16)
-    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), bb, 0, st, X, M, B0, B1, C,
+    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, X, M, B0, B1, C,
                        offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
   else if (epi == EPI_SWIGLU_F32)
-    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), bb, 0, st, X, M, B0, B1, C,
+    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, X, M, B0, B1, C,
                        offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
   else
     return hipErrorInvalidValue;
@@ -1296,10 +1303,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
         // persistent wave-specialised kernel (256 workgroups, one per CU)
         int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
         if (epi == EPI_SWIGLU_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
+          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1,
                              C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
         else
-          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1,
+          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1,
                              C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
         return hipGetLastError();
       }
@@ -1330,10 +1337,10 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
         int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
         if (epi == EPI_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_BF16, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
+          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
                              offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
         else
-          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_F32, 3, 8>), dim3(256), bb, 0, st, A, M, B0, B1, C,
+          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
                              offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
         return hipGetLastError();
       }
@@ -1419,7 +1426,7 @@ hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const u
     if (gather && !gemm_gather_ok(M, E, N, K, true)) return hipErrorInvalidValue;
     if (wsp_fits<true>(tiles, E, N, K)) {
       int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
-      hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, true>), dim3(256), bb, 0, st, a, M, b0, b1,
+      hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, true>), dim3(256), dim3(8 * 64 + 192), 0, st, a, M, b0, b1,
                          C, offsets, mtile_start, E, N, K, mx, claim, gather);
     } else {
       const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128));
