@@ -150,6 +150,12 @@ def stage_bytes_flops(cfg, counts):
     return st, touched
 
 
+def event_stride(steps, samples=10):
+    """Every how many timed steps the gate/up GEMM's two events are recorded: about
+    `samples` launches sampled, every step when there are fewer steps than that."""
+    return max(1, steps // samples)
+
+
 def pct(vals, q):
     """Nearest-rank q-th percentile."""
     srt = sorted(vals)
@@ -470,16 +476,18 @@ def main(argv=None):
     nev = B.MOE_NUM_STAGE_EVENTS
     names = B.STAGE_NAMES
     # The timed steps record only the two events around the expert gate/up GEMM (the
-    # dominant kernel the roofline object describes): every event record puts a few
-    # microseconds between the kernels either side of it.  The per-stage breakdown comes
-    # from a separate pass with every stage event, after the timed region.
+    # dominant kernel the roofline object describes), and only on every `stride`-th
+    # step (about 10 sampled launches): every event record puts a few microseconds
+    # between the kernels either side of it.  The per-stage breakdown comes from a
+    # separate pass with every stage event, after the timed region.
     g = names.index("gemm_gate_up")
-    gev = [hip.create(2) for _ in range(args.steps)]
-    tev = []
-    for pair in gev:
+    stride = event_stride(args.steps)
+    gev = [hip.create(2) for _ in range(0, args.steps, stride)]
+    tev = [None] * args.steps
+    for j, pair in enumerate(gev):
         arr = [None] * nev
         arr[g], arr[g + 1] = pair
-        tev.append(arr)
+        tev[j * stride] = arr
 
     for _ in range(args.warmup):
         B.layer_forward(w, x, logits, out, od, s, ws, aux=aux, stream=stream)
@@ -631,7 +639,8 @@ def main(argv=None):
         "grouped_gemm_tflops": round((sb["gemm_gate_up"][1] + sb["gemm_down"][1]) / (gemm_ms * 1e-3) / 1e12, 1),
         "permute_gbps": stages["permute"]["GB/s"],
         "combine_gbps": stages["combine"]["GB/s"],
-        "stage_timing": ("timed steps record the two events around the expert gate/up GEMM; "
+        "stage_timing": (f"timed steps record the two events around the expert gate/up GEMM on every "
+                         f"{stride}-th step ({len(gev)} of {args.steps} launches sampled); "
                          "stages and layer_event_ms come from a second pass of as many steps "
                          "with every stage event"),
         "layer_event_ms": round(layer_ev_ms, 5),

@@ -466,14 +466,14 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     // a2 + a3
     MOE_HIP(launch_topk(scores, d.T, d.E, d.k, ids, tw, bc, st));
     MOE_HIP(launch_expert_scan(bc, d.nb, d.E, d.cap, counts, st));
-    MOE_HIP(launch_offsets(counts, nullptr, d.E, offs, gemm_bm(kind), mtile, st));
     if (!ev(3)) return MOE_ERR_HIP;
-    // a4
+    // a3 (segment starts, GEMM tile tables) inside the a4 launch
+    const PermuteOffsets po{counts, offs, gemm_bm(kind), mtile};
     if (gath) {
       if (d.mx) MOE_HIP(launch_mx_quantize(src, true, d.T, d.D, xq, xqs, st));  // token rows, once
-      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, nullptr, nullptr, rtok, trow, st));
+      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, nullptr, nullptr, rtok, trow, st, &po));
     } else {
-      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, xs, rtok, trow, st));
+      MOE_HIP(launch_permute(src, row16, ids, d.T, d.E, d.k, d.cap, offs, bc, xperm, xs, rtok, trow, st, &po));
     }
   }
   if (!ev(4)) return MOE_ERR_HIP;

@@ -62,9 +62,21 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
 // bases: per-block rows before each block (launch_expert_scan); offsets: segment starts.
 // x_scale non-NULL: MXFP8 dispatch of bf16 rows (x_perm gets E4M3 codes, x_scale the
 // [rows x D/32] E8M0 scales; row16 = D / 8 must be a multiple of 4).
+// po (optional, fused layer): the permutation takes the segment starts from the
+// per-expert counts itself (each workgroup scans them in LDS; `offsets` is then
+// unused), and workgroup (0, 0) writes what launch_offsets(counts, NULL, E,
+// po->offsets_out, po->bm, po->mtile_start) would, claim counters included, so the
+// layer saves that launch.
+struct PermuteOffsets {
+  const int32_t* counts;
+  int32_t* offsets_out;
+  int bm;
+  int32_t* mtile_start;
+};
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
                           const int32_t* offsets, const int32_t* bases, void* x_perm, uint8_t* x_scale,
-                          int32_t* row_token, int32_t* token_row, hipStream_t st);
+                          int32_t* row_token, int32_t* token_row, hipStream_t st,
+                          const PermuteOffsets* po = nullptr);
 // MXFP8 quantisation of [rows x cols] bf16 or fp32 values (cols % 32 == 0).
 hipError_t launch_mx_quantize(const void* src, bool src_bf16, long rows, long cols, uint8_t* q,
                               uint8_t* scale, hipStream_t st);

@@ -21,6 +21,39 @@ namespace moe {
 
 constexpr int kCopyUnroll = 4;
 
+// Exclusive prefix sum of f(i), i < n <= 1024, over the 256 threads of a workgroup
+// into out[0, n) (LDS); returns the total.  Thread t takes i = 4t .. 4t + 3.
+template <class F>
+__device__ __forceinline__ int wg256_exclusive_scan(F f, int n, int* out, int* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int v[4], s = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    v[u] = i < n ? f(i) : 0;
+    s += v[u];
+  }
+  int incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int base = incl - s;
+  for (int w = 0; w < wave; ++w) base += wtot[w];
+  const int total = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 4 * tid + u;
+    if (i < n) out[i] = base;
+    base += v[u];
+  }
+  __syncthreads();
+  return total;
+}
+
 // With x_perm == NULL only the metadata is written (row_token, token_row): the
 // fused layer's persistent gate/up GEMM then gathers the token rows itself.
 //
@@ -44,9 +77,34 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
                                                  u32x4* __restrict__ x_perm,
                                                  uint8_t* __restrict__ xs,
                                                  int32_t* __restrict__ row_token,
-                                                 int32_t* __restrict__ token_row) {
+                                                 int32_t* __restrict__ token_row,
+                                                 PermuteOffsets po) {
   __shared__ unsigned long long mask[kMaxE];
+  __shared__ int off_s[kMaxE];
+  __shared__ int wtot[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (po.counts) {  // segment starts from the counts (workgroup-uniform branch)
+    const int32_t* cn = po.counts;
+    const int tot = wg256_exclusive_scan([=](int i) { return cn[i]; }, E, off_s, wtot);
+    if (blockIdx.x == 0 && blockIdx.y == 0) {
+      if (po.offsets_out) {
+        for (int e = tid; e < E; e += 256) po.offsets_out[e] = off_s[e];
+        if (tid == 0) po.offsets_out[E] = tot;
+      }
+      if (po.bm > 0) {  // m-tile tables for tile heights bm and 2 bm, claim counters cleared
+        __shared__ int mt_s[kMaxE];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int bmh = po.bm << h;
+          const int mtot = wg256_exclusive_scan([=](int i) { return ceil_div(cn[i], bmh); }, E, mt_s, wtot);
+          int32_t* tab = po.mtile_start + h * (E + 1);
+          for (int e = tid; e < E; e += 256) tab[e] = mt_s[e];
+          if (tid == 0) tab[E] = mtot;
+        }
+        if (tid < kClaimSlots) po.mtile_start[2 * (E + 1) + tid] = 0;
+      }
+    }
+  }
   const int tok0 = blockIdx.x * 4 * tpw;
   const int btok = block_tokens(T);
   const int blk = tok0 / btok;
@@ -73,7 +131,7 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
       const int e = topk_ids[(size_t)t * k + lane];
       const int tl = t - bt0;
       const int rank = bases[(size_t)blk * E + e] + __popcll(mask[e] & ((1ull << tl) - 1ull));
-      row = (cap > 0 && rank >= cap) ? -1 : offsets[e] + rank;
+      row = (cap > 0 && rank >= cap) ? -1 : (po.counts ? off_s[e] : offsets[e]) + rank;
       if (meta) {
         token_row[(size_t)t * k + lane] = row;
         if (row >= 0) row_token[row] = t;
@@ -132,7 +190,10 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
 
 hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, int E, int k, int cap,
                           const int32_t* offsets, const int32_t* bases, void* x_perm, uint8_t* x_scale,
-                          int32_t* row_token, int32_t* token_row, hipStream_t st) {
+                          int32_t* row_token, int32_t* token_row, hipStream_t st,
+                          const PermuteOffsets* po) {
+  const PermuteOffsets pov = po ? *po : PermuteOffsets{nullptr, nullptr, 0, nullptr};
+  if (pov.counts && E > 4 * 256) return hipErrorInvalidValue;
   // 4 tokens per wave for large T, 1 for small T (a workgroup's tokens always lie
   // in one ranking block); split columns until ~1024 workgroups
   const int tpw = T >= 4096 ? 4 : 1;
@@ -143,11 +204,11 @@ hipError_t launch_permute(const void* x, int row16, const int32_t* ids, int T, i
     if (row16 % 4) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_permute<true>, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
                        ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), x_scale,
-                       row_token, token_row);
+                       row_token, token_row, pov);
   } else {
     hipLaunchKernelGGL(k_permute<false>, dim3(gx, cs), dim3(256), 0, st, static_cast<const u32x4*>(x), row16,
                        ids, T, E, k, tpw, cap, offsets, bases, static_cast<u32x4*>(x_perm), nullptr,
-                       row_token, token_row);
+                       row_token, token_row, pov);
   }
   return hipGetLastError();
 }
