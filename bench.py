@@ -46,6 +46,9 @@ BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 F32_PEAK_TFLOPS = 157.3
 GEMM_SRC = os.path.join(ROOT, "routing_dispatch_expert_logits_amd", "csrc", "gemm.hip")
+# the headers gemm.hip includes: a change in either changes the compiled GEMM too
+GEMM_HEADERS = [os.path.join(ROOT, "routing_dispatch_expert_logits_amd", "csrc", h)
+                for h in ("moe_kernels.h", "moe_device.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{config}.json")
 
 
@@ -251,7 +254,13 @@ def ep_rank_share(B, torch, np, gen, cfg, ranks, up, stream, hip, reps=10):
 
 
 def src_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the GEMM source (`path`) followed by the
+    headers it includes: traffic counters are reported only for the code they
+    were taken on."""
+    h = hashlib.sha256(open(path, "rb").read())
+    for inc in GEMM_HEADERS:
+        h.update(open(inc, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(cfg, inp, target_s):
