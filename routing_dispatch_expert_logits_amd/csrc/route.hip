@@ -31,34 +31,47 @@ namespace moe {
 // bias formed on the fly, or the gate's split-K partial rows summed in ascending
 // slice order plus the bias, the sum then written out as the token's logits row
 // (the arithmetic of k_gate_reduce, so the logits are the same bits).
+// A pointer every lane of the wave holds, moved to scalar registers (the caller
+// guarantees it is wave-uniform), so loads through it take a scalar base.
+template <class P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<P*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int SLOTS>
 __device__ __forceinline__ void rank_token(const ScoreSrc& src, size_t row0, int E, int k, int lane,
                                            int& my_e, float& my_w) {
   // every load is issued unconditionally (lanes past E read the last score and
-  // are masked afterwards) so they overlap instead of each waiting in a branch
+  // are masked afterwards) so they overlap instead of each waiting in a branch.
+  // The row is the same for the whole wave: a scalar base plus 32-bit lane offsets
+  // (per-slot 64-bit addresses overflowed the register budget at 16 slots).
   float v[SLOTS];
-  const float* first = src.parts ? src.parts : src.scores;
+  const float* first = uniform_ptr((src.parts ? src.parts : src.scores) + row0);
 #pragma unroll
-  for (int s = 0; s < SLOTS; ++s) v[s] = first[row0 + min(lane + s * kWave, E - 1)];
+  for (int s = 0; s < SLOTS; ++s) v[s] = first[static_cast<unsigned>(min(lane + s * kWave, E - 1))];
   for (int p = 1; p < src.S; ++p) {
     float q[SLOTS];
-    const float* part = src.parts + (size_t)p * src.stride + row0;
+    const float* part = uniform_ptr(src.parts + (size_t)p * src.stride + row0);
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) q[s] = part[min(lane + s * kWave, E - 1)];
+    for (int s = 0; s < SLOTS; ++s) q[s] = part[static_cast<unsigned>(min(lane + s * kWave, E - 1))];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) v[s] += q[s];
   }
   if (src.bias) {
     float b[SLOTS];
 #pragma unroll
-    for (int s = 0; s < SLOTS; ++s) b[s] = src.bias[min(lane + s * kWave, E - 1)];
+    for (int s = 0; s < SLOTS; ++s) b[s] = src.bias[static_cast<unsigned>(min(lane + s * kWave, E - 1))];
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s) v[s] += b[s];
   }
   if (src.logits_out) {
+    float* lrow = uniform_ptr(src.logits_out + row0);
 #pragma unroll
     for (int s = 0; s < SLOTS; ++s)
-      if (lane + s * kWave < E) src.logits_out[row0 + lane + s * kWave] = v[s];
+      if (lane + s * kWave < E) lrow[static_cast<unsigned>(lane + s * kWave)] = v[s];
   }
   uint32_t key[SLOTS];
 #pragma unroll
