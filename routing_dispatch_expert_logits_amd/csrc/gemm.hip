@@ -1276,12 +1276,15 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
     //    tiles, 8 MFMA waves (against one workgroup per tile: Qwen3-shaped 303 -> 271 us,
     //    R1-shaped 4.66 -> 4.45 ms, latent equal; against 256-row tiles with every wave
     //    loading, faster on both of the first two);
-    //  - expert down: the persistent wave-specialised kernel, with 256 x 128 tiles for
-    //    K >= 2048 (R1-shaped 2.61 -> 2.46 ms against one workgroup per tile,
-    //    latent-shaped equal) and 128 x 256 tiles below (Qwen3-shaped, K = 768: 174 us
-    //    against 189 us for the register-staged kernel at three waves per SIMD, which
-    //    remains the fallback when the tile table does not fit; 128 x 128 and
-    //    256 x 128 persistent tiles took 208 and 187 us there);
+    //  - expert down: the persistent wave-specialised kernel.  128 x 256 tiles (half
+    //    the re-reads of the intermediate rows) when K < 2048 or the experts average
+    //    at least 192 rows: Qwen3-shaped (K = 768, 256 rows) 174 us against 189 us for
+    //    the register-staged kernel at three waves per SIMD and 187 / 208 us for
+    //    256 x 128 / 128 x 128 persistent tiles; R1-shaped (K = 2048, 256 rows) 2.30 ms
+    //    against 2.61 ms on 256 x 128 tiles.  Otherwise 256 x 128 tiles for K >= 2048
+    //    (latent-shaped, 128 rows: 0.89 ms against 0.94 ms on 128 x 256 tiles; R1-shaped
+    //    2.61 -> 2.46 ms against one workgroup per tile), and the register-staged
+    //    kernel when no persistent tile table fits;
     //  - dense latent projections (one group): wave-specialised kernel with
     //    256 x 128 tiles (one tile row per 256 tokens fills 256 CUs in one pass).
     if (!offsets) {
@@ -1331,6 +1334,21 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       }
       return hipGetLastError();
     }
+    // down GEMM: 128 x 256 persistent tiles when K is short or the experts average
+    // at least 192 rows, when the tile table fits
+    if (K < 2048 || (long)M >= 192L * E) {
+      const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 256);
+      if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
+        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
+        if (epi == EPI_BF16)
+          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
+                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
+        else
+          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
+                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
+        return hipGetLastError();
+      }
+    }
     if (K >= 2048) {  // down GEMM with a long K: 256-row tiles (second m-tile table)
       const int32_t* mt256 = mtile_start + E + 1;
       const long tiles = (long)max_mtiles(M, E, 256) * ceil_div(N, 128);
@@ -1355,19 +1373,6 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
       else
         return hipErrorInvalidValue;
       return hipGetLastError();
-    }
-    {  // down GEMM with a short K: persistent kernel on 128 x 256 tiles when it fits
-      const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 256);
-      if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
-        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
-        if (epi == EPI_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        else
-          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        return hipGetLastError();
-      }
     }
     switch (epi) {
       case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16, 3>), g); break;
