@@ -94,44 +94,63 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
   // The trip count is wave-uniform so every lane takes part in the shuffles of the
   // row indices and weights (a shuffle from an inactive lane returns no defined
   // value); lanes past the end of the row clamp their loads and store nothing.
-  for (int cb = c0; cb < c1; cb += kWave) {
-    const bool on = cb + lane < c1;
-    const int c = on ? cb + lane : c1 - 1;
-    float acc[NV];
+  // Each pass covers two 16-byte column chunks per lane (c and c + 64), so the
+  // loads of both are in flight together and each row is read in 2 KB pieces.
+  constexpr int CH = 2;
+  for (int cb = c0; cb < c1; cb += CH * kWave) {
+    bool on[CH];
+    int c[CH];
+    float acc[CH][NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+    for (int h = 0; h < CH; ++h) {
+      on[h] = cb + h * kWave + lane < c1;
+      c[h] = on[h] ? cb + h * kWave + lane : c1 - 1;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[h][i] = 0.f;
+    }
     int j = 0;
     for (; j + 4 <= k; j += 4) {
-      uint4 v[4];
+      uint4 v[4][CH];
       float wj[4];
       int r[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         r[u] = __shfl(my_row, j + u, kWave);
         wj[u] = __shfl(my_w, j + u, kWave);
-        v[u] = y[(size_t)max(r[u], 0) * row16 + c];
+        const uint4* yr = y + (size_t)max(r[u], 0) * row16;
+#pragma unroll
+        for (int h = 0; h < CH; ++h) v[u][h] = yr[c[h]];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (r[u] < 0) continue;  // dropped (uniform over the wave)
-        float f[NV];
-        Vec16<IT>::unpack(v[u], f);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj[u], f[i], acc[i]);
+        for (int h = 0; h < CH; ++h) {
+          float f[NV];
+          Vec16<IT>::unpack(v[u][h], f);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) acc[h][i] = fmaf(wj[u], f[i], acc[h][i]);
+        }
       }
     }
     for (; j < k; ++j) {
       const int r = __shfl(my_row, j, kWave);
       const float wj = __shfl(my_w, j, kWave);
       if (r < 0) continue;
-      float f[NV];
-      Vec16<IT>::unpack(y[(size_t)r * row16 + c], f);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
+      for (int h = 0; h < CH; ++h) {
+        float f[NV];
+        Vec16<IT>::unpack(y[(size_t)r * row16 + c[h]], f);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) acc[h][i] = fmaf(wj, f[i], acc[h][i]);
+      }
     }
-    if (!on) continue;
-    if (add) add_row<IT>(acc, add[(size_t)t * row16 + c]);
-    store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
+#pragma unroll
+    for (int h = 0; h < CH; ++h) {
+      if (!on[h]) continue;
+      if (add) add_row<IT>(acc[h], add[(size_t)t * row16 + c[h]]);
+      store_out<NV>(out, ((size_t)t * row16 + c[h]) * NV, acc[h], out_f32 != 0);
+    }
   }
 }
 
