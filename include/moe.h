@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 #ifndef MOE_API
 #define MOE_API __attribute__((visibility("default")))
@@ -147,6 +147,32 @@ typedef struct moe_shape {
 
 /* Workspace bytes `call` needs for shape `s` (0 if the shape is invalid). Host only. */
 MOE_API size_t moe_workspace_bytes(const moe_shape* s, int call);
+
+/* moe_layer_plan flags: which optional inputs the planned moe_layer_forward call gets. */
+#define MOE_PLAN_GATE 1    /* a router weight (gate_w) is given: the gate scores are computed */
+#define MOE_PLAN_X_PERM 2  /* the caller asks for the permuted rows (aux.x_perm, and with MXFP8
+                            * dispatch aux.x_perm_scale) */
+
+/* The kernels moe_layer_forward runs for a shape: the same decision the call itself
+ * takes (one function makes it for both), reported so that measurements can name and
+ * price the kernels that actually ran. */
+typedef struct moe_plan {
+  int32_t launches;            /* kernel launches of one moe_layer_forward (stage events aside) */
+  int32_t decode_path;         /* 1: decode-scale step, routing + counts + offsets + row metadata
+                                * in one launch */
+  int32_t rows_gathered;       /* 1: no permuted copy is written; the expert gate/up GEMM reads
+                                * the token rows through row_token */
+  int32_t gate_up_tile_m, gate_up_tile_n, gate_up_persistent;  /* expert gate/up GEMM */
+  int32_t down_tile_m, down_tile_n, down_persistent;           /* expert down GEMM */
+  int32_t reserved;
+  const char* gate_up_kernel;  /* static: kernel name up to its tile arguments, as a trace shows it */
+  const char* down_kernel;     /* static, likewise */
+} moe_plan;
+
+/* Fill *plan for a moe_layer_forward call on shape s with flags MOE_PLAN_*.  Host only:
+ * no GPU work.  Returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED for a shape that
+ * moe_layer_forward would reject the same way, or for a NULL plan or unknown flags. */
+MOE_API moe_status moe_layer_plan(const moe_shape* s, int flags, moe_plan* plan);
 
 /* Static string for a status code. */
 MOE_API const char* moe_status_string(int status);

@@ -20,7 +20,8 @@ MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_FFN, MOE_CALL_COMBINE, MOE_CALL_LAYE
 MOE_COMBINE_FUSED, MOE_COMBINE_UNFUSED = 0, 1
 MOE_DISPATCH_DTYPE, MOE_DISPATCH_MXFP8 = 0, 1
 MOE_NUM_STAGE_EVENTS = 10
-ABI_VERSION = 4
+ABI_VERSION = 5
+MOE_PLAN_GATE, MOE_PLAN_X_PERM = 1, 2
 
 STAGE_NAMES = ["latent_down", "gate", "route", "permute", "gemm_gate_up", "gemm_down",
                "shared_expert", "combine", "latent_up"]
@@ -54,6 +55,13 @@ class MoeLayerAux(ctypes.Structure):
                 ("z", _vp), ("out_latent", _vp), ("x_perm_scale", _vp)]
 
 
+class MoePlan(ctypes.Structure):
+    _fields_ = [("launches", _i32), ("decode_path", _i32), ("rows_gathered", _i32),
+                ("gate_up_tile_m", _i32), ("gate_up_tile_n", _i32), ("gate_up_persistent", _i32),
+                ("down_tile_m", _i32), ("down_tile_n", _i32), ("down_persistent", _i32),
+                ("reserved", _i32), ("gate_up_kernel", ctypes.c_char_p), ("down_kernel", ctypes.c_char_p)]
+
+
 def _load() -> ctypes.CDLL:
     # torch ships its own libamdhip64.so.7; loading torch first makes libmoe bind
     # to that same HIP runtime instance, so torch's streams, events and
@@ -70,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_workspace_bytes.argtypes = [P(MoeShape), ctypes.c_int]
     sz = ctypes.c_size_t
+    lib.moe_layer_plan.argtypes = [P(MoeShape), ctypes.c_int, P(MoePlan)]
+    lib.moe_layer_plan.restype = ctypes.c_int
     lib.moe_route_topk.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
     lib.moe_dispatch_permute.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz, _vp]
     lib.moe_grouped_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, P(MoeShape), _vp, sz,
@@ -103,6 +113,17 @@ def shape(T: int, H: int, E: int, k: int, I: int, L: int = 0, dtype: str = "bf16
 
 def workspace_bytes(s: MoeShape, call: int) -> int:
     return int(lib.moe_workspace_bytes(ctypes.byref(s), call))
+
+
+def layer_plan(s: MoeShape, gate: bool, x_perm: bool = False) -> dict:
+    """The kernels moe_layer_forward runs for shape s (host-only query)."""
+    p = MoePlan()
+    flags = (MOE_PLAN_GATE if gate else 0) | (MOE_PLAN_X_PERM if x_perm else 0)
+    _check("moe_layer_plan", lib.moe_layer_plan(ctypes.byref(s), flags, ctypes.byref(p)))
+    d = {f: getattr(p, f) for f, _ in MoePlan._fields_ if f != "reserved"}
+    for f in ("gate_up_kernel", "down_kernel"):
+        d[f] = d[f].decode()
+    return d
 
 
 def _p(t) -> Optional[int]:

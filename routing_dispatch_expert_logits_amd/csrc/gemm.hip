@@ -591,14 +591,16 @@ template <bool F8>
 constexpr int wsp_table_cap() { return F8 ? 2624 : 3520; }
 constexpr int kWaitLgkm0 = 0xC07F;  // s_waitcnt lgkmcnt(0) (vmcnt, expcnt not waited)
 
-// Whether the persistent kernel takes a GEMM of at most `tiles` 128 x 128 tiles with K
-// 16-bit columns: the XCD chunk fits the LDS table, tile coordinates fit the entry,
-// and a tile has at least 4 K-steps (the scheduler wave publishes the next tile's
-// claim by K-step nsteps - 4, the loader waves read it at K-step nsteps - 2).
+// Whether the persistent kernel takes a GEMM of at most `tiles` tiles of BM rows, over
+// at most M rows per expert, N columns and K 16-bit columns: the XCD chunk fits the LDS
+// table, every tile coordinate fits its field of a table entry (expert 10 bits, m-tile
+// 12 bits, n-tile 10 bits), and a tile has at least 4 K-steps (the scheduler wave
+// publishes the next tile's claim by K-step nsteps - 4, the loader waves read it at
+// K-step nsteps - 2).
 template <bool F8>
-static inline bool wsp_fits(long tiles, int E, int N, int K) {
-  return (tiles + 7) / 8 <= wsp_table_cap<F8>() && E <= 1024 && ceil_div(N, 128) <= 1024 && K % 64 == 0 &&
-         K / 64 >= 4;
+static inline bool wsp_fits(long tiles, int M, int BM, int E, int N, int K) {
+  return (tiles + 7) / 8 <= wsp_table_cap<F8>() && E <= 1024 && ceil_div(M, BM) <= 4096 &&
+         ceil_div(N, 128) <= 1024 && K % 64 == 0 && K / 64 >= 4;
 }
 
 template <int BM, int BN, int NB, int EPI, int S, int MW = 8, bool F8 = false>
@@ -1236,30 +1238,83 @@ int max_mtiles(int M, int E, int bm) {
   return M / bm + (E < M ? E : M) + 1;
 }
 
-#define MOE_LAUNCH(kern, grid) \
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K)
-#define MOE_LAUNCH_DEC(kern, grid)                                                                   \
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, A, M, B0, B1, C, offsets, mtile_start, E, N, K, \
-                     static_cast<const int32_t*>(nullptr), MxScales{})
+// Kernel per GEMM, measured on MI355X with the real per-expert row counts of the
+// Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped and latent layers (one box, one run):
+//  - expert gate/up: the persistent wave-specialised LDS-DMA kernel, 128 x 128
+//    tiles, 8 MFMA waves (against one workgroup per tile: Qwen3-shaped 303 -> 271 us,
+//    R1-shaped 4.66 -> 4.45 ms, latent equal; against 256-row tiles with every wave
+//    loading, faster on both of the first two); one workgroup per tile (n-tiles in
+//    pairs from 16 n-tiles on) when the persistent kernel's tile table does not fit;
+//  - expert down: the persistent wave-specialised kernel.  128 x 256 tiles (half
+//    the re-reads of the intermediate rows) when K < 2048 or the experts average
+//    at least 192 rows: Qwen3-shaped (K = 768, 256 rows) 174 us against 189 us for
+//    the register-staged kernel at three waves per SIMD and 187 / 208 us for
+//    256 x 128 / 128 x 128 persistent tiles; R1-shaped (K = 2048, 256 rows) 2.30 ms
+//    against 2.61 ms on 256 x 128 tiles.  Otherwise 256 x 128 tiles for K >= 2048
+//    (latent-shaped, 128 rows: 0.89 ms against 0.94 ms on 128 x 256 tiles; R1-shaped
+//    2.61 -> 2.46 ms against one workgroup per tile), and the register-staged
+//    kernel when no persistent tile table fits;
+//  - dense latent projections (one group): wave-specialised kernel with
+//    256 x 128 tiles (one tile row per 256 tokens fills 256 CUs in one pass).
+GemmChoice choose_gemm(GemmKind kind, bool swiglu, bool grouped, bool f8, int M, int E, int N, int K) {
+  if (kind == GEMM_SIMT)
+    return {GV_SIMT, 64, 64, false, swiglu ? "k_gemm_simt<float, 2," : "k_gemm_simt<float, 1,"};
+  if (kind == GEMM_DECODE) {
+    if (swiglu) return {f8 ? GV_DECODE_SWIGLU_F8 : GV_DECODE_SWIGLU, 16, 128, false, "k_gemm_decode<2, 2,"};
+    return {GV_DECODE, 16, 128, false, "k_gemm_decode<1, 2,"};
+  }
+  if (!grouped) return {GV_WS_256x128, 256, 128, false, "k_gemm_ws<256, 128, 1,"};
+  if (swiglu) {
+    const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
+    const bool fits = f8 ? wsp_fits<true>(tiles, M, 128, E, N, K) : wsp_fits<false>(tiles, M, 128, E, N, K);
+    if (fits) return {f8 ? GV_WSP_128x128_SWIGLU_F8 : GV_WSP_128x128_SWIGLU, 128, 128, true, "k_gemm_wsp<128, 128, 2,"};
+    if (ceil_div(N, 128) >= 16)
+      return {f8 ? GV_WS_128x128_SWIGLU_PAIRS_F8 : GV_WS_128x128_SWIGLU_PAIRS, 128, 128, false, "k_gemm_ws<128, 128, 2,"};
+    return {f8 ? GV_WS_128x128_SWIGLU_F8 : GV_WS_128x128_SWIGLU, 128, 128, false, "k_gemm_ws<128, 128, 2,"};
+  }
+  if (f8) return {GV_NONE, 0, 0, false, "none"};  // MXFP8 operands feed the gate/up GEMM only
+  if (K < 2048 || (long)M >= 192L * E) {
+    const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 256);
+    if (wsp_fits<false>(tiles, M, 128, E, N, K)) return {GV_WSP_128x256, 128, 256, true, "k_gemm_wsp<128, 256, 1,"};
+  }
+  if (K >= 2048) {
+    const long tiles = (long)max_mtiles(M, E, 256) * ceil_div(N, 128);
+    if (wsp_fits<false>(tiles, M, 256, E, N, K)) return {GV_WSP_256x128, 256, 128, true, "k_gemm_wsp<256, 128, 1,"};
+    return {GV_WS_256x128, 256, 128, false, "k_gemm_ws<256, 128, 1,"};
+  }
+  return {GV_PREFILL_128x128, 128, 128, false, "k_gemm_prefill<128, 128, 1,"};
+}
 
 bool gemm_gather_ok(int M, int E, int N, int K, bool mx) {
-  const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
-  return mx ? wsp_fits<true>(tiles, E, N, K) : wsp_fits<false>(tiles, E, N, K);
+  return choose_gemm(GEMM_PREFILL, true, true, mx, M, E, N, K).persistent;
 }
+
+// The persistent kernels' claim counters: slots 0-7 for the gate/up GEMM, 8-15 for the
+// down GEMM, after the two m-tile tables.
+static inline int32_t* claim_slots(const int32_t* mtile_start, int E, bool down) {
+  return const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + (down ? 8 : 0);
+}
+
+#define MOE_WSP(BM_, BN_, NB_, EPI_, F8_, a_, b0_, b1_, mt_, mx_, gather_)                                   \
+  hipLaunchKernelGGL((k_gemm_wsp<BM_, BN_, NB_, EPI_, 3, 8, F8_>), dim3(256), dim3(8 * 64 + 192), 0, st, a_, \
+                     M, b0_, b1_, C, offsets, mt_, E, N, K, mx_, claim_slots(mtile_start, E, NB_ == 1),    \
+                     gather_)
+#define MOE_WS(BM_, G_, NB_, EPI_, F8_, a_, b0_, b1_, mt_, grid_, mx_)                                        \
+  hipLaunchKernelGGL((k_gemm_ws<BM_, 128, NB_, EPI_, 3, 8, 64, G_, F8_>), dim3(grid_), dim3(8 * 64 + 128), 0,  \
+                     st, a_, M, b0_, b1_, C, offsets, mt_, E, N, K, mx_)
+#define MOE_DEC(NB_, EPI_, F8_, a_, b0_, b1_, gather_, mx_)                                                 \
+  hipLaunchKernelGGL((k_gemm_decode<NB_, 2, EPI_, F8_>), dim3(grid_for(max_mtiles(M, E, 16), N, 128)),       \
+                     dim3(256), 0, st, a_, M, b0_, b1_, C, offsets, mtile_start, E, N, K, gather_, mx_)
 
 hipError_t launch_gemm_prefill_gather(int epi, const uint16_t* X, const int32_t* gather, int M,
                                       const uint16_t* B0, const uint16_t* B1, void* C,
                                       const int32_t* offsets, const int32_t* mtile_start, int E, int N,
                                       int K, hipStream_t st) {
   if (!gather || !gemm_gather_ok(M, E, N, K, false)) return hipErrorInvalidValue;
-  int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
-  const dim3 bb(8 * 64 + 128);
   if (epi == EPI_SWIGLU_BF16)
-    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, X, M, B0, B1, C,
-                       offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
+    MOE_WSP(128, 128, 2, EPI_SWIGLU_BF16, false, X, B0, B1, mtile_start, MxScales{}, gather);
   else if (epi == EPI_SWIGLU_F32)
-    hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, X, M, B0, B1, C,
-                       offsets, mtile_start, E, N, K, MxScales{}, claim, gather);
+    MOE_WSP(128, 128, 2, EPI_SWIGLU_F32, false, X, B0, B1, mtile_start, MxScales{}, gather);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -1269,125 +1324,65 @@ hipError_t launch_gemm_bf16(GemmKind kind, int epi, const uint16_t* A, int M, co
                             const uint16_t* B1, void* C, const int32_t* offsets,
                             const int32_t* mtile_start, int E, int N, int K, hipStream_t st) {
   const bool swiglu = epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_F32;
-  if (kind == GEMM_PREFILL) {
-    // Kernel per GEMM, measured on MI355X with the real per-expert row counts of the
-    // Qwen3-30B-A3B-shaped, DeepSeek-R1-shaped and latent layers (one box, one run):
-    //  - expert gate/up: the persistent wave-specialised LDS-DMA kernel, 128 x 128
-    //    tiles, 8 MFMA waves (against one workgroup per tile: Qwen3-shaped 303 -> 271 us,
-    //    R1-shaped 4.66 -> 4.45 ms, latent equal; against 256-row tiles with every wave
-    //    loading, faster on both of the first two);
-    //  - expert down: the persistent wave-specialised kernel.  128 x 256 tiles (half
-    //    the re-reads of the intermediate rows) when K < 2048 or the experts average
-    //    at least 192 rows: Qwen3-shaped (K = 768, 256 rows) 174 us against 189 us for
-    //    the register-staged kernel at three waves per SIMD and 187 / 208 us for
-    //    256 x 128 / 128 x 128 persistent tiles; R1-shaped (K = 2048, 256 rows) 2.30 ms
-    //    against 2.61 ms on 256 x 128 tiles.  Otherwise 256 x 128 tiles for K >= 2048
-    //    (latent-shaped, 128 rows: 0.89 ms against 0.94 ms on 128 x 256 tiles; R1-shaped
-    //    2.61 -> 2.46 ms against one workgroup per tile), and the register-staged
-    //    kernel when no persistent tile table fits;
-    //  - dense latent projections (one group): wave-specialised kernel with
-    //    256 x 128 tiles (one tile row per 256 tokens fills 256 CUs in one pass).
-    if (!offsets) {
-      const dim3 g(grid_for(ceil_div(M, 256), N, 128)), b(8 * 64 + 128);
-      if (epi == EPI_BF16)
-        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
-                           offsets, mtile_start, E, N, K, MxScales{});
-      else if (epi == EPI_F32)
-        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), g, b, 0, st, A, M, B0, B1, C,
-                           offsets, mtile_start, E, N, K, MxScales{});
+  if (kind == GEMM_SIMT || (!offsets && swiglu)) return hipErrorInvalidValue;
+  if (swiglu ? !(epi == EPI_SWIGLU_BF16 || epi == EPI_SWIGLU_F32) : !(epi == EPI_BF16 || epi == EPI_F32))
+    return hipErrorInvalidValue;
+  const GemmChoice c = choose_gemm(kind, swiglu, offsets != nullptr, false, M, E, N, K);
+  const int32_t* no_gather = nullptr;
+  const int32_t* mt256 = offsets ? mtile_start + E + 1 : nullptr;  // second m-tile table (256-row tiles)
+  const bool f32 = epi == EPI_F32 || epi == EPI_SWIGLU_F32;
+  switch (c.v) {
+    case GV_WSP_128x128_SWIGLU:
+      if (f32) MOE_WSP(128, 128, 2, EPI_SWIGLU_F32, false, A, B0, B1, mtile_start, MxScales{}, no_gather);
+      else MOE_WSP(128, 128, 2, EPI_SWIGLU_BF16, false, A, B0, B1, mtile_start, MxScales{}, no_gather);
+      break;
+    case GV_WS_128x128_SWIGLU_PAIRS: {
+      const int g = grid_for(max_mtiles(M, E, 128), N, 128);
+      if (f32) MOE_WS(128, 2, 2, EPI_SWIGLU_F32, false, A, B0, B1, mtile_start, g, MxScales{});
+      else MOE_WS(128, 2, 2, EPI_SWIGLU_BF16, false, A, B0, B1, mtile_start, g, MxScales{});
+      break;
+    }
+    case GV_WS_128x128_SWIGLU: {
+      const int g = grid_for(max_mtiles(M, E, 128), N, 128);
+      if (f32) MOE_WS(128, 1, 2, EPI_SWIGLU_F32, false, A, B0, B1, mtile_start, g, MxScales{});
+      else MOE_WS(128, 1, 2, EPI_SWIGLU_BF16, false, A, B0, B1, mtile_start, g, MxScales{});
+      break;
+    }
+    case GV_WSP_128x256:
+      if (f32) MOE_WSP(128, 256, 1, EPI_F32, false, A, B0, B1, mtile_start, MxScales{}, no_gather);
+      else MOE_WSP(128, 256, 1, EPI_BF16, false, A, B0, B1, mtile_start, MxScales{}, no_gather);
+      break;
+    case GV_WSP_256x128:
+      if (f32) MOE_WSP(256, 128, 1, EPI_F32, false, A, B0, B1, mt256, MxScales{}, no_gather);
+      else MOE_WSP(256, 128, 1, EPI_BF16, false, A, B0, B1, mt256, MxScales{}, no_gather);
+      break;
+    case GV_WS_256x128: {
+      // grouped: 256-row tiles on the second m-tile table; dense: one group of M rows
+      const int g = grid_for(offsets ? max_mtiles(M, E, 256) : ceil_div(M, 256), N, 128);
+      if (f32) MOE_WS(256, 1, 1, EPI_F32, false, A, B0, B1, mt256, g, MxScales{});
+      else MOE_WS(256, 1, 1, EPI_BF16, false, A, B0, B1, mt256, g, MxScales{});
+      break;
+    }
+    case GV_PREFILL_128x128: {
+      const dim3 g(grid_for(max_mtiles(M, E, 128), N, 128));
+      if (f32)
+        hipLaunchKernelGGL((k_gemm_prefill<128, 128, 1, EPI_F32, 3>), g, dim3(256), 0, st, A, M, B0, B1, C,
+                           offsets, mtile_start, E, N, K);
       else
-        return hipErrorInvalidValue;
-      return hipGetLastError();
+        hipLaunchKernelGGL((k_gemm_prefill<128, 128, 1, EPI_BF16, 3>), g, dim3(256), 0, st, A, M, B0, B1, C,
+                           offsets, mtile_start, E, N, K);
+      break;
     }
-    const int g = grid_for(max_mtiles(M, E, 128), N, 128);
-    if (swiglu) {
-      const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
-      const dim3 bb(8 * 64 + 128);
-      if (wsp_fits<false>(tiles, E, N, K)) {
-        // persistent wave-specialised kernel (256 workgroups, one per CU)
-        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
-        if (epi == EPI_SWIGLU_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1,
-                             C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        else
-          hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1,
-                             C, offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        return hipGetLastError();
-      }
-      // one workgroup per tile; n-tiles in pairs when there are 16 or more of them
-      const dim3 gb(g);
-      const bool pairs = ceil_div(N, 128) >= 16;
-      if (epi == EPI_SWIGLU_BF16) {
-        if (pairs)
-          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
-                             B0, B1, C, offsets, mtile_start, E, N, K, MxScales{});
-        else
-          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8>), gb, bb, 0, st, A, M, B0,
-                             B1, C, offsets, mtile_start, E, N, K, MxScales{});
-      } else {
-        if (pairs)
-          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8, 64, 2>), gb, bb, 0, st, A, M,
-                             B0, B1, C, offsets, mtile_start, E, N, K, MxScales{});
-        else
-          hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_F32, 3, 8>), gb, bb, 0, st, A, M, B0,
-                             B1, C, offsets, mtile_start, E, N, K, MxScales{});
-      }
-      return hipGetLastError();
-    }
-    // down GEMM: 128 x 256 persistent tiles when K is short or the experts average
-    // at least 192 rows, when the tile table fits
-    if (K < 2048 || (long)M >= 192L * E) {
-      const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 256);
-      if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
-        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
-        if (epi == EPI_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        else
-          hipLaunchKernelGGL((k_gemm_wsp<128, 256, 1, EPI_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mtile_start, E, N, K, MxScales{}, claim, nullptr);
-        return hipGetLastError();
-      }
-    }
-    if (K >= 2048) {  // down GEMM with a long K: 256-row tiles (second m-tile table)
-      const int32_t* mt256 = mtile_start + E + 1;
-      const long tiles = (long)max_mtiles(M, E, 256) * ceil_div(N, 128);
-      const dim3 bb(8 * 64 + 128);
-      if (wsp_fits<false>(tiles, E, N, K) && (epi == EPI_BF16 || epi == EPI_F32)) {
-        int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1) + 8;
-        if (epi == EPI_BF16)
-          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_BF16, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
-        else
-          hipLaunchKernelGGL((k_gemm_wsp<256, 128, 1, EPI_F32, 3, 8>), dim3(256), dim3(8 * 64 + 192), 0, st, A, M, B0, B1, C,
-                             offsets, mt256, E, N, K, MxScales{}, claim, nullptr);
-        return hipGetLastError();
-      }
-      const dim3 gb(grid_for(max_mtiles(M, E, 256), N, 128));
-      if (epi == EPI_BF16)
-        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_BF16, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
-                           offsets, mt256, E, N, K, MxScales{});
-      else if (epi == EPI_F32)
-        hipLaunchKernelGGL((k_gemm_ws<256, 128, 1, EPI_F32, 3, 8>), gb, bb, 0, st, A, M, B0, B1, C,
-                           offsets, mt256, E, N, K, MxScales{});
-      else
-        return hipErrorInvalidValue;
-      return hipGetLastError();
-    }
-    switch (epi) {
-      case EPI_BF16: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_BF16, 3>), g); break;
-      case EPI_F32: MOE_LAUNCH((k_gemm_prefill<128, 128, 1, EPI_F32, 3>), g); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
-    switch (epi) {
-      case EPI_SWIGLU_BF16: MOE_LAUNCH_DEC((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), g); break;
-      case EPI_SWIGLU_F32: MOE_LAUNCH_DEC((k_gemm_decode<2, 2, EPI_SWIGLU_F32>), g); break;
-      case EPI_BF16: MOE_LAUNCH_DEC((k_gemm_decode<1, 2, EPI_BF16>), g); break;
-      case EPI_F32: MOE_LAUNCH_DEC((k_gemm_decode<1, 2, EPI_F32>), g); break;
-      default: return hipErrorInvalidValue;
-    }
+    case GV_DECODE_SWIGLU:
+      if (f32) MOE_DEC(2, EPI_SWIGLU_F32, false, A, B0, B1, no_gather, MxScales{});
+      else MOE_DEC(2, EPI_SWIGLU_BF16, false, A, B0, B1, no_gather, MxScales{});
+      break;
+    case GV_DECODE:
+      if (f32) MOE_DEC(1, EPI_F32, false, A, B0, B1, no_gather, MxScales{});
+      else MOE_DEC(1, EPI_BF16, false, A, B0, B1, no_gather, MxScales{});
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -1422,46 +1417,42 @@ hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* 
                                      const uint16_t* B0, const uint16_t* B1, void* C,
                                      const int32_t* offsets, const int32_t* mtile_start, int E, int N,
                                      int K, hipStream_t st) {
-  const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
-  if (epi == EPI_SWIGLU_BF16)
-    hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16>), dim3(g), dim3(256), 0, st, X, M, B0, B1, C,
-                       offsets, mtile_start, E, N, K, gather, MxScales{});
-  else
-    return hipErrorInvalidValue;
+  if (epi != EPI_SWIGLU_BF16) return hipErrorInvalidValue;
+  MOE_DEC(2, EPI_SWIGLU_BF16, false, X, B0, B1, gather, MxScales{});
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_mx_swiglu(GemmKind kind, const uint8_t* A, int M, const uint8_t* B0, const uint8_t* B1,
                                  uint16_t* C, const int32_t* offsets, const int32_t* mtile_start, int E,
                                  int N, int D, MxScales mx, const int32_t* gather, hipStream_t st) {
-  if (D % 128) return hipErrorInvalidValue;
+  if (D % 128 || (kind != GEMM_PREFILL && kind != GEMM_DECODE)) return hipErrorInvalidValue;
   const uint16_t* a = reinterpret_cast<const uint16_t*>(A);
   const uint16_t* b0 = reinterpret_cast<const uint16_t*>(B0);
   const uint16_t* b1 = reinterpret_cast<const uint16_t*>(B1);
   const int K = D / 2;  // codes travel as 16-bit pairs
-  if (kind == GEMM_PREFILL) {
-    const long tiles = (long)max_mtiles(M, E, 128) * ceil_div(N, 128);
-    const dim3 bb(8 * 64 + 128);
-    if (gather && !gemm_gather_ok(M, E, N, K, true)) return hipErrorInvalidValue;
-    if (wsp_fits<true>(tiles, E, N, K)) {
-      int32_t* claim = const_cast<int32_t*>(mtile_start) + 2 * (E + 1);
-      hipLaunchKernelGGL((k_gemm_wsp<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, true>), dim3(256), dim3(8 * 64 + 192), 0, st, a, M, b0, b1,
-                         C, offsets, mtile_start, E, N, K, mx, claim, gather);
-    } else {
-      const dim3 gb(grid_for(max_mtiles(M, E, 128), N, 128));
-      if (ceil_div(N, 128) >= 16)
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 2, true>), gb, bb, 0, st, a, M,
-                           b0, b1, C, offsets, mtile_start, E, N, K, mx);
-      else
-        hipLaunchKernelGGL((k_gemm_ws<128, 128, 2, EPI_SWIGLU_BF16, 3, 8, 64, 1, true>), gb, bb, 0, st, a, M,
-                           b0, b1, C, offsets, mtile_start, E, N, K, mx);
-    }
-  } else {
-    const int g = grid_for(max_mtiles(M, E, 16), N, 4 * 16 * 2);
-    hipLaunchKernelGGL((k_gemm_decode<2, 2, EPI_SWIGLU_BF16, true>), dim3(g), dim3(256), 0, st, a, M, b0, b1,
-                       C, offsets, mtile_start, E, N, K, gather, mx);
+  const GemmChoice c = choose_gemm(kind, true, true, true, M, E, N, K);
+  if (gather && kind == GEMM_PREFILL && !c.persistent) return hipErrorInvalidValue;
+  switch (c.v) {
+    case GV_WSP_128x128_SWIGLU_F8:
+      MOE_WSP(128, 128, 2, EPI_SWIGLU_BF16, true, a, b0, b1, mtile_start, mx, gather);
+      break;
+    case GV_WS_128x128_SWIGLU_PAIRS_F8:
+      MOE_WS(128, 2, 2, EPI_SWIGLU_BF16, true, a, b0, b1, mtile_start, grid_for(max_mtiles(M, E, 128), N, 128), mx);
+      break;
+    case GV_WS_128x128_SWIGLU_F8:
+      MOE_WS(128, 1, 2, EPI_SWIGLU_BF16, true, a, b0, b1, mtile_start, grid_for(max_mtiles(M, E, 128), N, 128), mx);
+      break;
+    case GV_DECODE_SWIGLU_F8:
+      MOE_DEC(2, EPI_SWIGLU_BF16, true, a, b0, b1, gather, mx);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+
+#undef MOE_WSP
+#undef MOE_WS
+#undef MOE_DEC
 
 }  // namespace moe

@@ -233,6 +233,59 @@ moe_status dense_proj(const Dims& d, const void* A, const void* W, void* C, int 
   return MOE_OK;
 }
 
+// Every decision moe_layer_forward takes from the shape and from which optional buffers
+// the caller passes; moe_layer_plan reports the same struct.
+struct LayerPlan {
+  GemmKind kind;
+  bool small;  // decode-scale routing in one launch, gate/up reading the token rows
+  bool gath;   // larger steps: the permutation writes metadata only, gate/up gathers the rows
+  GemmChoice gate_up, down, shared_gate_up, shared_down;
+  int launches;
+};
+
+LayerPlan plan_layer(const Dims& d, bool gate_computed, bool want_xperm, bool want_xperm_scale) {
+  LayerPlan p{};
+  p.kind = expert_kind(d);
+  // Decode-scale steps (16-row expert tiles, T <= kSmallT): routing, counts, offsets,
+  // tile tables and row metadata in one launch, and the gate/up GEMM reads its rows
+  // straight from the token rows through row_token (no permuted copy unless the
+  // caller asks for it in aux.x_perm).  With MXFP8 dispatch the token rows are
+  // quantised once and read the same way; a caller who asks for the permuted codes
+  // gets the general path.
+  p.small = p.kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (want_xperm || want_xperm_scale));
+  // Larger steps: unless the caller asks for the permuted rows, the permutation writes
+  // only the row metadata and the gate/up GEMM reads the token rows through row_token
+  // (decode-sized tiles always can; the persistent prefill kernel when its tile table
+  // fits).  The GEMM sees the same rows in the same order, so the results are the same
+  // bits as with the permuted copy.
+  p.gath = !p.small && d.bf16 && !want_xperm && !(d.mx && want_xperm_scale) &&
+           (p.kind == GEMM_DECODE ||
+            (p.kind == GEMM_PREFILL && gemm_gather_ok(d.R, d.E, d.I, d.mx ? d.D / 2 : d.D, d.mx)));
+  p.gate_up = choose_gemm(p.kind, true, true, d.mx, d.R, d.E, d.I, d.mx ? d.D / 2 : d.D);
+  p.down = choose_gemm(p.kind, false, true, false, d.R, d.E, d.D, d.I);
+  int n = 0;
+  if (d.L) n += 1;                            // latent down-projection
+  if (gate_computed) n += 1;                  // gate scores (split-K slices summed by the top-k kernel)
+  if (p.small) {
+    n += 1;                                   // routing, counts, offsets, tile tables, row metadata
+    if (d.mx || want_xperm) n += 1;           // token rows quantised once / permuted copy on request
+  } else {
+    n += 3;                                   // top-k + counts, expert scan, permutation
+    if (p.gath && d.mx) n += 1;               // token rows quantised once
+  }
+  n += 2;                                     // expert gate/up and down GEMMs
+  if (d.Is) {
+    const Dims ds = shared_dims(d);
+    p.shared_gate_up = choose_gemm(expert_kind(ds), true, true, false, ds.R, 1, ds.I, ds.D);
+    p.shared_down = choose_gemm(expert_kind(ds), false, true, false, ds.R, 1, ds.D, ds.I);
+    n += 3;                                   // its one-group table and two GEMMs
+  }
+  n += 1;                                     // combine
+  if (d.L) n += 1;                            // latent up-projection
+  p.launches = n;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +314,28 @@ size_t moe_workspace_bytes(const moe_shape* s, int call) {
     case MOE_CALL_LAYER: return layer_ws(d).total;
     default: return 0;
   }
+}
+
+moe_status moe_layer_plan(const moe_shape* s, int flags, moe_plan* out) {
+  Dims d;
+  moe_status rc = check_shape(s, d);
+  if (rc != MOE_OK) return rc;
+  if (!out || (flags & ~(MOE_PLAN_GATE | MOE_PLAN_X_PERM))) return MOE_ERR_INVALID_ARG;
+  const bool xp = (flags & MOE_PLAN_X_PERM) != 0;
+  const LayerPlan p = plan_layer(d, (flags & MOE_PLAN_GATE) != 0, xp, xp && d.mx);
+  *out = moe_plan{};
+  out->launches = p.launches;
+  out->decode_path = p.small;
+  out->rows_gathered = p.small || p.gath;
+  out->gate_up_tile_m = p.gate_up.bm;
+  out->gate_up_tile_n = p.gate_up.bn;
+  out->gate_up_persistent = p.gate_up.persistent;
+  out->down_tile_m = p.down.bm;
+  out->down_tile_n = p.down.bn;
+  out->down_persistent = p.down.persistent;
+  out->gate_up_kernel = p.gate_up.kernel;
+  out->down_kernel = p.down.kernel;
+  return MOE_OK;
 }
 
 moe_status moe_route_topk(const void* x, const float* gate_w, const float* gate_bias,
@@ -419,7 +494,8 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     return !stage_events || !stage_events[i] ||
            hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), st) == hipSuccess;
   };
-  const GemmKind kind = expert_kind(d);
+  const LayerPlan plan = plan_layer(d, wt->gate_w != nullptr, ax.x_perm != nullptr, ax.x_perm_scale != nullptr);
+  const GemmKind kind = plan.kind;
 
   if (!ev(0)) return MOE_ERR_HIP;
   if (d.L) {  // a7: Z = X wd^T (rounded to the layer dtype)
@@ -435,21 +511,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   if (!ev(2)) return MOE_ERR_HIP;
   const void* src = d.L ? z : x;  // the rows that are dispatched
   const int row16 = d.D * d.es / 16;
-  // Decode-scale steps (16-row expert tiles, T <= kSmallT): routing, counts, offsets,
-  // tile tables and row metadata in one launch, and the gate/up GEMM reads its rows
-  // straight from the token rows through row_token (no permuted copy unless the
-  // caller asks for it in aux.x_perm).  With MXFP8 dispatch the token rows are
-  // quantised once and read the same way; a caller who asks for the permuted codes
-  // gets the general path.
-  const bool small = kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (ax.x_perm || ax.x_perm_scale));
-  // Larger steps: unless the caller asks for the permuted rows, the permutation writes
-  // only the row metadata and the gate/up GEMM reads the token rows through row_token
-  // (decode-sized tiles always can; the persistent prefill kernel when its tile table
-  // fits).  The GEMM sees the same rows in the same order, so the results are the same
-  // bits as with the permuted copy.
-  const bool gath = !small && d.bf16 && !ax.x_perm && !(d.mx && ax.x_perm_scale) &&
-                    (kind == GEMM_DECODE ||
-                     (kind == GEMM_PREFILL && gemm_gather_ok(d.R, d.E, d.I, d.mx ? d.D / 2 : d.D, d.mx)));
+  const bool small = plan.small, gath = plan.gath;
   const bool rows_from_tokens = small || gath;
   uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
   uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;

@@ -32,6 +32,35 @@ struct MxScales {
   const uint8_t* b1;
 };
 
+// The kernel (and tile shape) one GEMM runs on; choose_gemm is the single place that
+// decides it, for the launchers and for the host-side plan query alike.
+enum GemmVariant {
+  GV_NONE = 0,
+  GV_WSP_128x128_SWIGLU,           // persistent, gate/up
+  GV_WS_128x128_SWIGLU_PAIRS,      // one workgroup per tile, n-tiles in pairs
+  GV_WS_128x128_SWIGLU,            // one workgroup per tile
+  GV_WSP_128x256,                  // persistent, down
+  GV_WSP_256x128,                  // persistent, down with a long K (256-row m-tile table)
+  GV_WS_256x128,                   // one workgroup per tile, long-K down or dense projection
+  GV_PREFILL_128x128,              // register-staged, down
+  GV_DECODE_SWIGLU,                // 16-row tiles, gate/up
+  GV_DECODE,                       // 16-row tiles, down
+  GV_SIMT,                         // fp32
+  GV_WSP_128x128_SWIGLU_F8,        // MXFP8 gate/up variants of the above
+  GV_WS_128x128_SWIGLU_PAIRS_F8,
+  GV_WS_128x128_SWIGLU_F8,
+  GV_DECODE_SWIGLU_F8
+};
+struct GemmChoice {
+  GemmVariant v;
+  int bm, bn;          // workgroup tile
+  bool persistent;     // one workgroup per CU claiming tiles
+  const char* kernel;  // the kernel's name up to its tile arguments, as a trace prints it
+};
+// swiglu: the gate/up GEMM (two weight matrices); grouped: per-expert row groups (else one
+// dense group of M rows); f8: MXFP8 operands (K counts 16-bit code pairs).
+GemmChoice choose_gemm(GemmKind kind, bool swiglu, bool grouped, bool f8, int M, int E, int N, int K);
+
 int gemm_bm(GemmKind kind);
 int max_mtiles(int M, int E, int bm);
 

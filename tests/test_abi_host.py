@@ -164,3 +164,46 @@ def test_other_calls_reject_bad_arguments_on_host():
     ss = B.shape(64, 128, 8, 2, 256, shared_I=128)
     assert L.moe_layer_forward(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(ss), ctypes.byref(aux),
                                None, FAKE, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_layer_plan_names_the_kernels_of_each_layer():
+    """The host-only plan query reports the decision moe_layer_forward takes."""
+    want = {  # layer: (decode path, rows gathered, gate/up kernel, down kernel, launches)
+        "qwen3_30b_a3b_shaped": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<128, 256, 1,", 7),
+        "deepseek_r1_shaped": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<128, 256, 1,", 7),
+        "latent_moe": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<256, 128, 1,", 9),
+        "k3_shaped_decode_t8": (1, 1, "k_gemm_decode<2, 2,", "k_gemm_decode<1, 2,", 4),
+        "tiny_f32": (0, 0, "k_gemm_simt<float, 2,", "k_gemm_simt<float, 1,", 6),
+    }
+    for name, (dec, gath, gu, dn, n) in want.items():
+        c = FULL_CONFIGS[name]
+        p = B.layer_plan(B.shape(c.T, c.H, c.E, c.k, c.I, c.L, c.dtype, c.shared_I, c.capacity),
+                         c.gate == "computed")
+        assert (p["decode_path"], p["rows_gathered"], p["gate_up_kernel"], p["down_kernel"],
+                p["launches"]) == (dec, gath, gu, dn, n), name
+    # asking for the permuted copy turns the gathered dataflow off (one more launch on
+    # the decode path, the same count elsewhere: the permutation writes the rows)
+    c = FULL_CONFIGS["qwen3_30b_a3b_shaped"]
+    s = B.shape(c.T, c.H, c.E, c.k, c.I)
+    assert B.layer_plan(s, True, x_perm=True)["rows_gathered"] == 0
+    with pytest.raises(B.MoeError):
+        B.layer_plan(B.shape(0, 128, 8, 2, 256), True)
+    assert B.lib.moe_layer_plan(ctypes.byref(s), 8, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_persistent_tile_table_fields_bound_the_expert_rows():
+    """A persistent-GEMM table entry keeps an expert's m-tile index in 12 bits, so a
+    layer in which one expert may hold more than 4096 m-tiles of rows (E = 1, k = 1,
+    T > 4096 * 128) must take the one-workgroup-per-tile kernels instead."""
+    at = B.layer_plan(B.shape(4096 * 128, 256, 1, 1, 128), False)
+    assert at["gate_up_persistent"] == 1 and at["gate_up_kernel"] == "k_gemm_wsp<128, 128, 2,"
+    over = B.layer_plan(B.shape(4096 * 128 + 1, 256, 1, 1, 128), False)
+    assert over["gate_up_persistent"] == 0 and over["gate_up_kernel"] == "k_gemm_ws<128, 128, 2,"
+    assert over["rows_gathered"] == 0            # gathering needs the persistent kernel
+    assert over["down_persistent"] == 0
+    # the down GEMM's 128 x 256 tiles meet the bound first (K >= 2048: the 256-row tiles
+    # come next, with the same bound on 256-row m-tiles)
+    at = B.layer_plan(B.shape(4096 * 256, 128, 1024, 1, 2048), False)
+    assert at["down_kernel"] == "k_gemm_wsp<256, 128, 1," and at["down_persistent"] == 1
+    over = B.layer_plan(B.shape(4096 * 256 + 256, 128, 1024, 1, 2048), False)
+    assert over["down_kernel"] == "k_gemm_ws<256, 128, 1," and over["down_persistent"] == 0
