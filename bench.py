@@ -7,15 +7,19 @@ HBM before timing starts.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-The default workload is the Qwen3-30B-A3B-shaped layer (T=4096, H=2048,
-E=128, k=8, I=768, bf16).  Other configs: deepseek_r1_shaped,
-k3_shaped_decode, latent_moe, tiny_f32, deepseek_r1_shaped_shared (the
-R1-shaped layer with a shared expert of width 2048).
+The default workload is the largest layer, DeepSeek-R1-shaped (T=8192,
+H=7168, E=256, k=8, I=2048, bf16, Zipf-skewed routing).  Other configs:
+qwen3_30b_a3b_shaped, k3_shaped_decode, k3_shaped_decode_t8, latent_moe,
+tiny_f32, deepseek_r1_shaped_shared (the R1-shaped layer with a shared
+expert of width 2048).
 
 Per-stage times come from HIP events that moe_layer_forward records on the
 stream the kernels run on.  The roofline object describes the dominant kernel
-(the expert gate/up GEMM): algorithmic bytes per launch over its average
-event-timed duration, against MI355X's 8 TB/s HBM peak.  cpu_baseline is the
+(the expert gate/up GEMM): algorithmic bytes per launch (the compulsory bytes:
+touched experts' W1 and W3, one input row per routed assignment, the
+intermediate written) over its average event-timed duration, against
+MI355X's 8 TB/s HBM peak.  Which kernels run is the library's own decision,
+read from moe_layer_plan.  cpu_baseline is the
 CPU oracle (tests' reference implementation) timed on a bounded token sample of
 the same layer on this host's cores.
 
@@ -24,6 +28,8 @@ Besides the contract's back-to-back steps, the line carries:
                   the 256 MB last-level cache (median / p95 of event times);
   combine_alone   moe_combine on its own, fused and as the unpermute +
                   weighted-reduce pair;
+  permute_alone   moe_dispatch_permute on its own, writing the T*k*D*b
+                  permuted copy (the fused layer writes only row metadata);
   ep_rank_share   (--ep-rank-share R) the grouped expert FFN at the share one
                   rank of R-way expert parallelism would run: R source batches
                   routed on this GPU, the rows of experts [0, E/R) gathered.
@@ -97,31 +103,24 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def rows_from_tokens(cfg):
-    """Whether moe_layer_forward (called without aux x_perm, as here) feeds the gate/up
-    GEMM the token rows through row_token instead of a permuted copy: every bf16 layer
-    on decode-sized tiles, and on the persistent 128-row tiles when the library's
-    condition holds (the XCD chunk of tiles fits the LDS table, at least 4 K-steps)."""
-    if cfg.dtype != "bf16":
-        return False
-    if cfg.R < 48 * cfg.E:
-        return True                                   # decode-sized tiles
-    mx = cfg.dispatch == "mxfp8"
-    K = cfg.D // 2 if mx else cfg.D                   # 16-bit columns (MXFP8 codes in pairs)
-    tiles = (cfg.R // 128 + min(cfg.E, cfg.R) + 1) * -(-cfg.I // 128)
-    cap = 2624 if mx else 3520
-    return (-(-tiles // 8) <= cap and cfg.E <= 1024 and -(-cfg.I // 128) <= 1024
-            and K % 64 == 0 and K // 64 >= 4)
+def layer_plan(B, cfg):
+    """The kernels moe_layer_forward runs for this layer (called without aux x_perm, as
+    here): the library's own decision, from moe_layer_plan."""
+    s = B.shape(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity,
+                cfg.dispatch)
+    return B.layer_plan(s, cfg.gate == "computed")
 
 
-def stage_bytes_flops(cfg, counts):
+def stage_bytes_flops(cfg, counts, gath):
     """Algorithmic HBM bytes and FLOPs per stage for one layer forward.
 
     b = element bytes of activations/weights; touched = experts with >= 1 row; the
     row count R is the rows kept (all T*k unless an expert capacity drops some).
-    When the gate/up GEMM reads the token rows through row_token (rows_from_tokens),
-    the permutation writes only the metadata and the GEMM's row bytes are those of
-    the T token rows (MXFP8: the quantised token rows, converted once per token).
+    gath: whether the gate/up GEMM reads the token rows through row_token (the plan's
+    rows_gathered); then the permutation writes only the metadata.  The gate/up GEMM's
+    bytes count one input row per routed assignment (R*D*b, the permuted operand it
+    multiplies), whichever way it fetches it; "gemm_gate_up_gathered" counts the T
+    token rows instead, the least a gathering kernel must fetch.
     """
     T, H, E, k, I, L, D = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.L, cfg.D
     R = int(sum(counts))
@@ -133,17 +132,16 @@ def stage_bytes_flops(cfg, counts):
     st["gate"] = ((T * H * b + E * H * 4 + T * E * 4, 2 * T * H * E) if cfg.gate == "computed"
                   else (0, 0))
     st["route"] = (T * E * 4 + 8 * R + (2 * E + 1) * 4, 0)
-    gath = rows_from_tokens(cfg)
     if cfg.dispatch == "mxfp8":
         # rows and W1 / W3 as one code byte per element plus one scale byte per 32
         q = D * 33 // 32
-        rows_q = T * q if gath else R * q
-        st["permute"] = (T * D * b + rows_q + 12 * R, 0)
-        st["gemm_gate_up"] = (touched * 2 * q * I + rows_q + R * I * b, 4 * R * D * I)
+        st["permute"] = (T * D * b + (T if gath else R) * q + 12 * R, 0)
+        st["gemm_gate_up"] = (touched * 2 * q * I + R * q + R * I * b, 4 * R * D * I)
+        st["gemm_gate_up_gathered"] = (touched * 2 * q * I + T * q + R * I * b, 4 * R * D * I)
     else:
         st["permute"] = ((12 * R, 0) if gath else (T * D * b + R * D * b + 12 * R, 0))
-        rows_b = (T if gath else R) * D * b
-        st["gemm_gate_up"] = (touched * 2 * D * I * b + rows_b + R * I * b, 4 * R * D * I)
+        st["gemm_gate_up"] = (touched * 2 * D * I * b + R * D * b + R * I * b, 4 * R * D * I)
+        st["gemm_gate_up_gathered"] = (touched * 2 * D * I * b + T * D * b + R * I * b, 4 * R * D * I)
     st["gemm_down"] = (touched * D * I * b + R * I * b + R * D * b, 2 * R * D * I)
     Is = cfg.shared_I
     st["shared_expert"] = ((T * H * b + 3 * Is * H * b + 2 * T * Is * b + T * H * b, 6 * T * H * Is)
@@ -153,10 +151,13 @@ def stage_bytes_flops(cfg, counts):
     return st, touched
 
 
-def event_stride(steps, samples=10):
-    """Every how many timed steps the gate/up GEMM's two events are recorded: about
-    `samples` launches sampled, every step when there are fewer steps than that."""
-    return max(1, steps // samples)
+def sampled_steps(steps, samples=4):
+    """The timed steps that record the two events around the gate/up GEMM: a fixed
+    number (`samples`), spread evenly over the timed region whatever its length, so the
+    idle time each event record adds between kernels stays a few microseconds per
+    sampled step."""
+    n = min(samples, steps)
+    return sorted({(i * steps) // n + (steps // n) // 2 for i in range(n)})
 
 
 def pct(vals, q):
@@ -191,6 +192,44 @@ def time_combine_alone(B, torch, cfg, w, x, logits, od, s, ws, counts, stream, h
         res[name] = round(hip.elapsed_ms(e[0], e[1]) / reps, 5)
         hip.destroy(e)
     return res
+
+
+def time_permute_alone(B, torch, cfg, w, x, logits, s, ws, stream, hip, reps=20):
+    """moe_dispatch_permute on its own, writing the T*k*D*b permuted copy of the rows the
+    layer dispatches (X, or Z for latent layers) on the layer's own routing: the call's
+    three launches (per-block counts, expert scan, permutation) and its algorithmic
+    bytes T*D*b + R*D*b + 12*R over the call time (mean ms per call over `reps`)."""
+    dev = x.device
+    act = torch.int16 if cfg.dtype == "bf16" else torch.float32
+    T, k, D, R = cfg.T, cfg.k, cfg.D, cfg.R
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    offs = torch.empty((cfg.E + 1,), dtype=torch.int32, device=dev)
+    aux = {"topk_ids": ids, "offsets": offs}
+    z = None
+    if cfg.L:
+        z = torch.empty((T, cfg.L), dtype=act, device=dev)
+        aux["z"] = z
+    out = torch.empty((T, cfg.H), dtype=torch.float32, device=dev)
+    B.layer_forward(w, x, logits, out, B.MOE_F32, s, ws, aux=aux, stream=stream)
+    src = z if cfg.L else x
+    xp = torch.empty((R, D), dtype=act, device=dev)
+    rt = torch.empty((R,), dtype=torch.int32, device=dev)
+    tr = torch.empty((T, k), dtype=torch.int32, device=dev)
+    sd = B.shape(T, cfg.H, cfg.E, k, cfg.I, cfg.L, cfg.dtype, cfg.shared_I, cfg.capacity)
+    wsd = torch.empty(max(B.workspace_bytes(sd, B.MOE_CALL_DISPATCH), 256), dtype=torch.uint8, device=dev)
+    B.dispatch_permute(src, ids, offs, xp, rt, tr, sd, wsd, stream=stream)
+    e = hip.create(2)
+    hip.record(e[0], stream)
+    for _ in range(reps):
+        B.dispatch_permute(src, ids, offs, xp, rt, tr, sd, wsd, stream=stream)
+    hip.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e[0], e[1]) / reps
+    hip.destroy(e)
+    kept = int(offs[-1].item())
+    byt = T * D * cfg.elem_bytes + kept * D * cfg.elem_bytes + 12 * R
+    return {"ms": round(ms, 5), "bytes": byt, "GB/s": round(byt / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def ep_rank_share(B, torch, np, gen, cfg, ranks, up, stream, hip, reps=10):
@@ -275,7 +314,7 @@ def cpu_baseline(cfg, inp, target_s):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = 1
-    n = min(64, cfg.T)
+    n = min(8, cfg.T)
     while True:
         sub = dict(inp)
         sub["x"] = inp["x"][:n]
@@ -319,32 +358,13 @@ def cpu_baseline(cfg, inp, target_s):
             "cpu_model": cpu, "blas": blas}
 
 
-def gate_up_kernel(cfg):
-    """Name of the kernel moe_grouped_ffn picks for the expert gate/up GEMM (the
-    library's choice: the persistent wave-specialised kernel on 128-row MFMA tiles
-    when the mean rows per expert reach 48, 16-row weight-streaming tiles below 48
-    rows, SIMT for fp32)."""
-    if cfg.dtype != "bf16":
-        return "k_gemm_simt<SwiGLU> (expert gate/up GEMM, fp32)"
-    mx = cfg.dispatch == "mxfp8"
-    if cfg.R >= 48 * cfg.E:
-        if mx:
-            return "k_gemm_wsp<128,128,2,SwiGLU,3,8,MXFP8> (expert gate/up GEMM, MXFP8, persistent)"
-        return "k_gemm_wsp<128,128,2,SwiGLU,3,8> (expert gate/up GEMM, persistent)"
-    if mx:
-        return "k_gemm_decode<2,2,SwiGLU,MXFP8> (expert gate/up GEMM, MXFP8)"
-    return "k_gemm_decode<2,2,SwiGLU> (expert gate/up GEMM)"
-
-
-DOMINANT_KERNEL_PATTERNS = ("k_gemm_prefill<128, 128, 2,", "k_gemm_wsp<128, 128, 2,", "k_gemm_ws<128, 128, 2,", "k_gemm_decode<2, 2,")
-
-
 def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cmd):
     """HBM bytes per launch of the expert gate/up GEMM from two rocprofv3 --pmc runs.
 
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are each scaled by what the same
     counter reads for the 1 GiB calibration copy (a plain device copy of known
-    size in the same run), then averaged over the GEMM's dispatches.
+    size in the same run), then averaged over the dispatches of the kernel the
+    library's plan names for the layer's gate/up GEMM.
     """
     import csv
 
@@ -357,9 +377,13 @@ def traffic_from_pmc(fetch_csv, write_csv, config, copy_mib, fetch_cmd, write_cm
 
     copy_bytes = copy_mib << 20
     mx = config.endswith("_mxfp8")   # the MXFP8 kernels carry a trailing "true" template argument
+    from routing_dispatch_expert_logits_amd import binding as B
+    from workloads import FULL_CONFIGS
+    cfg = FULL_CONFIGS[config[:-len("_mxfp8")] if mx else config]
+    kern = layer_plan(B, cfg.with_(dispatch="mxfp8") if mx else cfg)["gate_up_kernel"]
 
     def dominant(name):
-        return any(p in name for p in DOMINANT_KERNEL_PATTERNS) and (("true>" in name) == mx)
+        return kern in name and (("true>" in name) == mx)
 
     res = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -397,7 +421,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="qwen3_30b_a3b_shaped")
+    ap.add_argument("--config", default="deepseek_r1_shaped")
     ap.add_argument("--skew-steps", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -430,6 +454,7 @@ def main(argv=None):
         cfg = cfg.with_(capacity=int(np.ceil(args.capacity_factor * cfg.R / cfg.E)))
     if args.dispatch != "dtype":
         cfg = cfg.with_(dispatch=args.dispatch)
+    plan = layer_plan(B, cfg)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"bench: {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} L={cfg.L} {cfg.dtype}")
@@ -485,18 +510,18 @@ def main(argv=None):
     nev = B.MOE_NUM_STAGE_EVENTS
     names = B.STAGE_NAMES
     # The timed steps record only the two events around the expert gate/up GEMM (the
-    # dominant kernel the roofline object describes), and only on every `stride`-th
-    # step (about 10 sampled launches): every event record puts a few microseconds
-    # between the kernels either side of it.  The per-stage breakdown comes from a
-    # separate pass with every stage event, after the timed region.
+    # dominant kernel the roofline object describes), on a fixed handful of sampled
+    # steps whatever --steps is: every event record puts a few microseconds between
+    # the kernels either side of it.  The per-stage breakdown comes from a separate
+    # pass with every stage event, after the timed region.
     g = names.index("gemm_gate_up")
-    stride = event_stride(args.steps)
-    gev = [hip.create(2) for _ in range(0, args.steps, stride)]
+    sampled = sampled_steps(args.steps)
+    gev = [hip.create(2) for _ in sampled]
     tev = [None] * args.steps
-    for j, pair in enumerate(gev):
+    for i, pair in zip(sampled, gev):
         arr = [None] * nev
         arr[g], arr[g + 1] = pair
-        tev[j * stride] = arr
+        tev[i] = arr
 
     for _ in range(args.warmup):
         B.layer_forward(w, x, logits, out, od, s, ws, aux=aux, stream=stream)
@@ -550,6 +575,8 @@ def main(argv=None):
         log(f"cold: {cold['ms_per_layer_median']:.4f} ms per layer (median of {args.cold_steps})")
 
     combine_alone = time_combine_alone(B, torch, cfg, w, x, logits, od, s, ws, counts, stream, hip)
+    permute_alone = (time_permute_alone(B, torch, cfg, w, x, logits, s, ws, stream, hip)
+                     if cfg.dispatch == "dtype" else None)
     ep_share = (ep_rank_share(B, torch, np, gen, cfg, args.ep_rank_share, up, stream, hip)
                 if args.ep_rank_share > 1 and cfg.dispatch == "dtype" else None)
     if mx_info is not None:
@@ -576,7 +603,7 @@ def main(argv=None):
         log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
 
     cnt = counts.cpu().numpy()
-    sb, touched = stage_bytes_flops(cfg, cnt)
+    sb, touched = stage_bytes_flops(cfg, cnt, bool(plan["rows_gathered"]))
     stages = {}
     for n in names:
         byt, flp = sb[n]
@@ -618,10 +645,17 @@ def main(argv=None):
     g_bytes, g_flops = sb["gemm_gate_up"]
     g_s = stage_ms["gemm_gate_up"] * 1e-3
     achieved = g_bytes / g_s / 1e9
+    gg_bytes = sb["gemm_gate_up_gathered"][0]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": gate_up_kernel(cfg),
-            "algorithmic_bytes": int(g_bytes), "avg_ms": round(stage_ms["gemm_gate_up"], 5),
+            "kernel": plan["gate_up_kernel"] + " (expert gate/up GEMM" +
+                      (", persistent" if plan["gate_up_persistent"] else "") +
+                      (", token rows gathered through row_token" if plan["rows_gathered"] else "") + ")",
+            "algorithmic_bytes": int(g_bytes),
+            "algorithmic_bytes_note": "touched experts' W1+W3, one input row per routed assignment (R*D*b), "
+                                      "the R*I intermediate written",
+            "gathered_bytes": int(gg_bytes), "gathered_frac": round(gg_bytes / g_s / 1e9 / HBM_PEAK_GBS, 4),
+            "avg_ms": round(stage_ms["gemm_gate_up"], 5), "sampled_launches": len(gev),
             "mfma_tflops": round(g_flops / g_s / 1e12, 1),
             "mfma_frac": round(g_flops / g_s / 1e12 / (
                 F32_PEAK_TFLOPS if cfg.dtype != "bf16" else FP8_PEAK_TFLOPS if cfg.dispatch == "mxfp8"
@@ -648,15 +682,16 @@ def main(argv=None):
         "grouped_gemm_tflops": round((sb["gemm_gate_up"][1] + sb["gemm_down"][1]) / (gemm_ms * 1e-3) / 1e12, 1),
         "permute_gbps": stages["permute"]["GB/s"],
         "combine_gbps": stages["combine"]["GB/s"],
-        "stage_timing": (f"timed steps record the two events around the expert gate/up GEMM on every "
-                         f"{stride}-th step ({len(gev)} of {args.steps} launches sampled); "
-                         "stages and layer_event_ms come from a second pass of as many steps "
-                         "with every stage event"),
+        "stage_timing": (f"timed steps record the two events around the expert gate/up GEMM on "
+                         f"{len(gev)} sampled steps of {args.steps}; stages and layer_event_ms come "
+                         "from a second pass of as many steps with every stage event"),
+        "plan": plan,
         "layer_event_ms": round(layer_ev_ms, 5),
         "layer_event_ms_median": round(float(np.median(layer_list)), 5),
         "layer_event_ms_p95": round(pct(layer_list, 95), 5),
         "cold": cold,
         "combine_alone": combine_alone,
+        "permute_alone": permute_alone,
         "ep_rank_share": ep_share,
         "stages": stages,
         "p95_skew": round(p95, 3) if p95 is not None else None,

@@ -28,3 +28,13 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _output_guard_bands():
+    """After each test, the guard bands around every output buffer the GPU tests
+    allocated (tests/gpu_util.empty) must be intact."""
+    yield
+    gu = sys.modules.get("tests.gpu_util")
+    if gu is not None:
+        gu.check_guards()

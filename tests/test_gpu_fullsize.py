@@ -2,9 +2,15 @@
 
 * routing (ids, counts, offsets) on the full seeded fp32 logits: bit-exact over
   all T tokens;
-* moe_layer_forward on the full layer: a valid permutation of all T*k rows,
-  counts summing to T*k, the dispatch buffer exactly T*k*D*b bytes, and the fp32
-  output of sampled tokens against the oracle evaluated token by token
+* moe_layer_forward on the full layer, in the dataflow bench.py times (no permuted
+  copy requested): ids, weights, counts and offsets over all T tokens against the
+  oracle's router on the fp32 logits the layer ranked (bit-exact; weights within
+  1e-6), the permutation bit-exact, the dispatch buffer exactly T*k*D*b bytes;
+* every row of whole experts' outputs Y (the most loaded expert, one whose rows end
+  in a ragged m-tile, one of median load and the least loaded one) against the
+  oracle's expert FFN: these are the rows the full-size kernels and tile tables
+  (XCD-chunk tables, 256-row long-K down tiles) produce;
+* the fp32 output of sampled tokens against the oracle evaluated token by token
   (max |d| <= 2e-2 x RMS for bf16, 1e-5 x RMS for fp32), on tokens whose top-k
   set the scores fix beyond rounding;
 * the bf16 output is the round-to-nearest-even of the fp32 output everywhere.
@@ -19,7 +25,7 @@ import oracle
 from workloads import FULL_CONFIGS, generator as gen
 from routing_dispatch_expert_logits_amd import binding as B
 from tests.gpu_util import (dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits,
-                            check_permutation_valid, out_err_over_rms)
+                            check_permutation_valid, out_err_over_rms, check_y_rows, bf16_ulp)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -60,7 +66,8 @@ def test_layer_full_size_sampled(name):
     logits = dev(inp["logits"]) if "logits" in inp else empty((T, E), "f32")
     aux = {"topk_ids": empty((T, k), "i32"), "topk_w": empty((T, k), "f32"),
            "counts": empty((E,), "i32"), "offsets": empty((E + 1,), "i32"),
-           "row_token": empty((R,), "i32"), "token_row": empty((T, k), "i32")}
+           "row_token": empty((R,), "i32"), "token_row": empty((T, k), "i32"),
+           "y_perm": empty((R, D), act_kind(cfg))}
     if cfg.L:
         aux["z"] = empty((T, cfg.L), act_kind(cfg))
     wsp = ws(s, B.MOE_CALL_LAYER)
@@ -70,18 +77,50 @@ def test_layer_full_size_sampled(name):
     B.layer_forward(w, x, logits, out32, B.MOE_F32, s, wsp, aux)
     B.layer_forward(w, x, logits, out16, B.MOE_BF16, s, wsp)
     torch.cuda.synchronize()
-    got = {n: host(t) for n, t in aux.items() if n != "z"}
+    got = {n: host(t, bf and n == "y_perm") for n, t in aux.items() if n != "z"}
     o32 = host(out32)
     # whole-size invariants
     assert got["counts"].sum() == T * k
     np.testing.assert_array_equal(got["counts"], np.diff(got["offsets"]))
     check_permutation_valid(got["topk_ids"], got["offsets"], got["row_token"], got["token_row"])
+    # routing over all T tokens, given the fp32 scores the layer ranked: the logits it
+    # wrote (computed gates, bias included) or the given logits plus the bias
+    if "logits" in inp:
+        scores_all = oracle.router_scores(inp["logits"], inp.get("bias"))
+    else:
+        scores_all = oracle.router_scores(host(logits), None)
+    r_all = oracle.route(scores_all, k, E)
+    np.testing.assert_array_equal(got["topk_ids"], r_all["ids"])
+    np.testing.assert_array_equal(got["counts"], r_all["counts"])
+    np.testing.assert_array_equal(got["offsets"], r_all["offsets"])
+    assert np.max(np.abs(got["topk_w"] - r_all["weights"])) <= 1e-6
     # the row order is a function of the ids alone: bit-exact against the oracle's
     rt, tr = oracle.permutation(got["topk_ids"], E)
     np.testing.assert_array_equal(got["row_token"], rt)
     np.testing.assert_array_equal(got["token_row"], tr)
     assert R * D * cfg.elem_bytes == oracle.dispatch_bytes(T, k, D, cfg.elem_bytes)
     np.testing.assert_array_equal(host(out16, True), rne_bf16_bits(o32))
+    # whole experts' Y rows against the oracle's expert FFN on the same input rows
+    cnt = got["counts"]
+    live = np.nonzero(cnt)[0]
+    ragged = [e for e in live if cnt[e] % 128 and cnt[e] > 128]
+    pick = {int(live[np.argmax(cnt[live])]), int(live[np.argmin(cnt[live])]),
+            int(live[np.argsort(cnt[live])[len(live) // 2]])}
+    if ragged:
+        pick.add(int(ragged[len(ragged) // 2]))
+    for e in sorted(pick):
+        lo, hi = int(got["offsets"][e]), int(got["offsets"][e + 1])
+        toks = rt[lo:hi]
+        if cfg.L:   # the dispatched rows are the latent ones: the oracle's own Z of these tokens,
+            # and the layer's Z of them within one bf16 ulp of it (fp32 sums in another order)
+            xr = oracle.latent_down(inp["x"][toks], inp["wd"], bf)
+            zg = oracle.decode(host(aux["z"], True)[toks])
+            assert np.all(np.abs(zg - xr) <= bf16_ulp(xr)), "latent Z beyond one bf16 ulp"
+        else:
+            xr = inp["x"][toks]
+        print(f"[{name}] expert {e}: {hi - lo} rows", flush=True)
+        ref_y = oracle.expert_ffn_rows(xr, inp["w1"][e], inp["w3"][e], inp["w2"][e], bf)
+        check_y_rows(bf, got["y_perm"][lo:hi], ref_y, inputs_rounded_apart=bool(cfg.L))
     # sampled tokens against the oracle
     rng = np.random.default_rng(cfg.seed)
     tok = np.sort(rng.choice(T, size=min(N_SAMPLE, T), replace=False))

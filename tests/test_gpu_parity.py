@@ -24,7 +24,7 @@ import oracle
 from workloads import MoEConfig, PARITY_CONFIGS, generator as gen
 from routing_dispatch_expert_logits_amd import binding as B
 from tests.gpu_util import (dev, host, empty, ws, shape_of, act_kind, rne_bf16_bits, rel_err,
-                            check_permutation_valid, out_err_over_rms)
+                            check_permutation_valid, out_err_over_rms, check_y_rows, assert_poison)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,6 +117,9 @@ def test_route_and_dispatch_max_tokens(E, k, cap):
     np.testing.assert_array_equal(host(row_token)[:n], rt)
     np.testing.assert_array_equal(host(token_row), tr)
     np.testing.assert_array_equal(host(xp, True)[:n], x[rt])
+    if cap:  # rows from offsets[E] on are left untouched
+        assert_poison(xp, n)
+        assert_poison(row_token, n)
 
 
 # Gates that take the 64-expert-wide wave tile (long K slices): ragged T and E, with
@@ -141,7 +144,16 @@ def test_gate_logits(cfg):
                  ids, w, counts, offs, s, ws(s, B.MOE_CALL_ROUTE))
     torch.cuda.synchronize()
     ref = oracle.gate_logits(inp["x"], inp["gate_w"], bias)
-    assert rel_err(host(logits), ref) <= 1e-5
+    glg = host(logits)
+    assert rel_err(glg, ref) <= 1e-5
+    # routing given fp32 logits is bit-exact: the call ranked exactly the fp32 values it
+    # wrote (bias included), so its ids, weights, counts and offsets are the oracle
+    # router's on those values
+    r = oracle.route(oracle.router_scores(glg, None), k, E)
+    np.testing.assert_array_equal(host(ids), r["ids"])
+    np.testing.assert_array_equal(host(counts), r["counts"])
+    np.testing.assert_array_equal(host(offs), r["offsets"])
+    assert np.max(np.abs(host(w) - r["weights"])) <= 1e-6
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=IDS)
@@ -165,6 +177,10 @@ def test_dispatch_permute_bit_exact(cfg):
     np.testing.assert_array_equal(xp, oracle.gather_rows(x, rt))
     if not cfg.capacity:
         assert xp.nbytes == oracle.dispatch_bytes(cfg.T, cfg.k, D, cfg.elem_bytes)
+    else:  # rows from offsets[E] on are left untouched
+        assert n < cfg.R
+        assert_poison(x_perm, n)
+        assert_poison(row_token, n)
 
 
 def _ffn_inputs(cfg):
@@ -176,22 +192,8 @@ def _ffn_inputs(cfg):
 
 
 def _check_y(cfg, got, ref_y):
-    """Expert outputs: both sides round A and Y to bf16 at the same points, but the
-    fp32 sums run in different orders, so an A element near a rounding midpoint
-    can land one ulp apart; that moves Y by ulp(a) * |w2| (about 1e-3 x RMS(Y) for
-    |a| ~ 5 x RMS(a) at I = 256).  Bound: every element within one bf16 ulp of Y
-    plus 5e-3 x RMS(Y); at most 1e-4 of them beyond one ulp plus 1e-3 x RMS(Y)."""
-    if cfg.dtype == "bf16":
-        y = oracle.decode(got)
-        rms = float(np.sqrt(np.mean(ref_y ** 2)))
-        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref_y), 1e-30))) - 7)
-        err = np.abs(y - ref_y)
-        worst = float(np.max((err - ulp) / rms))
-        assert not (err > ulp + 5e-3 * rms).any(), f"worst excess over 1 ulp: {worst:.2e} x RMS"
-        frac = float(np.mean(err > ulp + 1e-3 * rms))
-        assert frac <= 1e-4, f"{frac:.2e} of elements beyond 1 ulp + 1e-3 RMS (worst {worst:.2e})"
-    else:
-        assert rel_err(got, ref_y) <= 1e-5
+    """Expert outputs against the oracle's: see check_y_rows."""
+    check_y_rows(cfg.dtype == "bf16", got, ref_y)
 
 
 @pytest.mark.parametrize("cfg", CFGS, ids=IDS)
@@ -427,6 +429,44 @@ def test_layer_gathered_rows_equal_permuted_copy(name):
     np.testing.assert_array_equal(host(aux["token_row"]), a["token_row"])
 
 
+WIDE = ["wide_experts", "long_k_down", "wsp_chunk_gate_up", "wsp_chunk_down"]
+
+
+@pytest.mark.parametrize("name", WIDE)
+def test_layer_gathered_y_every_row(name):
+    """The fused layer in the dataflow bench.py times (no permuted copy: the gate/up GEMM
+    gathers the token rows through row_token) on layers that take the full-size layers'
+    kernels: 16 and 64 n-tiles of 128, K = 2048 and 8192, the persistent 128 x 256 and
+    256 x 128 down tiles, and XCD-chunk-only tile tables (more tiles than one table
+    holds).  Every row of every expert's Y against the oracle, and the layer output on
+    every token."""
+    cfg = PARITY_CONFIGS[name]
+    s = shape_of(cfg)
+    plan = B.layer_plan(s, cfg.gate == "computed")
+    assert plan["rows_gathered"] == 1 and plan["gate_up_persistent"] == 1
+    inp = gen.layer_inputs(cfg)
+    T, E, k, R, D = cfg.T, cfg.E, cfg.k, cfg.R, cfg.D
+    w = {n: dev(inp[n]) for n in ("w1", "w3", "w2")}
+    w["gate_bias"] = dev(inp["bias"])
+    aux = {"topk_ids": empty((T, k), "i32"), "topk_w": empty((T, k), "f32"),
+           "offsets": empty((E + 1,), "i32"), "row_token": empty((R,), "i32"),
+           "token_row": empty((T, k), "i32"), "y_perm": empty((R, D), "bf16")}
+    out = empty((T, cfg.H), "f32")
+    B.layer_forward(w, dev(inp["x"]), dev(inp["logits"]), out, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER), aux)
+    torch.cuda.synchronize()
+    ref = oracle.route(oracle.router_scores(inp["logits"], inp["bias"]), k, E)
+    rt, tr = oracle.permutation(ref["ids"], E)
+    np.testing.assert_array_equal(host(aux["topk_ids"]), ref["ids"])
+    np.testing.assert_array_equal(host(aux["offsets"]), ref["offsets"])
+    np.testing.assert_array_equal(host(aux["row_token"]), rt)
+    np.testing.assert_array_equal(host(aux["token_row"]), tr)
+    ref_y = oracle.grouped_expert_ffn(oracle.gather_rows(inp["x"], rt), ref["offsets"], inp["w1"],
+                                      inp["w3"], inp["w2"], bf16=True)
+    _check_y(cfg, host(aux["y_perm"], True), ref_y)
+    ref_out = oracle.combine(ref_y, tr, ref["weights"])
+    assert out_err_over_rms(host(out), ref_out) <= 2e-2
+
+
 def test_stage_events_skip_null_entries():
     """A stage-event array may leave entries NULL: only the others are recorded, and the
     layer's results do not depend on which are."""
@@ -527,6 +567,7 @@ def test_concurrent_layers_on_two_streams():
         cfg, s, w, x, logits = setups[i]
         out = empty((cfg.T, cfg.H), "f32")
         wsp = ws(s, B.MOE_CALL_LAYER)
+        torch.cuda.synchronize()  # the buffers' poison fill ran on the default stream
         for _ in range(reps):
             B.layer_forward(w, x, logits, out, B.MOE_F32, s, wsp, stream=stream)
         return out

@@ -123,10 +123,23 @@ PARITY_CONFIGS = {c.name: c for c in (
     # more than 2048 tokens: 163 ranking blocks of 16 tokens
     MoEConfig(name="many_tokens", T=2600, H=128, E=40, k=3, I=128, seed=21, gate="drawn",
               zipf_s=1.1, zipf_alpha=0.5),
-    # wide experts: 16 n-tiles of 128 in the gate/up GEMM and K = 2048 in the down
-    # GEMM (the large-layer kernel choices), skewed counts spanning several m-tiles
+    # wide experts: 16 n-tiles of 128 in the gate/up GEMM and K = 2048 in the down GEMM
+    # with at least 192 rows per expert on average (so the persistent 128 x 256 down
+    # tiles), skewed counts spanning several m-tiles
     MoEConfig(name="wide_experts", T=400, H=256, E=4, k=2, I=2048, seed=22, gate="drawn",
               zipf_s=1.1, zipf_alpha=1.0),
+    # long-K down GEMM (K = I = 2048) with fewer than 192 rows per expert on average:
+    # the persistent 256 x 128 down tiles on the second m-tile table
+    MoEConfig(name="long_k_down", T=400, H=256, E=8, k=2, I=2048, seed=29, gate="drawn",
+              zipf_s=1.1, zipf_alpha=1.0),
+    # more persistent-GEMM tiles than one LDS tile table holds (3520): each workgroup
+    # decodes only its XCD's chunk and no tile is taken across XCDs.  Gate/up: 64
+    # n-tiles x ~70 m-tiles; the down GEMM of this layer has 73 tiles (whole table).
+    MoEConfig(name="wsp_chunk_gate_up", T=4096, H=256, E=8, k=2, I=8192, seed=30, gate="drawn",
+              zipf_s=1.1, zipf_alpha=1.0),
+    # the same for the down GEMM on 128 x 256 tiles: ~272 m-tiles x 14 n-tiles
+    MoEConfig(name="wsp_chunk_down", T=4096, H=3584, E=16, k=8, I=256, seed=34, gate="drawn",
+              zipf_s=1.1, zipf_alpha=0.5),
     # a shared expert next to the routed ones: 128-row tiles (T >= 48), 16-row
     # tiles (T < 48) and fp32
     MoEConfig(name="shared_expert", T=300, H=256, E=16, k=4, I=192, seed=23, gate="computed",
