@@ -372,6 +372,29 @@ MOE_API moe_status moe_layer_forward(const moe_layer_weights* w, const void* x, 
                              int out_dtype, const moe_shape* s, moe_layer_aux* aux,
                              void** stage_events, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_layer_forward without a caller workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  The same computation, kernels and results as moe_layer_forward (same
+ * arguments minus ws / ws_bytes); the workspace is a device array inside the library,
+ * MOE_NOALLOC_SCRATCH_BYTES long, one per GPU, set up on the first call on each device
+ * (a symbol lookup, no allocation) and held until the process ends.  The call itself
+ * allocates nothing.
+ *
+ * Limit: shapes whose layer workspace, moe_workspace_bytes(s, MOE_CALL_LAYER), exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE (64 MiB holds decode-scale steps, e.g.
+ * the 896-expert top-16 layer up to T = 256 tokens, or a 256-expert top-8 layer of width
+ * 7168 up to T = 128).  Other errors as moe_layer_forward.
+ *
+ * Every call on one GPU shares that GPU's array and finds the last call's contents in
+ * it (nothing in it needs to start at zero): calls that overlap on one GPU (different
+ * streams, or threads without ordering) race and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MOE_API moe_status moe_layer_forward_noalloc(const moe_layer_weights* w, const void* x, float* logits,
+                                             void* out, int out_dtype, const moe_shape* s,
+                                             moe_layer_aux* aux, void** stage_events, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

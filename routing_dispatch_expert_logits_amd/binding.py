@@ -20,6 +20,7 @@ MOE_CALL_ROUTE, MOE_CALL_DISPATCH, MOE_CALL_FFN, MOE_CALL_COMBINE, MOE_CALL_LAYE
 MOE_COMBINE_FUSED, MOE_COMBINE_UNFUSED = 0, 1
 MOE_DISPATCH_DTYPE, MOE_DISPATCH_MXFP8 = 0, 1
 MOE_NUM_STAGE_EVENTS = 10
+NOALLOC_SCRATCH_BYTES = 64 << 20
 ABI_VERSION = 5
 MOE_PLAN_GATE, MOE_PLAN_X_PERM = 1, 2
 
@@ -89,8 +90,10 @@ def _load() -> ctypes.CDLL:
                                 _vp, sz, _vp]
     lib.moe_layer_forward.argtypes = [P(MoeLayerWeights), _vp, _vp, _vp, ctypes.c_int,
                                       P(MoeShape), P(MoeLayerAux), P(_vp), _vp, sz, _vp]
+    lib.moe_layer_forward_noalloc.argtypes = [P(MoeLayerWeights), _vp, _vp, _vp, ctypes.c_int,
+                                              P(MoeShape), P(MoeLayerAux), P(_vp), _vp]
     for f in ("moe_route_topk", "moe_dispatch_permute", "moe_grouped_ffn", "moe_combine",
-              "moe_layer_forward", "moe_quantize_mxfp8"):
+              "moe_layer_forward", "moe_quantize_mxfp8", "moe_layer_forward_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     v = lib.moe_abi_version()
     if v != ABI_VERSION:
@@ -203,3 +206,19 @@ def layer_forward(weights: dict, x, logits, out, out_dtype: int, s: MoeShape, ws
     _check("moe_layer_forward", lib.moe_layer_forward(
         ctypes.byref(w), _p(x), _p(logits), _p(out), int(out_dtype), ctypes.byref(s),
         ctypes.byref(a), ev, _p(ws), _nbytes(ws), _stream(stream)))
+
+
+def layer_forward_noalloc(weights: dict, x, logits, out, out_dtype: int, s: MoeShape, aux: dict = None,
+                          stage_events=None, stream=None):
+    """moe_layer_forward_noalloc: the layer forward with the library's own per-GPU scratch
+    array as its workspace (no caller workspace)."""
+    w = MoeLayerWeights(*[_p(weights.get(f)) for f, _ in MoeLayerWeights._fields_])
+    a = MoeLayerAux(*[_p((aux or {}).get(f)) for f, _ in MoeLayerAux._fields_])
+    ev = None
+    if stage_events is not None:
+        assert len(stage_events) == MOE_NUM_STAGE_EVENTS
+        ev = (_vp * MOE_NUM_STAGE_EVENTS)(*[e.cuda_event if hasattr(e, "cuda_event") else e
+                                            for e in stage_events])
+    _check("moe_layer_forward_noalloc", lib.moe_layer_forward_noalloc(
+        ctypes.byref(w), _p(x), _p(logits), _p(out), int(out_dtype), ctypes.byref(s), ctypes.byref(a), ev,
+        _stream(stream)))

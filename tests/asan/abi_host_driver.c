@@ -85,6 +85,14 @@ int main(void) {
   aux.x_perm = (void*)((char*)F + 8);
   EXPECT(moe_layer_forward(&w, F, F, F, MOE_F32, &s, &aux, NULL, F, 1 << 30, NULL) == MOE_ERR_INVALID_ARG);
 
+  /* the allocation-free variant: validation, then the scratch-size limit, on the host */
+  aux.x_perm = NULL;
+  EXPECT(moe_layer_forward_noalloc(&w, F, NULL, F, MOE_F32, &s, &aux, NULL, NULL) == MOE_ERR_INVALID_ARG);
+  EXPECT(moe_layer_forward_noalloc(&w, F, F, F, MOE_F32, &bad, &aux, NULL, NULL) == MOE_ERR_INVALID_ARG);
+  moe_shape huge = shape(8192, 7168, 256, 8, 2048, 0, 1);
+  EXPECT(moe_workspace_bytes(&huge, MOE_CALL_LAYER) > MOE_NOALLOC_SCRATCH_BYTES);
+  EXPECT(moe_layer_forward_noalloc(&w, F, F, F, MOE_F32, &huge, &aux, NULL, NULL) == MOE_ERR_WORKSPACE);
+
   if (failures) fprintf(stderr, "%d failure(s)\n", failures);
   else printf("abi host driver: all checks passed\n");
   return failures ? 1 : 0;

@@ -207,3 +207,26 @@ def test_persistent_tile_table_fields_bound_the_expert_rows():
     assert at["down_kernel"] == "k_gemm_wsp<256, 128, 1," and at["down_persistent"] == 1
     over = B.layer_plan(B.shape(4096 * 256 + 256, 128, 1024, 1, 2048), False)
     assert over["down_kernel"] == "k_gemm_ws<256, 128, 1," and over["down_persistent"] == 0
+
+
+def test_noalloc_rejects_before_any_gpu_work():
+    """The allocation-free layer forward validates like moe_layer_forward, and a shape
+    whose layer workspace exceeds the library's scratch array is MOE_ERR_WORKSPACE, all on
+    the host before any HIP call."""
+    L = B.lib
+    w = B.MoeLayerWeights(None, None, FAKE, FAKE, FAKE, None, None, None, None, None)
+    aux = B.MoeLayerAux()
+    s = B.shape(64, 128, 8, 2, 256)
+    assert L.moe_layer_forward_noalloc(ctypes.byref(w), FAKE, None, FAKE, 0, ctypes.byref(s),
+                                       ctypes.byref(aux), None, None) == B.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward_noalloc(ctypes.byref(w), FAKE, FAKE, FAKE, 0,
+                                       ctypes.byref(B.shape(0, 128, 8, 2, 256)), ctypes.byref(aux), None,
+                                       None) == B.MOE_ERR_INVALID_ARG
+    c = FULL_CONFIGS["deepseek_r1_shaped"]
+    big = B.shape(c.T, c.H, c.E, c.k, c.I)
+    assert B.workspace_bytes(big, B.MOE_CALL_LAYER) > B.NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_forward_noalloc(ctypes.byref(w), FAKE, FAKE, FAKE, 0, ctypes.byref(big),
+                                       ctypes.byref(aux), None, None) == B.MOE_ERR_WORKSPACE
+    # the decode-scale 896-expert top-16 step fits up to 256 tokens
+    k3 = FULL_CONFIGS["k3_shaped_decode"]
+    assert B.workspace_bytes(B.shape(256, k3.H, k3.E, k3.k, k3.I), B.MOE_CALL_LAYER) <= B.NOALLOC_SCRATCH_BYTES

@@ -1,0 +1,70 @@
+"""moe_layer_forward_noalloc (the variant for callers that cannot allocate: its
+workspace is the library's per-GPU scratch array) against moe_layer_forward with a
+caller workspace: same kernels, same results, bit for bit.
+
+Consecutive calls share the scratch array and find the previous call's contents in
+it, so the calls run back to back, the later ones on smaller inputs than the first:
+nothing left behind may change a result.
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import PARITY_CONFIGS, generator as gen
+from routing_dispatch_expert_logits_amd import binding as B
+from tests.gpu_util import dev, host, empty, ws, shape_of
+
+pytestmark = pytest.mark.gpu
+
+AUX = (("topk_ids", "i32", "Tk"), ("topk_w", "f32", "Tk"), ("counts", "i32", "E"),
+       ("offsets", "i32", "E1"), ("row_token", "i32", "R"), ("token_row", "i32", "Tk"))
+
+
+def _run(cfg, inp, noalloc):
+    s = shape_of(cfg)
+    T, E, k, R = cfg.T, cfg.E, cfg.k, cfg.R
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "ws1", "ws3", "ws2") if n in inp}
+    if "bias" in inp:
+        w["gate_bias"] = dev(inp["bias"])
+    logits = dev(inp["logits"]) if "logits" in inp else empty((T, E), "f32")
+    dims = {"Tk": (T, k), "E": (E,), "E1": (E + 1,), "R": (R,)}
+    aux = {n: empty(dims[d], kind) for n, kind, d in AUX}
+    out = empty((T, cfg.H), "f32")
+    if noalloc:
+        B.layer_forward_noalloc(w, dev(inp["x"]), logits, out, B.MOE_F32, s, aux)
+    else:
+        B.layer_forward(w, dev(inp["x"]), logits, out, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER), aux)
+    torch.cuda.synchronize()
+    res = {n: host(t) for n, t in aux.items()}
+    res["out"] = host(out)
+    res["logits"] = host(logits)
+    return res
+
+
+def _same(a, b):
+    n = int(a["offsets"][-1])
+    for key in a:
+        x, y = (a[key][:n], b[key][:n]) if key == "row_token" else (a[key], b[key])
+        np.testing.assert_array_equal(x, y, err_msg=key)
+
+
+def test_noalloc_equals_layer_forward_on_calls_in_a_row():
+    big = PARITY_CONFIGS["small_bf16_zipf"]          # persistent gate/up GEMM, gathered rows
+    calls = [big, big.with_(T=120),                   # the second call on a smaller input
+             PARITY_CONFIGS["small_bf16_decode"],     # decode-scale step (one-launch routing)
+             PARITY_CONFIGS["shared_expert"].with_(T=77)]
+    assert B.workspace_bytes(shape_of(big), B.MOE_CALL_LAYER) <= B.NOALLOC_SCRATCH_BYTES
+    for cfg in calls:
+        inp = gen.layer_inputs(cfg)
+        got = _run(cfg, inp, noalloc=True)
+        ref = _run(cfg, inp, noalloc=False)
+        _same(ref, got)
+
+
+def test_noalloc_twice_is_deterministic():
+    cfg = PARITY_CONFIGS["capacity_prefill"]
+    inp = gen.layer_inputs(cfg)
+    a = _run(cfg, inp, noalloc=True)
+    b = _run(cfg, inp, noalloc=True)
+    _same(a, b)
+    _same(_run(cfg, inp, noalloc=False), a)
