@@ -124,7 +124,9 @@ typedef enum moe_call {
 /* [0] start  [1] after latent down-projection  [2] after gate  [3] after top-k+count+scan
  * [4] after permute  [5] after expert gate/up GEMM  [6] after expert down GEMM
  * [7] after the shared expert  [8] after combine  [9] after latent up-projection.
- * Stages that do not run leave two consecutive events back to back. */
+ * Stages that do not run leave two consecutive events back to back.  On decode-scale
+ * steps (moe_plan.decode_path; no shared expert) the combine runs inside the down
+ * GEMM's launch, so its time shows in [5]..[6] and [7]..[8] is empty. */
 
 typedef struct moe_shape {
   int64_t T;      /* tokens */
@@ -341,6 +343,15 @@ typedef struct moe_layer_aux {
  * of "Three Parameter Counts...", table of "Which optimizations need a
  * task-level gate": routing ids, counts, offsets and the permutation are
  * bit-identical to the separate calls on the same logits.
+ *
+ * Decode-scale steps (fewer than 48 rows per expert on average, T <= 128) take a
+ * low-latency path of three launches ("Three Parameter Counts...", "Halving top-k is a
+ * network change first": at decode-scale token counts the layer is bound by launch
+ * latency): routing, counts, offsets and row metadata in one workgroup; the gate/up GEMM
+ * reading the token rows through row_token; the down GEMM with the combine, each
+ * workgroup owning 16 output columns of every row.  The output bits are those of the
+ * separate calls.  Latent projections, MXFP8 conversion of the token rows, a requested
+ * permuted copy and a shared expert add their own launches.
  *
  * Latent layers (s->L > 0) follow "Latent MoE" (Definition; Current Synthesis):
  * the router scores the full-width X, the rows dispatched are Z = X wd^T, and the

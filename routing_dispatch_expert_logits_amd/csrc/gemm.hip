@@ -1138,6 +1138,126 @@ __global__ __launch_bounds__(256) void k_gemm_decode(
     }
 }
 
+// ------------------------------------------------------------------ decode down GEMM + combine
+// Decode-scale steps: the expert down GEMM and the combine in one launch, with no
+// hand-off of data between workgroups.  Workgroup b owns output columns
+// [16 b, 16 b + 16) of EVERY row: its waves run the down GEMM's 16-row m-tiles of all
+// touched experts for those 16 columns only (streaming each expert's 16 x K slice of
+// W2 once), keep the bf16 Y columns of all R rows in LDS, and after one barrier the
+// whole workgroup combines them: out[t, c] = sum_j w[t, j] * Y[token_row[t, j], c]
+// (+ add[t, c]), fp32 fma in ascending j, one rounding, the bits k_combine produces.
+// Each m-tile runs the K-steps, operand layout and MFMA sequence of k_gemm_decode (a
+// lane carries k = 16 g .. 16 g + 15 of a 64-wide K-step, g = lane / 16), so Y has
+// the bits of the separate down GEMM.  The waves keep DEPTH - 1 K-steps of loads in
+// flight across m-tile boundaries; the m-tile table and segment starts are read from
+// LDS.
+
+constexpr int kDcCols = 16;  // output columns per workgroup
+
+// LDS bytes of k_down_combine for E experts, R rows and at most `tiles` m-tiles:
+// segment starts, m-tile table, token_row and routing weights, Y columns.
+static inline size_t down_combine_lds(int E, int R, int tiles) {
+  return ((size_t)(E + 1) + tiles + 2 * (size_t)R) * 4 + (size_t)R * kDcCols * 2;
+}
+
+template <int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void k_down_combine(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W2, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ mtile_start, int E, int N, int K, int R, const int32_t* __restrict__ token_row,
+    const float* __restrict__ topk_w, const uint16_t* __restrict__ add, int T, int k, void* __restrict__ out,
+    int out_f32, uint16_t* __restrict__ y_out, int tiles_cap) {
+  extern __shared__ __attribute__((aligned(16))) int32_t dc_lds[];
+  int32_t* s_off = dc_lds;                          // [E + 1] segment starts
+  int32_t* s_tile = s_off + (E + 1);                // [tiles] expert | m-tile << 16 of each m-tile
+  int32_t* s_trow = s_tile + tiles_cap;             // [T * k] token_row
+  float* s_w = reinterpret_cast<float*>(s_trow + R);  // [T * k] routing weights
+  uint16_t* ys = reinterpret_cast<uint16_t*>(s_w + R);  // [R x 16] Y columns of every row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int total = mtile_start[E];
+  for (int a = tid; a < T * k; a += NW * 64) {
+    s_trow[a] = token_row[a];
+    s_w[a] = topk_w[a];
+  }
+  for (int e = tid; e <= E; e += NW * 64) s_off[e] = offsets[e];
+  for (int e = tid; e < E; e += NW * 64) {
+    const int mt0 = mtile_start[e], mte = mtile_start[e + 1] - mt0;
+    for (int m = 0; m < mte; ++m) s_tile[mt0 + m] = e | (m << 16);
+  }
+  __syncthreads();
+  const int n0 = blockIdx.x * kDcCols;
+  const int g = lane >> 4, c = lane & 15;
+  const int my_tiles = total > wave ? ceil_div(total - wave, NW) : 0;  // tiles wave + NW q
+  const int S = K / 64;
+
+  // Issue side: tile i_q, K-step i_s.  Every K-step issues the same loads (past the
+  // wave's last tile they re-read that tile's last step: valid addresses, results
+  // unused), so the compiler's load-count waits stay exact and DEPTH - 1 steps stay in
+  // flight across tile boundaries.
+  int i_q = 0, i_s = 0;
+  const uint16_t* ipa = A;
+  const uint16_t* ipb[1][1] = {{W2}};
+  const uint8_t* const no_scale[1][1] = {{nullptr}};
+  auto issue = [&](DecodeRegs<1, 1>& r) {
+    if (i_s == 0 && i_q < my_tiles) {
+      const int v = s_tile[wave + i_q * NW];
+      const int e = v & 0xffff;
+      const int row0 = s_off[e] + (v >> 16) * 16;
+      const int rows = min(16, s_off[e + 1] - row0);
+      ipa = A + (size_t)(row0 + min(c, rows - 1)) * K + g * 16;
+      ipb[0][0] = W2 + ((size_t)e * N + n0 + c) * K + g * 16;
+    }
+    decode_load<1, 1, false>(r, ipa, ipb, min(i_s, S - 1) * 64, nullptr, no_scale);
+    if (i_q < my_tiles && ++i_s == S) {
+      i_s = 0;
+      ++i_q;
+    }
+  };
+  if (my_tiles > 0) {
+    DecodeRegs<1, 1> ring[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) issue(ring[d]);
+    for (int q = 0; q < my_tiles; ++q) {
+      f32x4 acc[1][1] = {{f32x4{0.f, 0.f, 0.f, 0.f}}};
+      for (int s0 = 0; s0 < S; s0 += DEPTH) {  // DEPTH divides S
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          issue(ring[(d + DEPTH - 1) % DEPTH]);
+          decode_mma<1, 1, false>(acc, ring[d]);
+        }
+      }
+      // m-tile done: its 16 x 16 Y block, rounded to bf16, into LDS
+      const int v = s_tile[wave + q * NW];
+      const int e = v & 0xffff;
+      const int row0 = s_off[e] + (v >> 16) * 16;
+      const int rows = min(16, s_off[e + 1] - row0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        if (r < rows) {
+          const uint16_t y = f32_to_bf16(acc[0][0][i]);
+          ys[(row0 + r) * kDcCols + c] = y;
+          if (y_out) y_out[(size_t)(row0 + r) * N + n0 + c] = y;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // combine of this workgroup's 16 columns for every token
+  for (int idx = tid; idx < T * kDcCols; idx += NW * 64) {
+    const int t = idx / kDcCols, cc = idx % kDcCols;
+    float a = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int r = s_trow[t * k + j];
+      if (r < 0) continue;  // dropped by an expert capacity: no term
+      a = fmaf(s_w[t * k + j], bf16_to_f32(ys[r * kDcCols + cc]), a);
+    }
+    const size_t o = (size_t)t * N + n0 + cc;
+    if (add) a += bf16_to_f32(add[o]);
+    if (out_f32) static_cast<float*>(out)[o] = a;
+    else static_cast<uint16_t*>(out)[o] = f32_to_bf16(a);
+  }
+}
+
 // ------------------------------------------------------------------ fp32 SIMT kernel
 // fp32 layers and the exact-input fp32 gate: 64x64 tile, 16x16 threads with
 // 4x4 outputs each, K chunks of 16 through LDS; each output is one fma chain
@@ -1410,6 +1530,30 @@ hipError_t launch_gemm_simt(bool a_bf16, int epi, const void* A, int M, const fl
     }
   }
 #undef MOE_SIMT
+  return hipGetLastError();
+}
+
+bool down_combine_ok(int R, int E, int N, int K) {
+  return N % kDcCols == 0 && K % 64 == 0 && E < 65536 &&
+         down_combine_lds(E, R, max_mtiles(R, E, 16)) <= kDownCombineMaxLds;
+}
+
+hipError_t launch_down_combine(const uint16_t* act, int R, const uint16_t* W2, const int32_t* offsets,
+                               const int32_t* mtile_start, int E, int N, int K, const int32_t* token_row,
+                               const float* topk_w, const void* add, int T, int k, void* out, bool out_f32,
+                               void* y_out, hipStream_t st) {
+  if (!down_combine_ok(R, E, N, K)) return hipErrorInvalidValue;
+  const int tiles_cap = max_mtiles(R, E, 16);
+  const size_t lds = down_combine_lds(E, R, tiles_cap);
+  const int S = K / 64;  // K-steps per m-tile; the load pipeline's depth divides it
+#define MOE_DC(DEPTH_)                                                                                      \
+  hipLaunchKernelGGL((k_down_combine<16, DEPTH_>), dim3(N / kDcCols), dim3(16 * 64), lds, st, act, W2,      \
+                     offsets, mtile_start, E, N, K, R, token_row, topk_w, static_cast<const uint16_t*>(add), \
+                     T, k, out, (int)out_f32, static_cast<uint16_t*>(y_out), tiles_cap)
+  if (S % 4 == 0) MOE_DC(4);
+  else if (S % 2 == 0) MOE_DC(2);
+  else MOE_DC(1);
+#undef MOE_DC
   return hipGetLastError();
 }
 

@@ -239,6 +239,7 @@ struct LayerPlan {
   GemmKind kind;
   bool small;  // decode-scale routing in one launch, gate/up reading the token rows
   bool gath;   // larger steps: the permutation writes metadata only, gate/up gathers the rows
+  bool fused_dc;  // decode-scale steps: the down GEMM and the combine in one launch
   GemmChoice gate_up, down, shared_gate_up, shared_down;
   int launches;
 };
@@ -252,7 +253,13 @@ LayerPlan plan_layer(const Dims& d, bool gate_computed, bool want_xperm, bool wa
   // caller asks for it in aux.x_perm).  With MXFP8 dispatch the token rows are
   // quantised once and read the same way; a caller who asks for the permuted codes
   // gets the general path.
-  p.small = p.kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (want_xperm || want_xperm_scale));
+  // The one-workgroup router ranks ceil(T / 16) tokens per wave, one after another, so its
+  // time grows with ceil(T / 16) * k * ceil(E / 64) (measured on the 896-expert top-16 step:
+  // 13.6 us at T = 8, 112 us at T = 128, against about 27 us for the three launches of the
+  // general routing at T = 128); it is taken while that product stays within about 35 us.
+  const int rank_work = ceil_div(d.T, kBlockTok) * d.k * ceil_div(d.E, kWave);
+  p.small = p.kind == GEMM_DECODE && d.T <= kSmallT && rank_work <= kSmallRankWork &&
+            !(d.mx && (want_xperm || want_xperm_scale));
   // Larger steps: unless the caller asks for the permuted rows, the permutation writes
   // only the row metadata and the gate/up GEMM reads the token rows through row_token
   // (decode-sized tiles always can; the persistent prefill kernel when its tile table
@@ -263,6 +270,12 @@ LayerPlan plan_layer(const Dims& d, bool gate_computed, bool want_xperm, bool wa
             (p.kind == GEMM_PREFILL && gemm_gather_ok(d.R, d.E, d.I, d.mx ? d.D / 2 : d.D, d.mx)));
   p.gate_up = choose_gemm(p.kind, true, true, d.mx, d.R, d.E, d.I, d.mx ? d.D / 2 : d.D);
   p.down = choose_gemm(p.kind, false, true, false, d.R, d.E, d.D, d.I);
+  // Decode-scale steps: each workgroup runs the down GEMM for a 16-column slice of every
+  // row and combines those columns itself, so the combine needs no launch of its own
+  // (and no data passes between workgroups).  Not with a shared expert, whose term the
+  // combine adds after the routed ones.
+  p.fused_dc = p.kind == GEMM_DECODE && d.bf16 && !d.Is && down_combine_ok(d.R, d.E, d.D, d.I);
+  if (p.fused_dc) p.down = GemmChoice{GV_DOWN_COMBINE, 16, 16, false, "k_down_combine<16,"};
   int n = 0;
   if (d.L) n += 1;                            // latent down-projection
   if (gate_computed) n += 1;                  // gate scores (split-K slices summed by the top-k kernel)
@@ -280,7 +293,7 @@ LayerPlan plan_layer(const Dims& d, bool gate_computed, bool want_xperm, bool wa
     p.shared_down = choose_gemm(expert_kind(ds), false, true, false, ds.R, 1, ds.D, ds.I);
     n += 3;                                   // its one-group table and two GEMMs
   }
-  n += 1;                                     // combine
+  if (!p.fused_dc) n += 1;                    // combine (inside the down GEMM's launch when fused)
   if (d.L) n += 1;                            // latent up-projection
   p.launches = n;
   return p;
@@ -513,6 +526,16 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   const int row16 = d.D * d.es / 16;
   const bool small = plan.small, gath = plan.gath;
   const bool rows_from_tokens = small || gath;
+  // a5 down GEMM (bf16), or on decode-scale steps the down GEMM with the combine (a6)
+  auto down_bf16 = [&]() -> hipError_t {
+    if (plan.fused_dc)
+      return launch_down_combine(static_cast<const uint16_t*>(act), d.R, static_cast<const uint16_t*>(wt->w2),
+                                 offs, mtile, d.E, d.D, d.I, trow, tw, nullptr, d.T, d.k, d.L ? outl : out,
+                                 d.L ? !d.bf16 : out_dtype == MOE_F32, ax.y_perm, st);
+    return launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
+                            static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile, d.E, d.D, d.I,
+                            st);
+  };
   uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
   uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;
   if (small) {
@@ -547,9 +570,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
                                   static_cast<uint16_t*>(act), offs, mtile, d.E, d.I, d.D, mx,
                                   rows_from_tokens ? rtok : nullptr, st));
     if (!ev(5)) return MOE_ERR_HIP;
-    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
-                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
-                             d.E, d.D, d.I, st));
+    MOE_HIP(down_bf16());
   } else if (rows_from_tokens) {
     if (kind == GEMM_DECODE)
       MOE_HIP(launch_gemm_decode_gather(EPI_SWIGLU_BF16, static_cast<const uint16_t*>(src), rtok, d.R,
@@ -562,9 +583,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
                                          static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I,
                                          d.D, st));
     if (!ev(5)) return MOE_ERR_HIP;
-    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
-                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
-                             d.E, d.D, d.I, st));
+    MOE_HIP(down_bf16());
   } else if (kind == GEMM_SIMT) {
     MOE_HIP(launch_gemm_simt(false, EPI_SWIGLU_F32, xperm, d.R, static_cast<const float*>(wt->w1),
                              static_cast<const float*>(wt->w3), act, offs, mtile, d.E, d.I, d.D,
@@ -578,9 +597,7 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
                              static_cast<const uint16_t*>(wt->w3), act, offs, mtile, d.E, d.I, d.D,
                              st));
     if (!ev(5)) return MOE_ERR_HIP;
-    MOE_HIP(launch_gemm_bf16(kind, EPI_BF16, static_cast<const uint16_t*>(act), d.R,
-                             static_cast<const uint16_t*>(wt->w2), nullptr, yperm, offs, mtile,
-                             d.E, d.D, d.I, st));
+    MOE_HIP(down_bf16());
   }
   if (!ev(6)) return MOE_ERR_HIP;
   // shared expert: every token, whatever the router picked
@@ -595,12 +612,12 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
     if (rc != MOE_OK) return rc;
   }
   if (!ev(7)) return MOE_ERR_HIP;
-  // a6
-  if (d.L) {
-    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, nullptr, d.T, d.k, outl, !d.bf16, st));
-  } else {
-    MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, sy, d.T, d.k, out, out_dtype == MOE_F32,
-                           st));
+  // a6 (on fused decode-scale steps it ran inside the down GEMM's launch)
+  if (!plan.fused_dc) {
+    if (d.L)
+      MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, nullptr, d.T, d.k, outl, !d.bf16, st));
+    else
+      MOE_HIP(launch_combine(yperm, row16, d.bf16, trow, tw, sy, d.T, d.k, out, out_dtype == MOE_F32, st));
   }
   if (!ev(8)) return MOE_ERR_HIP;
   if (d.L) {  // a7: out = out_L wu^T

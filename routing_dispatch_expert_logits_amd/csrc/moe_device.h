@@ -14,8 +14,11 @@ constexpr int kBlockTok = 16;
 __host__ __device__ __forceinline__ int block_tokens(int) { return kBlockTok; }
 constexpr int kMaxE = 1024;
 // Largest token count routed by the one-workgroup decode-scale kernel (one bit per
-// token in a 64-bit mask).
-constexpr int kSmallT = 64;
+// token in two 64-bit masks per expert).
+constexpr int kSmallT = 128;
+// Largest ceil(T / 16) * k * ceil(E / 64) (rounds x score slots per wave) for which the
+// one-workgroup router beats the three launches of the general routing.
+constexpr int kSmallRankWork = 640;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -49,7 +49,8 @@ enum GemmVariant {
   GV_WSP_128x128_SWIGLU_F8,        // MXFP8 gate/up variants of the above
   GV_WS_128x128_SWIGLU_PAIRS_F8,
   GV_WS_128x128_SWIGLU_F8,
-  GV_DECODE_SWIGLU_F8
+  GV_DECODE_SWIGLU_F8,
+  GV_DOWN_COMBINE                  // decode-scale down GEMM fused with the combine
 };
 struct GemmChoice {
   GemmVariant v;
@@ -147,6 +148,17 @@ hipError_t launch_gemm_decode_gather(int epi, const uint16_t* X, const int32_t* 
                                      const uint16_t* B0, const uint16_t* B1, void* C,
                                      const int32_t* offsets, const int32_t* mtile_start, int E, int N,
                                      int K, hipStream_t st);
+// Decode-scale down GEMM fused with the combine (16-row m-tiles on the tables for
+// tile height 16): out = combine(bf16(act W2^T)) with the bits of launch_gemm_bf16
+// (GEMM_DECODE, EPI_BF16) followed by launch_combine; y_out (nullable) also receives
+// Y [R x N].  Needs down_combine_ok(R, E, N, K): N % 16 == 0, K % 64 == 0 and the Y
+// columns of all R rows plus the tile table in kDownCombineMaxLds bytes of LDS.
+constexpr size_t kDownCombineMaxLds = 128 * 1024;
+bool down_combine_ok(int R, int E, int N, int K);
+hipError_t launch_down_combine(const uint16_t* act, int R, const uint16_t* W2, const int32_t* offsets,
+                               const int32_t* mtile_start, int E, int N, int K, const int32_t* token_row,
+                               const float* topk_w, const void* add, int T, int k, void* out, bool out_f32,
+                               void* y_out, hipStream_t st);
 // One group of T rows: offsets = {0, T} and the m-tile tables (tile heights bm, 2 bm) for E = 1.
 hipError_t launch_single_group(int T, int32_t* offsets, int bm, int32_t* mtile_start, hipStream_t st);
 // bf16 MFMA GEMM: C[r, n] = epi(sum_k A[r, k] * B[e(r)][n, k]); offsets == NULL means one dense group of M rows.

@@ -151,10 +151,12 @@ __global__ __launch_bounds__(256) void k_permute(const u32x4* __restrict__ x, in
           const int r = __shfl(row, j, kWave);
           if (r < 0) continue;  // dropped (uniform over the wave)
           u32x4* dst = x_perm + (size_t)r * row16;
+          // the permuted rows are written once and read later by another kernel: a
+          // nontemporal store streams them out (R1-shaped copy: 224 -> 180 us)
 #pragma unroll
           for (int u = 0; u < kCopyUnroll; ++u) {
             const int c = cb + u * kWave + lane;
-            if (c < c1) dst[c] = v[u];
+            if (c < c1) __builtin_nontemporal_store(v[u], dst + c);
           }
         }
       }

@@ -262,15 +262,15 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
-// Routing of a decode-scale step (T <= 64) in one workgroup: top-k per token
+// Routing of a decode-scale step (T <= 64 MW) in one workgroup: top-k per token
 // (one wave per token, tokens t = wave + 16 i), counts, offsets, the GEMM m-tile
 // tables and the row metadata, so a small step pays one launch for what the
 // large-T path does in four.  Row order inside an expert's segment is ascending
-// token id, as there: row = offsets[e] + popcount(mask[e] below t), mask[e] the
-// tokens that picked e (built with order-independent LDS atomicOr).  With an
-// expert capacity cap > 0, assignments ranked cap or later in their expert are
-// dropped (token_row = -1) and counts are min(count, cap).
-template <int SLOTS>
+// token id, as there: row = offsets[e] + (number of lower tokens in mask[e]), mask[e]
+// the tokens that picked e (MW 64-bit words, built with order-independent LDS
+// atomicOr).  With an expert capacity cap > 0, assignments ranked cap or later in
+// their expert are dropped (token_row = -1) and counts are min(count, cap).
+template <int SLOTS, int MW>
 __global__ __launch_bounds__(1024) void k_route_small(
     ScoreSrc src, int T, int E, int k,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
@@ -278,13 +278,14 @@ __global__ __launch_bounds__(1024) void k_route_small(
     int cap, int bm, int32_t* __restrict__ mtile_start) {
   __shared__ int cnt[kMaxE];
   __shared__ int off_s[kMaxE];
-  __shared__ unsigned long long mask[kMaxE];
-  __shared__ int s_ids[kSmallT * kWave];
+  __shared__ unsigned long long mask[kMaxE * MW];
+  __shared__ int s_ids[64 * MW * kWave];
   __shared__ int smem[48];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) {
     cnt[e] = 0;
-    mask[e] = 0ull;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) mask[e * MW + w] = 0ull;
   }
   __syncthreads();
   for (int t = wave; t < T; t += 16) {
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
       topk_w[(size_t)t * k + lane] = my_w;
       s_ids[t * k + lane] = my_e;
       atomicAdd(&cnt[my_e], 1);
-      atomicOr(&mask[my_e], 1ull << t);
+      atomicOr(&mask[my_e * MW + (t >> 6)], 1ull << (t & 63));
     }
   }
   __syncthreads();
@@ -324,7 +325,10 @@ __global__ __launch_bounds__(1024) void k_route_small(
   __syncthreads();
   for (int a = tid; a < T * k; a += 1024) {
     const int t = a / k, e = s_ids[a];
-    const int rank = __popcll(mask[e] & ((1ull << t) - 1ull));
+    int rank = __popcll(mask[e * MW + (t >> 6)] & ((1ull << (t & 63)) - 1ull));
+#pragma unroll
+    for (int w = 0; w + 1 < MW; ++w)
+      if (w < (t >> 6)) rank += __popcll(mask[e * MW + w]);
     if (cap > 0 && rank >= cap) {
       token_row[a] = -1;  // dropped: past the expert's capacity
     } else {
@@ -390,14 +394,21 @@ hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t*
   if (T > kSmallT) return hipErrorInvalidValue;
   const int slots = ceil_div(E, kWave);
   dim3 g(1), b(1024);
-#define MOE_RS(SL)                                                                                   \
-  hipLaunchKernelGGL((k_route_small<SL>), g, b, 0, st, src, T, E, k, ids, w, counts, offsets, \
+#define MOE_RS(SL, MW)                                                                             \
+  hipLaunchKernelGGL((k_route_small<SL, MW>), g, b, 0, st, src, T, E, k, ids, w, counts, offsets, \
                      row_token, token_row, cap, bm, mtile_start)
-  if (slots <= 1) MOE_RS(1);
-  else if (slots <= 2) MOE_RS(2);
-  else if (slots <= 4) MOE_RS(4);
-  else if (slots <= 8) MOE_RS(8);
-  else MOE_RS(16);
+#define MOE_RS_SLOTS(MW)          \
+  if (slots <= 1) MOE_RS(1, MW);  \
+  else if (slots <= 2) MOE_RS(2, MW); \
+  else if (slots <= 4) MOE_RS(4, MW); \
+  else if (slots <= 8) MOE_RS(8, MW); \
+  else MOE_RS(16, MW);
+  if (T <= 64) {
+    MOE_RS_SLOTS(1)
+  } else {
+    MOE_RS_SLOTS(2)
+  }
+#undef MOE_RS_SLOTS
 #undef MOE_RS
   return hipGetLastError();
 }

@@ -133,33 +133,165 @@ def out_err_over_rms(got: np.ndarray, ref: np.ndarray, shared_ref=None) -> float
     return float(err.max() / np.sqrt(np.mean(ref ** 2)))
 
 
-def check_y_rows(bf16: bool, got: np.ndarray, ref_y: np.ndarray, inputs_rounded_apart: bool = False):
-    """Expert outputs Y against the oracle's (got: bf16 bits or fp32 values).
+U_F32 = 2.0 ** -24
 
-    Both sides round A and Y to bf16 at the same points, but the fp32 sums run in
-    different orders, so an A element near a rounding midpoint can land one ulp apart;
-    that moves Y by ulp(a) * |w2| (about 1e-3 x RMS(Y) for |a| ~ 5 x RMS(a) at I = 256).
-    Bound: every element within one bf16 ulp of Y plus 5e-3 x RMS(Y); at most 1e-4 of
-    them beyond one ulp plus 1e-3 x RMS(Y).  fp32 layers: 1e-5 x RMS(Y).
 
-    inputs_rounded_apart: the rows fed to the GPU's FFN are its own bf16 rounding of an
-    upstream fp32 sum (the latent layer's Z), which may sit one ulp from the oracle's
-    in some elements; each such element moves the exact A a little and so flips A's
-    rounding far more often than the summation order does.  Then every element must be
-    within the layer tolerance, 2e-2 x RMS(Y) (a wrong tile would be off by O(RMS))."""
-    from oracle import decode
+def fp32_dot_slack(K: int, rms_rows: np.ndarray) -> np.ndarray:
+    """How far the GPU's fp32 accumulation of a length-K dot product may land from the
+    exact sum, for a row of results whose exact values have RMS `rms_rows`: the larger of
+    8 sqrt(K) 2^-24 (eight times the random walk of K roundings of partial sums no larger
+    than the row's RMS) and 2^-14 (room for a matrix instruction that sums its products
+    more coarsely than fp32, as the fp8 one measurably does), times that RMS.  Either
+    is far below half a bf16 ulp (2^-9 relative)."""
+    return max(8.0 * np.sqrt(K) * U_F32, 2.0 ** -14) * rms_rows
+
+
+def bf16_round_interval(v: np.ndarray, dv: np.ndarray):
+    """The bf16 values (nearest even) that any value within dv of the exact v rounds to
+    lie in [round(v - dv), round(v + dv)] (rounding is monotone)."""
+    from oracle import round_bf16
+    return round_bf16(v - dv), round_bf16(v + dv)
+
+
+def _rms_rows(m: np.ndarray) -> np.ndarray:
+    return np.sqrt(np.mean(m * m, axis=1, keepdims=True))
+
+
+def expert_y_bound(x_rows, w1e, w3e, w2e, x_dev=None) -> np.ndarray:
+    """Per-element bound on |Y_gpu - Y_oracle| for one bf16 expert's rows, derived from
+    the arithmetic both sides perform: G = X W1^T and U = X W3^T as fp32 sums (within
+    fp32_dot_slack of the exact ones, plus what an input deviation x_dev >= |X_gpu - X|
+    moves them), A = bf16(SiLU(G) U) with SiLU from the hardware exp2 and reciprocal
+    (a few fp32 ulps), Y = bf16(A W2^T) as an fp32 sum.  Each rounding to bf16 may land
+    on any value between the roundings of the interval ends, so an A element near a
+    rounding midpoint may take its neighbour (that moves Y by its bf16 spacing times
+    |W2|), and Y itself may take its neighbour.  No statistics: every correct result is
+    inside, and a missing K-step, tile or expert moves Y by percent of its RMS."""
+    import oracle
+    x = oracle.decode(x_rows)
+    W1, W3, W2 = oracle.decode(w1e), oracle.decode(w3e), oracle.decode(w2e)
+    K, I = x.shape[1], W1.shape[0]
+    g, u = x @ W1.T, x @ W3.T
+    dg, du = fp32_dot_slack(K, _rms_rows(g)), fp32_dot_slack(K, _rms_rows(u))
+    if x_dev is not None:
+        dg = dg + x_dev @ np.abs(W1).T
+        du = du + x_dev @ np.abs(W3).T
+    sg = oracle.silu(g)
+    a = sg * u
+    sig = 0.5 * (1.0 + np.tanh(0.5 * g))
+    dsilu = sig * (1.0 + g * (1.0 - sig))             # d SiLU / dG, |.| <= 1.1
+    da = np.abs(dsilu * u) * dg + (np.abs(sg) + 1.1 * dg) * du + 8 * U_F32 * np.abs(a)
+    A = oracle.round_bf16(a)
+    a_lo, a_hi = bf16_round_interval(a, da)
+    dA = np.maximum(a_hi - A, A - a_lo)
+    yex = A @ W2.T
+    dy = dA @ np.abs(W2).T + fp32_dot_slack(I, _rms_rows(yex))
+    Y = oracle.round_bf16(yex)
+    y_lo, y_hi = bf16_round_interval(yex, dy)
+    return np.maximum(y_hi - Y, Y - y_lo)
+
+
+def check_y_rows(bf16: bool, got: np.ndarray, x_rows, w1e, w3e, w2e, x_dev=None):
+    """One expert's outputs Y (got: bf16 bits, or fp32 values for fp32 layers) against the
+    oracle's expert FFN on the same rows: bf16 within expert_y_bound per element, fp32
+    within 1e-5 x RMS(Y)."""
+    import oracle
+    ref = oracle.expert_ffn_rows(x_rows, w1e, w3e, w2e, bf16)
     if not bf16:
-        assert rel_err(got, ref_y) <= 1e-5
+        assert rel_err(got, ref) <= 1e-5
         return
-    y = decode(got)
-    rms = float(np.sqrt(np.mean(ref_y ** 2)))
-    err = np.abs(y - ref_y)
-    if inputs_rounded_apart:
-        worst = float(err.max()) / rms
-        assert worst <= 2e-2, f"max |err| = {worst:.2e} x RMS(Y)"
+    bound = expert_y_bound(x_rows, w1e, w3e, w2e, x_dev)
+    err = np.abs(oracle.decode(got) - ref)
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert np.all(err <= bound), (f"{int(np.sum(err > bound))} of {err.size} Y elements outside the "
+                                  f"derived bound (worst {worst:.2f}x)")
+
+
+def check_grouped_y(bf16: bool, got: np.ndarray, x_perm, offsets, w1, w3, w2):
+    """Every non-empty expert's rows of a grouped FFN output against the oracle (check_y_rows)."""
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            check_y_rows(bf16, got[lo:hi], x_perm[lo:hi], w1[e], w3[e], w2[e])
+
+
+def latent_rows_and_dev(x_rows, wd):
+    """The oracle's latent rows Z = bf16(X wd^T) of some tokens, and how far a correct
+    GPU Z may be from them per element (its fp32 sum of H products within
+    fp32_dot_slack of the exact one, then the same rounding)."""
+    import oracle
+    Z = oracle.latent_down(x_rows, wd, True)
+    z = oracle.decode(x_rows) @ oracle.decode(wd).T
+    z_lo, z_hi = bf16_round_interval(z, fp32_dot_slack(wd.shape[1], _rms_rows(z)))
+    return Z, np.maximum(z_hi - Z, Z - z_lo)
+
+
+def layer_out_bound(cfg, inp, ref) -> np.ndarray:
+    """Per-element bound on |out_gpu - out_oracle| for a bf16 layer's fp32 output, derived
+    from the arithmetic (no statistics): each routed term w_j Y_j may be off by
+    w_j times its Y bound (expert_y_bound on the rows the expert received: token rows,
+    or for latent layers the oracle's Z with the GPU Z's own derived deviation) plus the
+    fp32 routing weight's difference from the oracle's (|dw| <= 1e-6) times |Y_j|; the
+    shared expert's output by its own Y bound; the fp32 combine sums k + 1 terms (a few
+    fp32 ulps of the sum of magnitudes).  For latent layers the combined row is rounded
+    to bf16 (any value between the roundings of its interval ends) and multiplied by
+    wu as an fp32 sum.  `ref` is oracle.layer_forward's result on the same inputs."""
+    import oracle
+    E, k = cfg.E, cfg.k
+    rt, tr, offs, w = ref["row_token"], ref["token_row"], ref["offsets"], ref["weights"]
+    if cfg.L:
+        zs, zdev = latent_rows_and_dev(inp["x"], inp["wd"])
+        src, dev_rows = zs, zdev
+    else:
+        src, dev_rows = inp["x"], None
+    yb = np.zeros((int(offs[-1]), cfg.D))
+    for e in range(E):
+        lo, hi = int(offs[e]), int(offs[e + 1])
+        if hi > lo:
+            toks = rt[lo:hi]
+            yb[lo:hi] = expert_y_bound(src[toks], inp["w1"][e], inp["w3"][e], inp["w2"][e],
+                                       None if dev_rows is None else dev_rows[toks])
+    Y = oracle.decode(ref["y_perm"]) if ref["y_perm"].dtype == np.uint16 else ref["y_perm"]
+    bound = np.zeros((cfg.T, cfg.D))
+    mag = np.zeros((cfg.T, cfg.D))
+    for j in range(k):
+        r = tr[:, j]
+        kept = r >= 0
+        rr = np.where(kept, r, 0)
+        wj = np.where(kept, np.abs(w[:, j]), 0.0)[:, None]
+        bound += wj * yb[rr] + np.where(kept, 1e-6, 0.0)[:, None] * np.abs(Y[rr])
+        mag += wj * (np.abs(Y[rr]) + yb[rr])
+    if "ws1" in inp:
+        ysh = oracle.decode(ref["y_shared"]) if ref["y_shared"].dtype == np.uint16 else ref["y_shared"]
+        shb = expert_y_bound(inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
+        bound += shb
+        mag += np.abs(ysh) + shb
+    bound += 4 * (k + 1) * U_F32 * mag
+    if cfg.L:
+        oc = ref["out_combine"]
+        OL = oracle.round_bf16(oc)
+        lo_, hi_ = bf16_round_interval(oc, bound)
+        dol = np.maximum(hi_ - OL, OL - lo_)
+        WU = oracle.decode(inp["wu"])
+        out = OL @ WU.T
+        bound = dol @ np.abs(WU).T + fp32_dot_slack(cfg.L, _rms_rows(out))
+    return bound
+
+
+def check_layer_out(cfg, inp, ref, got_out: np.ndarray, keep: np.ndarray = None):
+    """The layer's fp32 output against the oracle's on every element (of the tokens in
+    `keep`): within layer_out_bound for bf16 layers, 1e-5 x RMS for fp32 layers."""
+    ref_out = ref["out"]
+    if keep is None:
+        keep = np.ones(cfg.T, dtype=bool)
+    assert not cfg.L, ("latent layers: the worst case of every Z element that may round either way "
+                       "moving every G element makes this bound uninformative; their layer check is the "
+                       "north-star tolerance")
+    if cfg.dtype != "bf16":
+        assert rel_err(got_out[keep], ref_out[keep]) <= 1e-5
         return
-    ulp = bf16_ulp(ref_y)
-    worst = float(np.max((err - ulp) / rms))
-    assert not (err > ulp + 5e-3 * rms).any(), f"worst excess over 1 ulp: {worst:.2e} x RMS"
-    frac = float(np.mean(err > ulp + 1e-3 * rms))
-    assert frac <= 1e-4, f"{frac:.2e} of elements beyond 1 ulp + 1e-3 RMS (worst {worst:.2e})"
+    bound = layer_out_bound(cfg, inp, ref)[keep]
+    err = np.abs(got_out[keep] - ref_out[keep])
+    bad = err > bound
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} outputs outside the derived bound (worst {worst:.2f}x)"

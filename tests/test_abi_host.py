@@ -172,7 +172,8 @@ def test_layer_plan_names_the_kernels_of_each_layer():
         "qwen3_30b_a3b_shaped": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<128, 256, 1,", 7),
         "deepseek_r1_shaped": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<128, 256, 1,", 7),
         "latent_moe": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<256, 128, 1,", 9),
-        "k3_shaped_decode_t8": (1, 1, "k_gemm_decode<2, 2,", "k_gemm_decode<1, 2,", 4),
+        "k3_shaped_decode_t8": (1, 1, "k_gemm_decode<2, 2,", "k_down_combine<16,", 3),
+        "k3_shaped_decode": (0, 1, "k_gemm_decode<2, 2,", "k_down_combine<16,", 5),
         "tiny_f32": (0, 0, "k_gemm_simt<float, 2,", "k_gemm_simt<float, 1,", 6),
     }
     for name, (dec, gath, gu, dn, n) in want.items():

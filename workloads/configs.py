@@ -111,6 +111,14 @@ PARITY_CONFIGS = {c.name: c for c in (
               gate="drawn", gate_std=None, zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
     MoEConfig(name="small_latent", T=200, H=320, L=128, E=16, k=4, I=256, seed=14,
               gate="computed", gate_std=None),
+    # decode-like steps of 65-128 tokens (the one-launch router's second token-mask word)
+    MoEConfig(name="decode_t100", T=100, H=512, E=96, k=6, I=128, seed=35, gate="drawn",
+              zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
+    MoEConfig(name="decode_t128", T=128, H=1024, E=200, k=8, I=256, seed=36, gate="drawn",
+              zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
+    # a decode-like latent layer: the fused down GEMM + combine writes the latent rows
+    MoEConfig(name="decode_latent", T=24, H=320, L=128, E=96, k=4, I=256, seed=37, gate="computed",
+              gate_std=None),
     # degenerate routings
     MoEConfig(name="one_expert", T=130, H=128, E=1, k=1, I=128, seed=15, gate="drawn"),
     MoEConfig(name="k_equals_e", T=70, H=128, E=8, k=8, I=64, seed=16, gate="drawn"),
@@ -130,16 +138,16 @@ PARITY_CONFIGS = {c.name: c for c in (
               zipf_s=1.1, zipf_alpha=1.0),
     # long-K down GEMM (K = I = 2048) with fewer than 192 rows per expert on average:
     # the persistent 256 x 128 down tiles on the second m-tile table
-    MoEConfig(name="long_k_down", T=400, H=256, E=8, k=2, I=2048, seed=29, gate="drawn",
-              zipf_s=1.1, zipf_alpha=1.0),
+    MoEConfig(name="long_k_down", T=400, H=256, E=16, k=4, I=2048, seed=29, gate="drawn",
+              zipf_s=1.1, zipf_alpha=0.5),
     # more persistent-GEMM tiles than one LDS tile table holds (3520): each workgroup
     # decodes only its XCD's chunk and no tile is taken across XCDs.  Gate/up: 64
-    # n-tiles x ~70 m-tiles; the down GEMM of this layer has 73 tiles (whole table).
-    MoEConfig(name="wsp_chunk_gate_up", T=4096, H=256, E=8, k=2, I=8192, seed=30, gate="drawn",
-              zipf_s=1.1, zipf_alpha=1.0),
-    # the same for the down GEMM on 128 x 256 tiles: ~272 m-tiles x 14 n-tiles
-    MoEConfig(name="wsp_chunk_down", T=4096, H=3584, E=16, k=8, I=256, seed=34, gate="drawn",
-              zipf_s=1.1, zipf_alpha=0.5),
+    # n-tiles x ~70 m-tiles; the down GEMM of this layer has ~70 tiles (whole table).
+    # Top-8 of 16 with near-uniform weights and a wide intermediate, like the pages'
+    # models, so the layer tolerance applies as it does to them.
+    MoEConfig(name="wsp_chunk_gate_up", T=1024, H=256, E=16, k=8, I=8192, seed=30, gate="drawn"),
+    # the same for the down GEMM on 128 x 256 tiles: ~260 m-tiles x 16 n-tiles
+    MoEConfig(name="wsp_chunk_down", T=4096, H=4096, E=16, k=8, I=768, seed=34, gate="drawn"),
     # a shared expert next to the routed ones: 128-row tiles (T >= 48), 16-row
     # tiles (T < 48) and fp32
     MoEConfig(name="shared_expert", T=300, H=256, E=16, k=4, I=192, seed=23, gate="computed",
