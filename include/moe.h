@@ -124,9 +124,11 @@ typedef enum moe_call {
 /* [0] start  [1] after latent down-projection  [2] after gate  [3] after top-k+count+scan
  * [4] after permute  [5] after expert gate/up GEMM  [6] after expert down GEMM
  * [7] after the shared expert  [8] after combine  [9] after latent up-projection.
- * Stages that do not run leave two consecutive events back to back.  On decode-scale
- * steps (moe_plan.decode_path; no shared expert) the combine runs inside the down
- * GEMM's launch, so its time shows in [5]..[6] and [7]..[8] is empty. */
+ * Stages that do not run leave two consecutive events back to back.  When the down
+ * GEMM's kernel is the fused down GEMM + combine (moe_plan.down_kernel
+ * "k_down_combine<...>": bf16 steps on the 16-row decode tiles, no shared expert) the
+ * combine runs inside the down GEMM's launch, so its time shows in [5]..[6] and
+ * [7]..[8] is empty. */
 
 typedef struct moe_shape {
   int64_t T;      /* tokens */
