@@ -286,7 +286,7 @@ def check_layer_out(cfg, inp, ref, got_out: np.ndarray, keep: np.ndarray = None)
         keep = np.ones(cfg.T, dtype=bool)
     assert not cfg.L, ("latent layers: the worst case of every Z element that may round either way "
                        "moving every G element makes this bound uninformative; their layer check is the "
-                       "north-star tolerance")
+                       "layer tolerance of 2e-2 x RMS(out)")
     if cfg.dtype != "bf16":
         assert rel_err(got_out[keep], ref_out[keep]) <= 1e-5
         return
