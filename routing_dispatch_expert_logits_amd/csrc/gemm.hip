@@ -579,11 +579,13 @@ __global__ __launch_bounds__(MW * 64 + 128) void k_gemm_ws(
 // eleventh wave makes the claims (and, for gathered rows, DMAs the next tile's token
 // row indices into LDS), so the loader waves never wait on anything but their own
 // LDS DMA: a claim's result in a loader wave would make the compiler drain its DMA.
-// Each workgroup decodes the tile coordinates once into an LDS table: every tile
-// when they fit, and then a workgroup whose chunk is done takes tiles left in
-// other XCDs' chunks; else its own chunk.  Tiles, K-steps,
-// LDS layout and MFMA order are those of k_gemm_ws, so the results are the same
-// bits.  The claim counters must be zero at launch: the m-tile table kernels
+// Each workgroup decodes the tile coordinates once into an LDS table (every tile
+// when they fit, else its own XCD's chunk).  A workgroup whose chunk is done takes
+// tiles left in other XCDs' chunks, from the chunk with the most left (the XCDs
+// finish a few percent apart); a taken tile outside its table is decoded from the
+// m-tile table in memory, and the scheduler wave publishes every claimed tile's
+// coordinates in LDS.  Tiles, K-steps, LDS layout and MFMA order are those of
+// k_gemm_ws, so the results are the same bits.  The claim counters must be zero at launch: the m-tile table kernels
 // (k_offsets, k_route_small, k_single_group) clear them.
 
 // Chunk entries an LDS table can hold (4 bytes each: expert | m-tile << 10 | n-tile << 22).
@@ -628,6 +630,7 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
   __shared__ __attribute__((aligned(16))) uint16_t lds[S * STAGE];
   __shared__ uint32_t table[CAP];
   __shared__ int claimed[4];       // logical index of tile ti of this workgroup at [ti % 4], -1 past the end
+  __shared__ uint32_t centry[4];   // its packed coordinates (expert | m-tile << 10 | n-tile << 22)
   __shared__ int32_t grow[2][BM];  // gathered rows: token row of each tile row, tile ti at [ti % 2]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -637,9 +640,7 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
   const int xcd = blockIdx.x & 7;
   const int lo = xcd * per_xcd, chunk = max(0, min(per_xcd, total - lo));  // chunk <= CAP by wsp_fits
   if (total == 0) return;
-  // With every tile in the table, a workgroup whose XCD chunk is done takes tiles
-  // from the chunk with the most left (the XCDs finish a few percent apart);
-  // otherwise the table holds this XCD's chunk only.
+  // The table holds every tile when they fit, else this XCD's chunk only.
   const bool all = total <= CAP;
   const int tlo = all ? 0 : lo, tcount = all ? total : chunk;
   // table[L - tlo] for logical tile L in logical order (expert-major, then n-tile, then m-tile)
@@ -654,10 +655,10 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
   __syncthreads();
   const int nsteps = K / BK;
 
-  // logical tile L: expert, first row, rows, first column (wave-uniform)
-#define MOE_WSP_COORDS(L, e, r0, rows, n0)                                                     \
+  // packed coordinates V of a tile: expert, first row, rows, first column (wave-uniform)
+#define MOE_WSP_COORDS(V, e, r0, rows, n0)                                                     \
   {                                                                                            \
-    const uint32_t v_ = table[(L) - tlo];                                                      \
+    const uint32_t v_ = (V);                                                                   \
     e = __builtin_amdgcn_readfirstlane((int)(v_ & 1023u));                                     \
     const int m_ = __builtin_amdgcn_readfirstlane((int)((v_ >> 10) & 4095u));                  \
     n0 = __builtin_amdgcn_readfirstlane((int)(v_ >> 22)) * BN;                                 \
@@ -674,7 +675,6 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
     // later agent-scope load of it shows, so the loop ends after at most 9 rounds.
     auto take = [&](int own) -> int {
       if (own < chunk) return lo + own;
-      if (!all) return -1;
       for (int round = 0; round < 16; ++round) {
         int left = -1;
         if (lane < 8) {
@@ -700,12 +700,36 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
       }
       return -1;
     };
-    // publish tile ti's claim and (gathered rows) DMA its token-row indices into grow
+    // The packed coordinates of logical tile L: from the LDS table when it holds L, else
+    // (a tile taken from another XCD's chunk) from the m-tile table in memory: the expert
+    // is the last e with mtile_start[e] <= L / NT (the table is non-decreasing, so those
+    // e form a prefix, counted 64 at a time with a ballot), then the table's own decode.
+    auto entry_of = [&](int L) -> uint32_t {
+      if (L >= tlo && L < tlo + tcount) return table[L - tlo];
+      const int mrow = L / NT;
+      int p = 0;
+      for (int base = 0; base <= E; base += 64) {
+        const int idx = base + lane;
+        const int c = __popcll(__ballot(idx <= E && mtile_start[min(idx, E)] <= mrow));
+        p += c;
+        if (c < 64) break;
+      }
+      const int e = p - 1;
+      const int mt0 = mtile_start[e], mte = mtile_start[e + 1] - mt0;
+      const int local = L - mt0 * NT, n = local / mte, m = local - n * mte;
+      return (uint32_t)e | ((uint32_t)m << 10) | ((uint32_t)n << 22);
+    };
+    // publish tile ti's claim and coordinates, and (gathered rows) DMA its token-row
+    // indices into grow
     auto publish = [&](int ti, int L) {
-      if (lane == 0) claimed[ti & 3] = L;
+      const uint32_t ent = L >= 0 ? entry_of(L) : 0u;
+      if (lane == 0) {
+        claimed[ti & 3] = L;
+        centry[ti & 3] = ent;
+      }
       if (gather && L >= 0) {
         int g_e, g_r0, g_rows, g_n0;
-        MOE_WSP_COORDS(L, g_e, g_r0, g_rows, g_n0)
+        MOE_WSP_COORDS(ent, g_e, g_r0, g_rows, g_n0)
         (void)g_e;
         (void)g_n0;
 #pragma unroll
@@ -752,10 +776,10 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
     int ldsoff[NQP];
     const uint8_t* ssrc[NSP > 0 ? NSP : 1];
     int sldsoff[NSP > 0 ? NSP : 1];
-#define MOE_WSP_SET_TILE(t, ti)                                                                       \
+#define MOE_WSP_SET_TILE(ti)                                                                          \
   {                                                                                                   \
     int t_e, t_r0, t_rows, t_n0;                                                                      \
-    MOE_WSP_COORDS(t, t_e, t_r0, t_rows, t_n0)                                                        \
+    MOE_WSP_COORDS(centry[(ti) & 3], t_e, t_r0, t_rows, t_n0)                                         \
     _Pragma("unroll") for (int j = 0; j < NQP; ++j) {                                                 \
       const int q = p * NQP + j;                                                                      \
       if (q < QA) {                                                                                   \
@@ -805,7 +829,7 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
     int it = 0, ist = 0;  // tile and K-step of the next stage to issue
     int fslot = 0;        // its LDS ring slot
     bool more = true;     // whether tile `it` still has stages to issue
-    MOE_WSP_SET_TILE(claimed[0], 0)
+    MOE_WSP_SET_TILE(0)
     for (int f = 0; f < S - 1; ++f) {  // nsteps >= 4: both stages belong to the first tile
       MOE_WSP_ISSUE(fslot)
       fslot = fslot + 1 == S ? 0 : fslot + 1;
@@ -822,7 +846,7 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
           if (tn >= 0) {
             ++it;
             ist = 0;
-            MOE_WSP_SET_TILE(tn, it)
+            MOE_WSP_SET_TILE(it)
           } else {
             more = false;
           }
@@ -948,7 +972,7 @@ __global__ __launch_bounds__(MW * 64 + 192) void k_gemm_wsp(
     const int t = __builtin_amdgcn_readfirstlane(claimed[ti & 3]);
     if (t < 0) break;
     int t_e, t_r0, t_rows, t_n0;
-    MOE_WSP_COORDS(t, t_e, t_r0, t_rows, t_n0)
+    MOE_WSP_COORDS(centry[ti & 3], t_e, t_r0, t_rows, t_n0)
     (void)t_e;
     if (wm * TM >= t_rows) {  // no valid rows for this wave: keep the barrier cadence
       for (int st = 0; st < nsteps; ++st) {
