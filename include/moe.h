@@ -353,7 +353,9 @@ typedef struct moe_layer_aux {
  * reading the token rows through row_token; the down GEMM with the combine, each
  * workgroup owning 16 output columns of every row.  The output bits are those of the
  * separate calls.  Latent projections, MXFP8 conversion of the token rows, a requested
- * permuted copy and a shared expert add their own launches.
+ * permuted copy and a shared expert add their own launches.  A step whose ranking is
+ * too much work for one workgroup (ceil(T / 16) * k * ceil(E / 64) above 640, e.g. 896
+ * experts, top-16, T = 128) routes with the general kernels instead: two launches more.
  *
  * Latent layers (s->L > 0) follow "Latent MoE" (Definition; Current Synthesis):
  * the router scores the full-width X, the rows dispatched are Z = X wd^T, and the
@@ -396,7 +398,7 @@ MOE_API moe_status moe_layer_forward(const moe_layer_weights* w, const void* x, 
  *
  * Limit: shapes whose layer workspace, moe_workspace_bytes(s, MOE_CALL_LAYER), exceeds
  * MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE (64 MiB holds decode-scale steps, e.g.
- * the 896-expert top-16 layer up to T = 256 tokens, or a 256-expert top-8 layer of width
+ * the 896-expert top-16 layer up to T = 340 tokens, or a 256-expert top-8 layer of width
  * 7168 up to T = 128).  Other errors as moe_layer_forward.
  *
  * Every call on one GPU shares that GPU's array and finds the last call's contents in

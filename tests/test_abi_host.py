@@ -190,6 +190,16 @@ def test_layer_plan_names_the_kernels_of_each_layer():
     with pytest.raises(B.MoeError):
         B.layer_plan(B.shape(0, 128, 8, 2, 256), True)
     assert B.lib.moe_layer_plan(ctypes.byref(s), 8, None) == B.MOE_ERR_INVALID_ARG
+    # decode-scale steps route in one launch while ceil(T / 16) * k * ceil(E / 64) <= 640
+    # and T <= 128: 3 launches, 4 when the Y columns do not fit the fused down GEMM +
+    # combine's LDS; past either bound the general routing kernels add two
+    for T, E, k, one in ((1, 8, 2, True), (64, 1024, 8, True), (8, 896, 16, True),
+                         (128, 200, 8, True), (120, 700, 12, False), (65, 896, 16, False),
+                         (129, 64, 2, False)):
+        p = B.layer_plan(B.shape(T, 256, E, k, 128), False)
+        fused = p["down_kernel"] == "k_down_combine<16,"
+        assert p["decode_path"] == int(one), (T, E, k)
+        assert p["launches"] == (3 if fused else 4) + (0 if one else 2), (T, E, k)
 
 
 def test_persistent_tile_table_fields_bound_the_expert_rows():

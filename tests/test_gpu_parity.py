@@ -509,15 +509,16 @@ def test_stage_events_skip_null_entries():
 
 @pytest.mark.parametrize("name", ["shared_expert", "shared_expert_decode", "shared_expert_f32",
                                   "small_bf16_decode", "single_token", "many_empty", "decode_t100",
-                                  "decode_t128", "all_ties", "capacity_prefill", "capacity_decode",
-                                  "capacity_f32"])
+                                  "decode_t128", "decode_many_experts", "decode_many_experts_cap", "all_ties",
+                                  "capacity_prefill", "capacity_decode", "capacity_f32"])
 def test_layer_output_equals_separate_calls(name):
     """Fused layer == route, permute, grouped FFN, (the shared expert as a
     one-expert grouped FFN over all tokens,) and the combine, bit for bit: the
     fusion is execution-only.  Decode-scale layers (T <= 128 with 16-row tiles)
-    take the one-launch routing, the gathering gate/up GEMM and the down GEMM fused
-    with the combine in the fused call (its Y, written to aux.y_perm, has the bits of
-    the separate down GEMM), the general kernels in the separate calls."""
+    take the one-launch routing (the general routing kernels for decode_many_experts*),
+    the gathering gate/up GEMM and the down GEMM fused with the combine in the fused
+    call (its Y, written to aux.y_perm, has the bits of the separate down GEMM), the
+    general kernels in the separate calls."""
     cfg = PARITY_CONFIGS[name]
     inp = gen.layer_inputs(cfg)
     a = run_layer(cfg, inp)
@@ -551,6 +552,38 @@ def test_layer_output_equals_separate_calls(name):
     if cfg.shared_I:  # and the shared expert alone matches the oracle's
         bf = cfg.dtype == "bf16"
         check_y_rows(bf, host(ysh, bf), inp["x"], inp["ws1"], inp["ws3"], inp["ws2"])
+
+
+@pytest.mark.parametrize("name", ["small_bf16_decode", "decode_many_experts", "small_bf16_zipf"])
+def test_layer_under_graph_capture(name):
+    """The layer captured into a graph on a side stream (the library launches kernels
+    only: no allocation, copy, memset or host synchronisation) replays with the output
+    bits of the eager call, on every replay, with eager work and synchronisations
+    between the replays."""
+    cfg = PARITY_CONFIGS[name]
+    inp = gen.layer_inputs(cfg)
+    s = shape_of(cfg)
+    w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2") if n in inp}
+    if "bias" in inp:
+        w["gate_bias"] = dev(inp["bias"])
+    x = dev(inp["x"])
+    logits = dev(inp["logits"]) if "logits" in inp else empty((cfg.T, cfg.E), "f32")
+    ref = empty((cfg.T, cfg.H), "f32")
+    B.layer_forward(w, x, logits, ref, B.MOE_F32, s, ws(s, B.MOE_CALL_LAYER))
+    torch.cuda.synchronize()
+    want = host(ref)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda:0")
+    wsg = ws(s, B.MOE_CALL_LAYER)
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        B.layer_forward(w, x, logits, out, B.MOE_F32, s, wsg, stream=st.cuda_stream)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), want)
 
 
 def test_concurrent_layers_on_two_streams():

@@ -116,6 +116,13 @@ PARITY_CONFIGS = {c.name: c for c in (
               zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
     MoEConfig(name="decode_t128", T=128, H=1024, E=200, k=8, I=256, seed=36, gate="drawn",
               zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
+    # decode-scale steps whose ranking is too much work for one workgroup (many experts,
+    # large k, like the 896-expert top-16 step at T = 128): the general routing kernels,
+    # then the decode tiles and the fused down GEMM + combine; one with an expert capacity
+    MoEConfig(name="decode_many_experts", T=120, H=256, E=700, k=12, I=128, seed=38, gate="drawn",
+              zipf_s=1.2, zipf_alpha=ZIPF_ALPHA),
+    MoEConfig(name="decode_many_experts_cap", T=60, H=256, E=1024, k=16, I=128, seed=39,
+              gate="drawn", zipf_s=1.2, zipf_alpha=ZIPF_ALPHA, capacity=3),
     # a decode-like latent layer: the fused down GEMM + combine writes the latent rows
     MoEConfig(name="decode_latent", T=24, H=320, L=128, E=96, k=4, I=256, seed=37, gate="computed",
               gate_std=None),
