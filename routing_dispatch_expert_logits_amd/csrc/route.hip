@@ -262,7 +262,7 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
-// Routing of a decode-scale step (T <= 64 MW) in one workgroup: top-k per token
+// Routing of a decode-scale step (T <= 64 MW, MW = 1 or 2) in one workgroup: top-k per token
 // (one wave per token, tokens t = wave + 16 i), counts, offsets, the GEMM m-tile
 // tables and the row metadata, so a small step pays one launch for what the
 // large-T path does in four.  Row order inside an expert's segment is ascending

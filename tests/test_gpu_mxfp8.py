@@ -36,9 +36,9 @@ def _mx(cfg):
 
 
 # bf16 layers whose dispatched width is a multiple of 128, plus a decode-scale layer
-# above 64 tokens (16-row tiles through the general routing kernels)
+# above 128 tokens (16-row tiles through the general routing kernels)
 MX_CFGS = [_mx(c) for c in PARITY_CONFIGS.values() if c.dtype == "bf16" and c.D % 128 == 0]
-MX_CFGS.append(MoEConfig(name="mx_decode_general", T=100, H=256, E=64, k=4, I=128, seed=41,
+MX_CFGS.append(MoEConfig(name="mx_decode_general", T=130, H=256, E=64, k=4, I=128, seed=41,
                          gate="drawn", dispatch="mxfp8"))
 MX_IDS = [c.name for c in MX_CFGS]
 
@@ -298,12 +298,12 @@ def test_layer_mx_equals_separate_calls(name):
 
 # MXFP8 layers whose gate/up GEMM reads the token rows through row_token when the caller
 # does not ask for the permuted codes: persistent prefill tiles (D / 2 >= 256 16-bit
-# columns) and decode-scale tiles above 64 tokens
+# columns) and decode-scale tiles above 128 tokens (the general routing kernels)
 MX_GATHER = [MoEConfig(name="mx_gather_prefill", T=300, H=512, E=16, k=4, I=192, seed=43,
                        gate="computed", gate_std=0.05, dispatch="mxfp8"),
              MoEConfig(name="mx_gather_prefill_ragged", T=517, H=640, E=24, k=6, I=320, seed=44,
                        gate="drawn", dispatch="mxfp8"),
-             MoEConfig(name="mx_gather_decode", T=100, H=512, E=64, k=4, I=128, seed=45,
+             MoEConfig(name="mx_gather_decode", T=130, H=512, E=64, k=4, I=128, seed=45,
                        gate="drawn", dispatch="mxfp8")]
 
 

@@ -406,15 +406,16 @@ def test_layer_matches_separate_calls_and_is_deterministic(name):
 
 
 GATHER_CFGS = ["small_bf16_zipf", "small_bf16_uniform", "wide_experts", "shared_expert", "capacity_prefill",
-               "all_ties"]
+               "all_ties", "decode_many_experts", "decode_t128"]
 
 
 @pytest.mark.parametrize("name", GATHER_CFGS)
 def test_layer_gathered_rows_equal_permuted_copy(name):
     """Without aux x_perm the fused layer writes only the row metadata and its gate/up
-    GEMM reads the token rows through row_token (persistent prefill tiles, or decode
-    tiles above 64 tokens); the output bits equal those of the layer that writes the
-    permuted copy, and its routing metadata is the same."""
+    GEMM reads the token rows through row_token (persistent prefill tiles; decode tiles
+    after the general routing or after the one-launch routing); the output bits equal
+    those of the layer that writes the permuted copy, and its routing metadata is the
+    same."""
     cfg = PARITY_CONFIGS[name]
     inp = gen.layer_inputs(cfg)
     a = run_layer(cfg, inp)
