@@ -14,23 +14,6 @@
 
 namespace moe {
 
-// One workgroup per 16-token ranking block, one token per wave.  A wave holds
-// the token's E scores as order keys (order_key(score): larger score, larger
-// key).  Each of the k rounds takes the wave-wide largest key, then the lowest
-// expert index holding it (so equal scores go to the lower index), and removes
-// that entry; both reductions are DPP row butterflies plus readlane.  Counts per
-// expert for the block are gathered in LDS (order-independent) and written to
-// block_counts[block][e].
-// The k experts of one token, ranked by one wave: lane j < k receives the j-th
-// expert id and its renormalised weight.  Scores become order keys
-// (order_key(score): larger score, larger key); each of the k rounds takes the
-// wave-wide largest key, then the lowest expert index holding it (so equal scores
-// go to the lower index), and removes that entry; both reductions are DPP row
-// butterflies plus readlane.
-// The token's scores come from src (see ScoreSrc): a scores row plus an optional
-// bias formed on the fly, or the gate's split-K partial rows summed in ascending
-// slice order plus the bias, the sum then written out as the token's logits row
-// (the arithmetic of k_gate_reduce, so the logits are the same bits).
 // A pointer every lane of the wave holds, moved to scalar registers (the caller
 // guarantees it is wave-uniform), so loads through it take a scalar base.
 template <class P>
@@ -41,9 +24,94 @@ __device__ __forceinline__ P* uniform_ptr(P* p) {
   return reinterpret_cast<P*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Between accesses of one wave to its own LDS slice: the LDS serves a wave's
+// instructions in issue order, so only the compiler must keep them in order.
+__device__ __forceinline__ void lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Top-k of one wave's keys (SLOTS per lane, entry lane + 64 s, expert index
+// < E real) by a threshold.  Each lane's largest key belongs to a different
+// entry, so if at least k lane maxima reach tau, the k-th largest key reaches it
+// too and every entry of the top k has a key >= tau.  tau is the largest value
+// with zero low 16 bits for which that holds (a bitwise search over the lane
+// maxima).  The real entries with key >= tau (typically k to 1.5 k of them) are
+// packed into one per lane through the wave's 64-entry LDS slice, and each takes
+// its exact position in the order from a pass over the others; the first k are
+// the top k, since every other entry's key is below tau.  Returns false, with
+// nothing written, when more than 64 entries reach tau (heavy ties); the caller
+// then ranks in rounds.  On success lane j < k holds the j-th expert and its
+// score (from the key, so -0.0 reads back as +0.0, as in the rounds).
+template <int SLOTS>
+__device__ __forceinline__ bool rank_by_threshold(const uint32_t (&key)[SLOTS], int E, int k, int lane,
+                                                  uint32_t* __restrict__ lkey, int* __restrict__ lidx,
+                                                  int& my_e, float& my_s) {
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int s = 1; s < SLOTS; ++s) lm = max(lm, key[s]);
+  uint32_t tau = 0;
+#pragma unroll
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t c = tau | (1u << b);
+    if (__popcll(__ballot(lm >= c)) >= k) tau = c;
+  }
+  // the candidates' masks are formed twice (count, then place) rather than kept:
+  // SLOTS 64-bit masks held across both loops spilled at 16 slots
+  int n = 0;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) n += __popcll(__ballot(lane + s * kWave < E && key[s] >= tau));
+  if (n > kWave) return false;
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    const bool in = lane + s * kWave < E && key[s] >= tau;
+    const unsigned long long m = __ballot(in);
+    if (in) {
+      const int at = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+      lkey[at] = key[s];
+      lidx[at] = lane + s * kWave;
+    }
+    base += __popcll(m);
+  }
+  lds_order();
+  const uint32_t ck = lane < n ? lkey[lane] : 0u;
+  const int ci = lane < n ? lidx[lane] : 0x7fffffff;
+  int pos = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ck), j));
+    const int ij = __builtin_amdgcn_readlane(ci, j);
+    pos += (kj > ck || (kj == ck && ij < ci)) ? 1 : 0;
+  }
+  lds_order();
+  if (lane < n && pos < k) {
+    lkey[pos] = ck;
+    lidx[pos] = ci;
+  }
+  lds_order();
+  my_e = lane < k ? lidx[lane] : 0;
+  my_s = lane < k ? key_to_score(lkey[lane]) : 0.f;
+  lds_order();  // read before the slice's next use
+  return true;
+}
+
+// The k experts of one token, ranked by one wave: lane j < k receives the j-th
+// expert id and its renormalised weight.  Scores become order keys
+// (order_key(score): larger score, larger key), and the order is larger key
+// first, then the lower expert index (so equal scores go to the lower index).
+// Two exact ways to the same k: rank_by_threshold below, and, where its candidate
+// set is too large, k rounds that each take the wave-wide largest key, then the
+// lowest expert index holding it, and remove that entry (both reductions DPP row
+// butterflies plus readlane).
+// The token's scores come from src (see ScoreSrc): a scores row plus an optional
+// bias formed on the fly, or the gate's split-K partial rows summed in ascending
+// slice order plus the bias, the sum then written out as the token's logits row
+// (the arithmetic of k_gate_reduce, so the logits are the same bits).
+// lkey / lidx: the wave's 64-entry LDS slice for rank_by_threshold.
 template <int SLOTS>
 __device__ __forceinline__ void rank_token(const ScoreSrc& src, size_t row0, int E, int k, int lane,
-                                           int& my_e, float& my_w) {
+                                           uint32_t* lkey, int* lidx, int& my_e, float& my_w) {
   // every load is issued unconditionally (lanes past E read the last score and
   // are masked afterwards) so they overlap instead of each waiting in a branch.
   // The row is the same for the whole wave: a scalar base plus 32-bit lane offsets
@@ -79,6 +147,11 @@ __device__ __forceinline__ void rank_token(const ScoreSrc& src, size_t row0, int
     key[s] = lane + s * kWave < E ? order_key(v[s]) : 0u;  // 0 is below every real key
   my_e = 0;
   float my_s = 0.f, top = 0.f;
+  // the threshold pass costs about as much as the rounds below at 2 slots and far
+  // less from 4 on (E = 896, k = 16: about 500 instead of 1900 instructions)
+  if (SLOTS >= 4 && rank_by_threshold<SLOTS>(key, E, k, lane, lkey, lidx, my_e, my_s)) {
+    top = __shfl(my_s, 0, kWave);
+  } else {
   for (int j = 0; j < k; ++j) {
     uint32_t lm = key[0];
 #pragma unroll
@@ -99,6 +172,7 @@ __device__ __forceinline__ void rank_token(const ScoreSrc& src, size_t row0, int
     for (int s = 0; s < SLOTS; ++s)
       if (lane + s * kWave == e) key[s] = 0u;
   }
+  }
   // Renormalised softmax over the selected k: the full-E denominator cancels.
   const float ex = lane < k ? expf(my_s - top) : 0.f;
   const float sum = wave_sum_f32(ex);
@@ -115,6 +189,8 @@ __global__ __launch_bounds__(1024) void k_topk(ScoreSrc src, int T, int E, int k
                                                int32_t* __restrict__ block_counts) {
   static_assert(kBlockTok == 16, "one token per wave of a 1024-thread workgroup");
   __shared__ int cnt[kMaxE];
+  __shared__ uint32_t rk_key[16][kWave];
+  __shared__ int rk_idx[16][kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) cnt[e] = 0;
   __syncthreads();
@@ -123,7 +199,7 @@ __global__ __launch_bounds__(1024) void k_topk(ScoreSrc src, int T, int E, int k
   if (t < T) {
     int my_e;
     float my_w;
-    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, my_e, my_w);
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, rk_key[wave], rk_idx[wave], my_e, my_w);
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_e;
       topk_w[(size_t)t * k + lane] = my_w;
@@ -281,6 +357,8 @@ __global__ __launch_bounds__(1024) void k_route_small(
   __shared__ unsigned long long mask[kMaxE * MW];
   __shared__ int s_ids[64 * MW * kWave];
   __shared__ int smem[48];
+  __shared__ uint32_t rk_key[16][kWave];
+  __shared__ int rk_idx[16][kWave];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += 1024) {
     cnt[e] = 0;
@@ -291,7 +369,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
   for (int t = wave; t < T; t += 16) {
     int my_e;
     float my_w;
-    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, my_e, my_w);
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, rk_key[wave], rk_idx[wave], my_e, my_w);
     if (lane < k) {
       topk_ids[(size_t)t * k + lane] = my_e;
       topk_w[(size_t)t * k + lane] = my_w;

@@ -80,6 +80,24 @@ def test_route_ties_and_signed_zeros(E, k):
     _check_route(cfg, lg, None)
 
 
+@pytest.mark.parametrize("E,k", [(256, 8), (300, 8), (700, 12), (896, 16), (1024, 16), (512, 32)])
+def test_route_ties_at_threshold(E, k):
+    """Integer scores from a range wide enough that ties sit at the k-th place but
+    few entries reach it (the threshold ranking, not the rounds, orders them), plus
+    tokens whose top entries are all one value (more than 64 reach the threshold,
+    so those tokens are ranked in rounds), and a token of -inf with k finite entries."""
+    T = 160
+    r = np.random.default_rng(E * 31 + k)
+    lg = r.integers(-40, 41, size=(T, E)).astype(np.float32)
+    lg[10:20, :] = 3.0                          # all tied
+    lg[20:30, : E // 2] = 7.0                   # half tied at the top
+    lg[30, :] = -np.inf
+    lg[30, E - k:] = 1.0                        # exactly k finite, at the highest indices
+    lg[31, :] = r.integers(0, 2, size=E).astype(np.float32) * 0.5   # two values
+    cfg = PARITY_CONFIGS["all_ties"].with_(T=T, E=E, k=k)
+    _check_route(cfg, lg, None)
+
+
 @pytest.mark.parametrize("E,k", [(300, 8), (500, 9), (1024, 64)])
 def test_route_many_tokens_wide(E, k):
     """More than 2048 tokens (over 128 ranking blocks, so every scan thread walks
@@ -384,6 +402,34 @@ def test_layer_forward(cfg):
     # bf16 output is the RNE of the fp32 output of the same kernels
     got16 = run_layer(cfg, inp, out_dtype=B.MOE_BF16, with_aux=False)
     np.testing.assert_array_equal(got16["out"], rne_bf16_bits(got["out"]))
+
+
+@pytest.mark.parametrize("T,E,k", [(8, 896, 16), (40, 300, 8), (100, 256, 8), (24, 1024, 16)])
+def test_layer_decode_routing_ties(T, E, k):
+    """The one-launch decode routing on wide expert sets (threshold ranking, and the
+    rounds for tokens with heavy ties) with integer router logits: ids, counts,
+    offsets and the row metadata bit-exact against the oracle."""
+    cfg = PARITY_CONFIGS["decode_t100"].with_(T=T, E=E, k=k, H=128, I=64, zipf_s=None)
+    s = shape_of(cfg)
+    assert B.layer_plan(s, gate=False)["decode_path"] == 1
+    inp = gen.layer_inputs(cfg)
+    r = np.random.default_rng(T * E + k)
+    lg = r.integers(-40, 41, size=(T, E)).astype(np.float32)
+    lg[1, :] = 2.0                                # all tied: ranked in rounds
+    lg[2, : E // 2] = 5.0
+    lg[3, :] = -np.inf
+    lg[3, E - k:] = 0.0                           # exactly k finite
+    inp["logits"] = lg
+    inp.pop("bias", None)
+    got = run_layer(cfg, inp)
+    ref = oracle.route(oracle.router_scores(lg, None), k, E)
+    rt, tr = oracle.permutation(ref["ids"], E)
+    np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
+    assert np.max(np.abs(got["topk_w"] - ref["weights"])) <= 1e-6
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["row_token"][:len(rt)], rt)
+    np.testing.assert_array_equal(got["token_row"], tr)
 
 
 @pytest.mark.parametrize("name", ["small_bf16_zipf", "small_latent", "tiny_f32"])
