@@ -168,7 +168,8 @@ typedef struct moe_plan {
                                 * the token rows through row_token */
   int32_t gate_up_tile_m, gate_up_tile_n, gate_up_persistent;  /* expert gate/up GEMM */
   int32_t down_tile_m, down_tile_n, down_persistent;           /* expert down GEMM */
-  int32_t reserved;
+  int32_t route_workgroups;    /* decode path: workgroups of the routing launch (1, or
+                                * ceil(T / 4) when one workgroup would take longer); else 0 */
   const char* gate_up_kernel;  /* static: kernel name up to its tile arguments, as a trace shows it */
   const char* down_kernel;     /* static, likewise */
 } moe_plan;
@@ -349,13 +350,16 @@ typedef struct moe_layer_aux {
  * Decode-scale steps (fewer than 48 rows per expert on average, T <= 128) take a
  * low-latency path of three launches ("Three Parameter Counts...", "Halving top-k is a
  * network change first": at decode-scale token counts the layer is bound by launch
- * latency): routing, counts, offsets and row metadata in one workgroup; the gate/up GEMM
+ * latency): routing, counts, offsets and row metadata in one launch; the gate/up GEMM
  * reading the token rows through row_token; the down GEMM with the combine, each
  * workgroup owning 16 output columns of every row.  The output bits are those of the
  * separate calls.  Latent projections, MXFP8 conversion of the token rows, a requested
- * permuted copy and a shared expert add their own launches.  A step whose ranking is
- * too much work for one workgroup (ceil(T / 16) * k * ceil(E / 64) above 640, e.g. 896
- * experts, top-16, T = 128) routes with the general kernels instead: two launches more.
+ * permuted copy and a shared expert add their own launches.  The routing launch is one
+ * workgroup while ceil(T / 16) * k * ceil(E / 64) <= 640, else ceil(T / 4) workgroups
+ * (e.g. 896 experts, top-16, T = 128) of which the last to finish writes the metadata,
+ * handing over through 8 bytes of the workspace (moe_plan.route_workgroups says which).
+ * Such calls read and clear that word; calls that overlap on one workspace race on it,
+ * as on the rest of the workspace.
  *
  * Latent layers (s->L > 0) follow "Latent MoE" (Definition; Current Synthesis):
  * the router scores the full-width X, the rows dispatched are Z = X wd^T, and the

@@ -60,7 +60,8 @@ class MoePlan(ctypes.Structure):
     _fields_ = [("launches", _i32), ("decode_path", _i32), ("rows_gathered", _i32),
                 ("gate_up_tile_m", _i32), ("gate_up_tile_n", _i32), ("gate_up_persistent", _i32),
                 ("down_tile_m", _i32), ("down_tile_n", _i32), ("down_persistent", _i32),
-                ("reserved", _i32), ("gate_up_kernel", ctypes.c_char_p), ("down_kernel", ctypes.c_char_p)]
+                ("route_workgroups", _i32), ("gate_up_kernel", ctypes.c_char_p),
+                ("down_kernel", ctypes.c_char_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -123,7 +124,7 @@ def layer_plan(s: MoeShape, gate: bool, x_perm: bool = False) -> dict:
     p = MoePlan()
     flags = (MOE_PLAN_GATE if gate else 0) | (MOE_PLAN_X_PERM if x_perm else 0)
     _check("moe_layer_plan", lib.moe_layer_plan(ctypes.byref(s), flags, ctypes.byref(p)))
-    d = {f: getattr(p, f) for f, _ in MoePlan._fields_ if f != "reserved"}
+    d = {f: getattr(p, f) for f, _ in MoePlan._fields_}
     for f in ("gate_up_kernel", "down_kernel"):
         d[f] = d[f].decode()
     return d

@@ -1,6 +1,7 @@
 // Host side of the libmoe C ABI: argument validation, workspace carve-up,
 // kernel selection by shape, and the launch sequence of each call.  No call
 // allocates, synchronises or reads device memory.
+#include <atomic>
 #include <climits>
 #include <cstddef>
 #include <cstdint>
@@ -104,8 +105,8 @@ CombWs comb_ws(const Dims& d) {
 }
 
 struct LayerWs {
-  size_t logits, ids, w, counts, offsets, row_token, token_row, bc, gpart, mtile, z, xperm, act, outl,
-      soffs, smtile, sact, sy, xs, xq, xqs, total;
+  size_t logits, ids, w, counts, offsets, row_token, token_row, bc, handover, gpart, mtile, z, xperm, act,
+      outl, soffs, smtile, sact, sy, xs, xq, xqs, total;
 };
 LayerWs layer_ws(const Dims& d) {
   Carve c; LayerWs w;
@@ -117,6 +118,8 @@ LayerWs layer_ws(const Dims& d) {
   w.row_token = c.take((size_t)d.R * 4);
   w.token_row = c.take((size_t)d.R * 4);
   w.bc = c.take((size_t)d.nb * d.E * 4);
+  // decode-scale routing over several workgroups: their hand-over word
+  w.handover = c.take(d.T <= kSmallT ? 8 : 0);
   w.gpart = c.take(gate_partial_bytes(d));
   w.mtile = c.take(mtile_table_bytes(d.E));  // tables for two tile heights + claim counters
   w.z = c.take(d.L ? (size_t)d.T * d.L * d.es : 0);
@@ -233,6 +236,13 @@ moe_status dense_proj(const Dims& d, const void* A, const void* W, void* C, int 
   return MOE_OK;
 }
 
+// Tags of the decode-scale router's hand-over word: distinct for every call in the
+// process, never 0 (the router clears the word to 0 after use), below 2^56.
+std::atomic<unsigned long long> g_route_tag{1};
+unsigned long long next_route_tag() {
+  return (g_route_tag.fetch_add(1, std::memory_order_relaxed) - 1) % ((1ull << 56) - 1) + 1;
+}
+
 // Every decision moe_layer_forward takes from the shape and from which optional buffers
 // the caller passes; moe_layer_plan reports the same struct.
 struct LayerPlan {
@@ -253,13 +263,10 @@ LayerPlan plan_layer(const Dims& d, bool gate_computed, bool want_xperm, bool wa
   // caller asks for it in aux.x_perm).  With MXFP8 dispatch the token rows are
   // quantised once and read the same way; a caller who asks for the permuted codes
   // gets the general path.
-  // The one-workgroup router ranks ceil(T / 16) tokens per wave, one after another, so its
-  // time grows with ceil(T / 16) * k * ceil(E / 64) (measured on the 896-expert top-16 step:
-  // 13.6 us at T = 8, 112 us at T = 128, against about 27 us for the three launches of the
-  // general routing at T = 128); it is taken while that product stays within about 35 us.
-  const int rank_work = ceil_div(d.T, kBlockTok) * d.k * ceil_div(d.E, kWave);
-  p.small = p.kind == GEMM_DECODE && d.T <= kSmallT && rank_work <= kSmallRankWork &&
-            !(d.mx && (want_xperm || want_xperm_scale));
+  // The routing runs in one workgroup while its ranking work is small, each wave ranking
+  // ceil(T / 16) tokens one after another (route_one_workgroup); above that, over
+  // ceil(T / 4) workgroups, one token per wave, the last to finish writing the metadata.
+  p.small = p.kind == GEMM_DECODE && d.T <= kSmallT && !(d.mx && (want_xperm || want_xperm_scale));
   // Larger steps: unless the caller asks for the permuted rows, the permutation writes
   // only the row metadata and the gate/up GEMM reads the token rows through row_token
   // (decode-sized tiles always can; the persistent prefill kernel when its tile table
@@ -346,6 +353,7 @@ moe_status moe_layer_plan(const moe_shape* s, int flags, moe_plan* out) {
   out->down_tile_m = p.down.bm;
   out->down_tile_n = p.down.bn;
   out->down_persistent = p.down.persistent;
+  out->route_workgroups = !p.small ? 0 : route_one_workgroup(d.T, d.E, d.k) ? 1 : ceil_div(d.T, kMultiTok);
   out->gate_up_kernel = p.gate_up.kernel;
   out->down_kernel = p.down.kernel;
   return MOE_OK;
@@ -539,8 +547,9 @@ moe_status moe_layer_forward(const moe_layer_weights* wt, const void* x, float* 
   uint8_t* xq = d.mx ? at<uint8_t>(ws, w.xq) : nullptr;
   uint8_t* xqs = d.mx ? at<uint8_t>(ws, w.xqs) : nullptr;
   if (small) {
-    MOE_HIP(launch_route_small(scores, d.T, d.E, d.k, ids, tw, counts,
-                               offs, rtok, trow, d.cap, gemm_bm(kind), mtile, st));
+    MOE_HIP(launch_route_small(scores, d.T, d.E, d.k, ids, tw, counts, offs, rtok, trow, d.cap,
+                               gemm_bm(kind), mtile, at<unsigned long long>(ws, w.handover),
+                               next_route_tag(), st));
     if (!ev(3)) return MOE_ERR_HIP;
     if (d.mx) {
       MOE_HIP(launch_mx_quantize(src, true, d.T, d.D, xq, xqs, st));

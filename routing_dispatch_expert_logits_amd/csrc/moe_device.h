@@ -16,9 +16,11 @@ constexpr int kMaxE = 1024;
 // Largest token count routed by the one-workgroup decode-scale kernel (one bit per
 // token in two 64-bit masks per expert).
 constexpr int kSmallT = 128;
-// Largest ceil(T / 16) * k * ceil(E / 64) (rounds x score slots per wave) for which the
-// one-workgroup router beats the three launches of the general routing.
+// Largest ceil(T / 16) * k * ceil(E / 64) (ranking work per wave) for which the
+// decode-scale routing runs in one workgroup; above it, over ceil(T / kMultiTok)
+// workgroups that rank kMultiTok tokens each.
 constexpr int kSmallRankWork = 640;
+constexpr int kMultiTok = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -115,6 +117,10 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__host__ __device__ __forceinline__ bool route_one_workgroup(int T, int E, int k) {
+  return ceil_div(T, kBlockTok) * k * ceil_div(E, kWave) <= kSmallRankWork;
+}
 
 // ---- MXFP8 (OCP MX: E4M3 elements, one E8M0 scale per 32 elements along K)
 

@@ -127,11 +127,14 @@ hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, co
                                   const float* w, const void* add, int T, int k, void* out,
                                   bool out_f32, hipStream_t st);
 // Decode-scale routing (T <= kSmallT) in one launch: ids, weights, counts, offsets, the m-tile
-// tables (bm > 0) and row_token / token_row, as the large-T kernels produce them.
+// tables (bm > 0) and row_token / token_row, as the large-T kernels produce them.  In one
+// workgroup where route_one_workgroup(T, E, k), else over ceil(T / kMultiTok) workgroups that
+// hand over through one 64-bit word of workspace (handover) with tag, a value in
+// [1, 2^56) that no earlier call used.
 hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
                              int32_t* token_row, int cap, int bm, int32_t* mtile_start,
-                             hipStream_t st);
+                             unsigned long long* handover, unsigned long long tag, hipStream_t st);
 // Decode GEMM whose A rows are read through an index: row r of the operand is X[gather[r]]
 // (the expert gate/up GEMM reading the token rows directly instead of a permuted copy).
 // Whether the persistent prefill gate/up GEMM can read its rows through a gather

@@ -49,8 +49,9 @@ extern "C" moe_status moe_layer_forward_noalloc(const moe_layer_weights* w, cons
   rc = scratch_of_current_device(&ws);
   if (rc != MOE_OK) return rc;
   // No part of the layer workspace has to start at zero (the tile-claim counters are
-  // cleared by the kernel that writes the tile tables, inside the same call), so the
-  // previous call's contents need no clearing.
+  // cleared by the kernel that writes the tile tables, inside the same call, and the
+  // decode-scale router's hand-over word counts only when it holds the call's own tag),
+  // so the previous call's contents need no clearing.
   return moe_layer_forward(w, x, logits, out, out_dtype, s, aux, stage_events, ws, MOE_NOALLOC_SCRATCH_BYTES,
                            stream);
 }

@@ -338,52 +338,55 @@ __global__ __launch_bounds__(1024) void k_offsets(const int32_t* __restrict__ co
   }
 }
 
-// Routing of a decode-scale step (T <= 64 MW, MW = 1 or 2) in one workgroup: top-k per token
-// (one wave per token, tokens t = wave + 16 i), counts, offsets, the GEMM m-tile
-// tables and the row metadata, so a small step pays one launch for what the
-// large-T path does in four.  Row order inside an expert's segment is ascending
-// token id, as there: row = offsets[e] + (number of lower tokens in mask[e]), mask[e]
-// the tokens that picked e (MW 64-bit words, built with order-independent LDS
-// atomicOr).  With an expert capacity cap > 0, assignments ranked cap or later in
-// their expert are dropped (token_row = -1) and counts are min(count, cap).
-template <int SLOTS, int MW>
-__global__ __launch_bounds__(1024) void k_route_small(
-    ScoreSrc src, int T, int E, int k,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
-    int cap, int bm, int32_t* __restrict__ mtile_start) {
-  __shared__ int cnt[kMaxE];
-  __shared__ int off_s[kMaxE];
-  __shared__ unsigned long long mask[kMaxE * MW];
-  __shared__ int s_ids[64 * MW * kWave];
-  __shared__ int smem[48];
-  __shared__ uint32_t rk_key[16][kWave];
-  __shared__ int rk_idx[16][kWave];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += 1024) {
-    cnt[e] = 0;
+// Decode-scale routing (T <= 64 MW, MW = 1 or 2): top-k per token (one wave per
+// token), counts, offsets, the GEMM m-tile tables and the row metadata in one
+// launch, for what the large-T path does in three.  Row order inside an expert's
+// segment is ascending token id, as there: row = offsets[e] + (number of lower
+// tokens in mask[e]), mask[e] the tokens that picked e (MW 64-bit words, built with
+// order-independent LDS atomicOr).  With an expert capacity cap > 0, assignments
+// ranked cap or later in their expert are dropped (token_row = -1) and counts are
+// min(count, cap).
+template <int MW>
+struct RouteLds {
+  int cnt[kMaxE];
+  int off_s[kMaxE];
+  unsigned long long mask[kMaxE * MW];
+  int ids[64 * MW * kWave];  // [t][j], t < T, j < k
+  int smem[48];
+  uint32_t rk_key[16][kWave];
+  int rk_idx[16][kWave];
+};
+
+template <int MW>
+__device__ __forceinline__ void route_clear(RouteLds<MW>& L, int E) {
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    L.cnt[e] = 0;
 #pragma unroll
-    for (int w = 0; w < MW; ++w) mask[e * MW + w] = 0ull;
+    for (int w = 0; w < MW; ++w) L.mask[e * MW + w] = 0ull;
   }
-  __syncthreads();
-  for (int t = wave; t < T; t += 16) {
-    int my_e;
-    float my_w;
-    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, rk_key[wave], rk_idx[wave], my_e, my_w);
-    if (lane < k) {
-      topk_ids[(size_t)t * k + lane] = my_e;
-      topk_w[(size_t)t * k + lane] = my_w;
-      s_ids[t * k + lane] = my_e;
-      atomicAdd(&cnt[my_e], 1);
-      atomicOr(&mask[my_e * MW + (t >> 6)], 1ull << (t & 63));
-    }
-  }
-  __syncthreads();
-  const int c = tid < E ? (cap > 0 ? min(cnt[tid], cap) : cnt[tid]) : 0;
+}
+
+// One assignment of token t: its count and its bit in the expert's token mask.
+template <int MW>
+__device__ __forceinline__ void route_note(RouteLds<MW>& L, int t, int j, int k, int e) {
+  L.ids[t * k + j] = e;
+  atomicAdd(&L.cnt[e], 1);
+  atomicOr(&L.mask[e * MW + (t >> 6)], 1ull << (t & 63));
+}
+
+// Counts, offsets, m-tile tables and row metadata from the noted assignments
+// (all T * k of them in L, after a barrier).
+template <int MW>
+__device__ __forceinline__ void route_metadata(RouteLds<MW>& L, int T, int E, int k,
+                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+                                               int cap, int bm, int32_t* __restrict__ mtile_start) {
+  const int tid = threadIdx.x;
+  const int c = tid < E ? (cap > 0 ? min(L.cnt[tid], cap) : L.cnt[tid]) : 0;
   int total = 0;
-  const int off = block_exclusive_scan(c, &total, smem);
+  const int off = block_exclusive_scan(c, &total, L.smem);
   if (tid < E) {
-    off_s[tid] = off;
+    L.off_s[tid] = off;
     counts[tid] = c;
     offsets[tid] = off;
     if (tid == E - 1) offsets[E] = off + c;
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(1024) void k_route_small(
     for (int h = 0; h < 2; ++h) {
       const int mt = tid < E ? ceil_div(c, bm << h) : 0;
       int tot = 0;
-      const int st = block_exclusive_scan(mt, &tot, smem);
+      const int st = block_exclusive_scan(mt, &tot, L.smem);
       int32_t* tab = mtile_start + h * (E + 1);
       if (tid < E) tab[tid] = st;
       if (tid == E - 1) tab[E] = st + mt;
@@ -402,18 +405,108 @@ __global__ __launch_bounds__(1024) void k_route_small(
   }
   __syncthreads();
   for (int a = tid; a < T * k; a += 1024) {
-    const int t = a / k, e = s_ids[a];
-    int rank = __popcll(mask[e * MW + (t >> 6)] & ((1ull << (t & 63)) - 1ull));
+    const int t = a / k, e = L.ids[a];
+    int rank = __popcll(L.mask[e * MW + (t >> 6)] & ((1ull << (t & 63)) - 1ull));
 #pragma unroll
     for (int w = 0; w + 1 < MW; ++w)
-      if (w < (t >> 6)) rank += __popcll(mask[e * MW + w]);
+      if (w < (t >> 6)) rank += __popcll(L.mask[e * MW + w]);
     if (cap > 0 && rank >= cap) {
       token_row[a] = -1;  // dropped: past the expert's capacity
     } else {
-      token_row[a] = off_s[e] + rank;
-      row_token[off_s[e] + rank] = t;
+      token_row[a] = L.off_s[e] + rank;
+      row_token[L.off_s[e] + rank] = t;
     }
   }
+}
+
+// In one workgroup: every wave ranks tokens wave, wave + 16, ... one after another.
+template <int SLOTS, int MW>
+__global__ __launch_bounds__(1024) void k_route_small(
+    ScoreSrc src, int T, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+    int cap, int bm, int32_t* __restrict__ mtile_start) {
+  __shared__ RouteLds<MW> L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  route_clear(L, E);
+  __syncthreads();
+  for (int t = wave; t < T; t += 16) {
+    int my_e;
+    float my_w;
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, L.rk_key[wave], L.rk_idx[wave], my_e, my_w);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = my_w;
+      route_note(L, t, lane, k, my_e);
+    }
+  }
+  __syncthreads();
+  route_metadata(L, T, E, k, counts, offsets, row_token, token_row, cap, bm, mtile_start);
+}
+
+// Over ceil(T / 4) workgroups, one token per wave in the first 4 waves (one ranking
+// wave per SIMD: 16 ranking waves on one CU's four SIMDs took twice as long), for
+// steps whose ranking is too much work for one CU; all 16 waves of the workgroup that
+// writes the metadata take part in it.  No workgroup waits for another.  Each writes its tokens'
+// ids and weights and then counts itself in a hand-over word (release): the word
+// holds this call's tag (a value no earlier call used) above an 8-bit count, and a
+// word with any other tag, whatever an earlier call or the workspace left there,
+// counts as zero.  The atomic that brings the count to the number of workgroups is
+// exactly one, and its workgroup (acquire) sees every id: it writes the counts,
+// offsets, tile tables and row metadata and clears the word (a replayed graph repeats
+// its tag).  Installing the tag is a compare-and-swap, which fails only when another
+// workgroup's succeeded in between; after that every count is a plain atomic add.
+template <int SLOTS, int MW>
+__global__ __launch_bounds__(1024) void k_route_multi(
+    ScoreSrc src, int T, int E, int k,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+    int cap, int bm, int32_t* __restrict__ mtile_start, unsigned long long* __restrict__ handover,
+    unsigned long long tag) {
+  __shared__ RouteLds<MW> L;
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kMultiTok + wave;
+  if (wave < kMultiTok && t < T) {
+    int my_e;
+    float my_w;
+    rank_token<SLOTS>(src, (size_t)t * E, E, k, lane, L.rk_key[wave], L.rk_idx[wave], my_e, my_w);
+    if (lane < k) {
+      topk_ids[(size_t)t * k + lane] = my_e;
+      topk_w[(size_t)t * k + lane] = my_w;
+    }
+    // the waves that wrote release their writes (each release writes back the L2)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // Count this workgroup: the first to arrive swaps the tag in (a stale word, from
+    // any other call, counts as zero), the others add 1 (no retries among them; the
+    // word keeps the tag until the metadata writer clears it, after every count).
+    unsigned long long old = __hip_atomic_load(handover, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long cnt;
+    for (;;) {
+      if ((old >> 8) == tag) {
+        cnt = (__hip_atomic_fetch_add(handover, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) & 0xffu) + 1;
+        break;
+      }
+      if (__hip_atomic_compare_exchange_strong(handover, &old, (tag << 8) | 1ull, __ATOMIC_ACQ_REL,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        cnt = 1;
+        break;
+      }
+    }
+    s_last = (int)cnt == (int)gridDim.x;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (threadIdx.x == 0) __hip_atomic_store(handover, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  route_clear(L, E);
+  __syncthreads();
+  for (int a = threadIdx.x; a < T * k; a += 1024) route_note(L, a / k, a % k, k, topk_ids[a]);
+  __syncthreads();
+  route_metadata(L, T, E, k, counts, offsets, row_token, token_row, cap, bm, mtile_start);
 }
 
 // One group of T rows (the shared expert's GEMMs run as a single expert).
@@ -468,19 +561,27 @@ hipError_t launch_offsets(const int32_t* counts, const int32_t* offsets_in, int 
 hipError_t launch_route_small(const ScoreSrc& src, int T, int E, int k, int32_t* ids,
                              float* w, int32_t* counts, int32_t* offsets, int32_t* row_token,
                              int32_t* token_row, int cap, int bm, int32_t* mtile_start,
-                             hipStream_t st) {
-  if (T > kSmallT) return hipErrorInvalidValue;
+                             unsigned long long* handover, unsigned long long tag, hipStream_t st) {
+  // the tag sits above an 8-bit count of at most ceil(128 / 4) workgroups
+  if (T > kSmallT || tag == 0 || (tag >> 56) != 0) return hipErrorInvalidValue;
   const int slots = ceil_div(E, kWave);
-  dim3 g(1), b(1024);
-#define MOE_RS(SL, MW)                                                                             \
-  hipLaunchKernelGGL((k_route_small<SL, MW>), g, b, 0, st, src, T, E, k, ids, w, counts, offsets, \
-                     row_token, token_row, cap, bm, mtile_start)
+  const bool one = route_one_workgroup(T, E, k);
+  if (!one && !handover) return hipErrorInvalidValue;
+  const dim3 b(1024);
+#define MOE_RS(SL, MW)                                                                              \
+  if (one)                                                                                          \
+    hipLaunchKernelGGL((k_route_small<SL, MW>), dim3(1), b, 0, st, src, T, E, k, ids, w, counts,    \
+                       offsets, row_token, token_row, cap, bm, mtile_start);                        \
+  else                                                                                              \
+    hipLaunchKernelGGL((k_route_multi<SL, MW>), dim3(ceil_div(T, kMultiTok)), b, 0, st, src, T, E, \
+                       k, ids, w, counts, offsets, row_token, token_row, cap, bm, mtile_start,      \
+                       handover, tag)
 #define MOE_RS_SLOTS(MW)          \
-  if (slots <= 1) MOE_RS(1, MW);  \
-  else if (slots <= 2) MOE_RS(2, MW); \
-  else if (slots <= 4) MOE_RS(4, MW); \
-  else if (slots <= 8) MOE_RS(8, MW); \
-  else MOE_RS(16, MW);
+  if (slots <= 1) { MOE_RS(1, MW); } \
+  else if (slots <= 2) { MOE_RS(2, MW); } \
+  else if (slots <= 4) { MOE_RS(4, MW); } \
+  else if (slots <= 8) { MOE_RS(8, MW); } \
+  else { MOE_RS(16, MW); }
   if (T <= 64) {
     MOE_RS_SLOTS(1)
   } else {

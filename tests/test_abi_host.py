@@ -173,7 +173,7 @@ def test_layer_plan_names_the_kernels_of_each_layer():
         "deepseek_r1_shaped": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<128, 256, 1,", 7),
         "latent_moe": (0, 1, "k_gemm_wsp<128, 128, 2,", "k_gemm_wsp<256, 128, 1,", 9),
         "k3_shaped_decode_t8": (1, 1, "k_gemm_decode<2, 2,", "k_down_combine<16,", 3),
-        "k3_shaped_decode": (0, 1, "k_gemm_decode<2, 2,", "k_down_combine<16,", 5),
+        "k3_shaped_decode": (1, 1, "k_gemm_decode<2, 2,", "k_down_combine<16,", 3),
         "tiny_f32": (0, 0, "k_gemm_simt<float, 2,", "k_gemm_simt<float, 1,", 6),
     }
     for name, (dec, gath, gu, dn, n) in want.items():
@@ -190,16 +190,18 @@ def test_layer_plan_names_the_kernels_of_each_layer():
     with pytest.raises(B.MoeError):
         B.layer_plan(B.shape(0, 128, 8, 2, 256), True)
     assert B.lib.moe_layer_plan(ctypes.byref(s), 8, None) == B.MOE_ERR_INVALID_ARG
-    # decode-scale steps route in one launch while ceil(T / 16) * k * ceil(E / 64) <= 640
-    # and T <= 128: 3 launches, 4 when the Y columns do not fit the fused down GEMM +
-    # combine's LDS; past either bound the general routing kernels add two
-    for T, E, k, one in ((1, 8, 2, True), (64, 1024, 8, True), (8, 896, 16, True),
-                         (128, 200, 8, True), (120, 700, 12, False), (65, 896, 16, False),
-                         (129, 64, 2, False)):
+    # decode-scale steps (T <= 128) route in one launch: one workgroup while
+    # ceil(T / 16) * k * ceil(E / 64) <= 640, else ceil(T / 4) of them; 3 launches, 4 when
+    # the Y columns do not fit the fused down GEMM + combine's LDS.  Past T = 128 the
+    # general routing kernels add two
+    for T, E, k, wgs in ((1, 8, 2, 1), (64, 1024, 8, 1), (8, 896, 16, 1), (128, 200, 8, 1),
+                         (120, 700, 12, 30), (65, 896, 16, 17), (128, 896, 16, 32), (129, 64, 2, 0)):
         p = B.layer_plan(B.shape(T, 256, E, k, 128), False)
         fused = p["down_kernel"] == "k_down_combine<16,"
-        assert p["decode_path"] == int(one), (T, E, k)
-        assert p["launches"] == (3 if fused else 4) + (0 if one else 2), (T, E, k)
+        assert p["decode_path"] == int(wgs > 0), (T, E, k)
+        assert p["route_workgroups"] == wgs, (T, E, k)
+        assert p["launches"] == (3 if fused else 4) + (0 if wgs else 2), (T, E, k)
+    assert B.layer_plan(B.shape(4096, 256, 8, 2, 128), False)["route_workgroups"] == 0
 
 
 def test_persistent_tile_table_fields_bound_the_expert_rows():

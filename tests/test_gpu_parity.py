@@ -404,14 +404,19 @@ def test_layer_forward(cfg):
     np.testing.assert_array_equal(got16["out"], rne_bf16_bits(got["out"]))
 
 
-@pytest.mark.parametrize("T,E,k", [(8, 896, 16), (40, 300, 8), (100, 256, 8), (24, 1024, 16)])
-def test_layer_decode_routing_ties(T, E, k):
-    """The one-launch decode routing on wide expert sets (threshold ranking, and the
-    rounds for tokens with heavy ties) with integer router logits: ids, counts,
-    offsets and the row metadata bit-exact against the oracle."""
+@pytest.mark.parametrize("T,E,k,wgs", [(8, 896, 16, 1), (40, 300, 8, 1), (100, 256, 8, 1), (24, 1024, 16, 1),
+                                       (128, 896, 16, 32), (60, 1024, 16, 15), (100, 512, 32, 25),
+                                       (17, 1000, 64, 5)])
+def test_layer_decode_routing_ties(T, E, k, wgs):
+    """The one-launch decode routing on wide expert sets, in one workgroup and over
+    ceil(T / 4) workgroups (threshold ranking, and the rounds for tokens with heavy
+    ties) with integer router logits: ids, counts, offsets and the row metadata
+    bit-exact against the oracle, on two calls in a row (the second one finds the
+    hand-over word the first one cleared)."""
     cfg = PARITY_CONFIGS["decode_t100"].with_(T=T, E=E, k=k, H=128, I=64, zipf_s=None)
     s = shape_of(cfg)
-    assert B.layer_plan(s, gate=False)["decode_path"] == 1
+    p = B.layer_plan(s, gate=False)
+    assert (p["decode_path"], p["route_workgroups"]) == (1, wgs)
     inp = gen.layer_inputs(cfg)
     r = np.random.default_rng(T * E + k)
     lg = r.integers(-40, 41, size=(T, E)).astype(np.float32)
@@ -421,15 +426,16 @@ def test_layer_decode_routing_ties(T, E, k):
     lg[3, E - k:] = 0.0                           # exactly k finite
     inp["logits"] = lg
     inp.pop("bias", None)
-    got = run_layer(cfg, inp)
     ref = oracle.route(oracle.router_scores(lg, None), k, E)
     rt, tr = oracle.permutation(ref["ids"], E)
-    np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
-    assert np.max(np.abs(got["topk_w"] - ref["weights"])) <= 1e-6
-    np.testing.assert_array_equal(got["counts"], ref["counts"])
-    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
-    np.testing.assert_array_equal(got["row_token"][:len(rt)], rt)
-    np.testing.assert_array_equal(got["token_row"], tr)
+    for _ in range(2):
+        got = run_layer(cfg, inp)
+        np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
+        assert np.max(np.abs(got["topk_w"] - ref["weights"])) <= 1e-6
+        np.testing.assert_array_equal(got["counts"], ref["counts"])
+        np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+        np.testing.assert_array_equal(got["row_token"][:len(rt)], rt)
+        np.testing.assert_array_equal(got["token_row"], tr)
 
 
 @pytest.mark.parametrize("name", ["small_bf16_zipf", "small_latent", "tiny_f32"])
@@ -562,7 +568,7 @@ def test_layer_output_equals_separate_calls(name):
     """Fused layer == route, permute, grouped FFN, (the shared expert as a
     one-expert grouped FFN over all tokens,) and the combine, bit for bit: the
     fusion is execution-only.  Decode-scale layers (T <= 128 with 16-row tiles)
-    take the one-launch routing (the general routing kernels for decode_many_experts*),
+    take the one-launch routing (over several workgroups for decode_many_experts*),
     the gathering gate/up GEMM and the down GEMM fused with the combine in the fused
     call (its Y, written to aux.y_perm, has the bits of the separate down GEMM), the
     general kernels in the separate calls."""

@@ -52,6 +52,7 @@ def test_noalloc_equals_layer_forward_on_calls_in_a_row():
     big = PARITY_CONFIGS["small_bf16_zipf"]          # persistent gate/up GEMM, gathered rows
     calls = [big, big.with_(T=120),                   # the second call on a smaller input
              PARITY_CONFIGS["small_bf16_decode"],     # decode-scale step (one-launch routing)
+             PARITY_CONFIGS["decode_many_experts"],   # the same over 30 workgroups (hand-over word)
              PARITY_CONFIGS["shared_expert"].with_(T=77)]
     assert B.workspace_bytes(shape_of(big), B.MOE_CALL_LAYER) <= B.NOALLOC_SCRATCH_BYTES
     for cfg in calls:
