@@ -90,8 +90,9 @@ __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
 // row: measured on 8192 x 7168 and 4096 x 2048 combines (8 of 256 / 128 experts,
 // rows in expert order), reading each row in one piece rather than in 2 KB pieces
 // took 4096 x 2048 from 37 to 29.6 us and 8192 x 7168 from 195 to 190 us, with the
-// same bits.
-template <typename IT, int U, int CH>
+// same bits.  TOK: the rows are the unpermuted ones, token t's j-th at t * k + j (the
+// second step of the unfused pair), still skipped where token_row[t, j] = -1.
+template <typename IT, int U, int CH, bool TOK>
 __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, int row16,
                                                  const int32_t* __restrict__ token_row,
                                                  const float* __restrict__ topk_w,
@@ -107,6 +108,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ y, in
   float my_w = 0.f;
   if (lane < k) {
     my_row = token_row[(size_t)t * k + lane];
+    if (TOK && my_row >= 0) my_row = t * k + lane;
     my_w = topk_w[(size_t)t * k + lane];
   }
   // The trip counts are wave-uniform so every lane takes part in the shuffles of
@@ -176,38 +178,10 @@ __global__ __launch_bounds__(256) void k_unpermute(const uint4* __restrict__ y, 
   for (int c = lane; c < row16; c += kWave) store_stream(dst + c, load_stream(src + c));
 }
 
-// Unfused step 2: out[t] = sum_j w[t, j] * y_tok[t*k + j], same fma order as k_combine.
-template <typename IT>
-__global__ __launch_bounds__(256) void k_weighted_reduce(const uint4* __restrict__ y_tok, int row16,
-                                                         const int32_t* __restrict__ token_row,
-                                                         const float* __restrict__ topk_w,
-                                                         const uint4* __restrict__ add, int T,
-                                                         int k, void* __restrict__ out,
-                                                         int out_f32) {
-  constexpr int NV = Vec16<IT>::n;
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * kCombTokPerWg + (threadIdx.x >> 6);
-  if (t >= T) return;
-  for (int c = lane; c < row16; c += kWave) {
-    float acc[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      if (token_row[(size_t)t * k + j] < 0) continue;  // dropped
-      const float wj = topk_w[(size_t)t * k + j];
-      float f[NV];
-      Vec16<IT>::unpack(load_stream(y_tok + ((size_t)t * k + j) * row16 + c), f);
-#pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i] = fmaf(wj, f[i], acc[i]);
-    }
-    if (add) add_row<IT>(acc, add[(size_t)t * row16 + c]);
-    store_out<NV>(out, ((size_t)t * row16 + c) * NV, acc, out_f32 != 0);
-  }
-}
-
-hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
-                          const float* w, const void* add, int T, int k, void* out, bool out_f32,
-                          hipStream_t st) {
+// tok: the rows are y_tok[t * k + j] (unfused step 2), else y[token_row[t, j]]
+static hipError_t launch_combine_rows(const void* y, int row16, bool in_bf16, const int32_t* token_row,
+                                     const float* w, const void* add, int T, int k, void* out,
+                                     bool out_f32, bool tok, hipStream_t st) {
   // split columns until ~1024 workgroups (small token counts)
   const int gx = ceil_div(T, kCombTokPerWg);
   int cs = 1;
@@ -218,14 +192,20 @@ hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t*
   const int width = ceil_div(row16, cs);
   int ch = 1;
   while (ch < 8 && ch * kWave < width) ch *= 2;
-#define MOE_COMB(IT, U, CH)                                                                  \
-  hipLaunchKernelGGL((k_combine<IT, U, CH>), g, b, 0, st, static_cast<const uint4*>(y), row16, \
-                     token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32)
-#define MOE_COMB_CH(IT)                   \
-  if (ch == 1) MOE_COMB(IT, 8, 1);        \
-  else if (ch == 2) MOE_COMB(IT, 8, 2);   \
-  else if (ch == 4) MOE_COMB(IT, 4, 4);   \
-  else MOE_COMB(IT, 2, 8);
+#define MOE_COMB(IT, U, CH)                                                                     \
+  if (tok)                                                                                      \
+    hipLaunchKernelGGL((k_combine<IT, U, CH, true>), g, b, 0, st, static_cast<const uint4*>(y), \
+                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out,          \
+                       (int)out_f32);                                                           \
+  else                                                                                          \
+    hipLaunchKernelGGL((k_combine<IT, U, CH, false>), g, b, 0, st, static_cast<const uint4*>(y), \
+                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out,          \
+                       (int)out_f32)
+#define MOE_COMB_CH(IT)                       \
+  if (ch == 1) { MOE_COMB(IT, 8, 1); }        \
+  else if (ch == 2) { MOE_COMB(IT, 8, 2); }   \
+  else if (ch == 4) { MOE_COMB(IT, 4, 4); }   \
+  else { MOE_COMB(IT, 2, 8); }
   if (in_bf16) {
     MOE_COMB_CH(uint16_t)
   } else {
@@ -236,6 +216,12 @@ hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t*
   return hipGetLastError();
 }
 
+hipError_t launch_combine(const void* y, int row16, bool in_bf16, const int32_t* token_row,
+                          const float* w, const void* add, int T, int k, void* out, bool out_f32,
+                          hipStream_t st) {
+  return launch_combine_rows(y, row16, in_bf16, token_row, w, add, T, k, out, out_f32, false, st);
+}
+
 hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, int R,
                             const int32_t* limit, void* y_tok, hipStream_t st) {
   hipLaunchKernelGGL(k_unpermute, dim3(ceil_div(R, 4)), dim3(256), 0, st,
@@ -244,17 +230,12 @@ hipError_t launch_unpermute(const void* y, int row16, const int32_t* token_row, 
   return hipGetLastError();
 }
 
+// Unfused step 2: out[t] = sum_j w[t, j] * y_tok[t*k + j] (dropped terms skipped), the
+// fused kernel's fma order over the unpermuted rows, so the same bits.
 hipError_t launch_weighted_reduce(const void* y_tok, int row16, bool in_bf16, const int32_t* token_row,
                                   const float* w, const void* add, int T, int k, void* out,
                                   bool out_f32, hipStream_t st) {
-  const dim3 g(ceil_div(T, kCombTokPerWg)), b(256);
-  if (in_bf16)
-    hipLaunchKernelGGL(k_weighted_reduce<uint16_t>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
-  else
-    hipLaunchKernelGGL(k_weighted_reduce<float>, g, b, 0, st, static_cast<const uint4*>(y_tok),
-                       row16, token_row, w, static_cast<const uint4*>(add), T, k, out, (int)out_f32);
-  return hipGetLastError();
+  return launch_combine_rows(y_tok, row16, in_bf16, token_row, w, add, T, k, out, out_f32, true, st);
 }
 
 }  // namespace moe

@@ -325,8 +325,9 @@ def test_combine_rows_narrower_than_k(cfg):
 
 # ------------------------------------------------------------------ whole layer
 
-def run_layer(cfg, inp, out_dtype=B.MOE_F32, with_aux=True):
-    """moe_layer_forward on uploaded inputs; returns host copies of out and the aux buffers."""
+def run_layer(cfg, inp, out_dtype=B.MOE_F32, with_aux=True, workspace=None):
+    """moe_layer_forward on uploaded inputs (in `workspace` if given); returns host copies
+    of out and the aux buffers."""
     s = shape_of(cfg)
     T, E, k, R, D = cfg.T, cfg.E, cfg.k, cfg.R, cfg.D
     w = {n: dev(inp[n]) for n in ("gate_w", "w1", "w3", "w2", "wd", "wu", "ws1", "ws3", "ws2")
@@ -344,7 +345,8 @@ def run_layer(cfg, inp, out_dtype=B.MOE_F32, with_aux=True):
             aux["z"] = empty((T, cfg.L), act_kind(cfg))
             aux["out_latent"] = empty((T, cfg.L), act_kind(cfg))
     out = empty((T, cfg.H), "f32" if out_dtype == B.MOE_F32 else "bf16")
-    B.layer_forward(w, dev(inp["x"]), logits, out, out_dtype, s, ws(s, B.MOE_CALL_LAYER), aux)
+    wsp = ws(s, B.MOE_CALL_LAYER) if workspace is None else workspace
+    B.layer_forward(w, dev(inp["x"]), logits, out, out_dtype, s, wsp, aux)
     torch.cuda.synchronize()
     res = {"out": host(out, out_dtype == B.MOE_BF16), "logits": host(logits)}
     bf = cfg.dtype == "bf16"
@@ -411,8 +413,8 @@ def test_layer_decode_routing_ties(T, E, k, wgs):
     """The one-launch decode routing on wide expert sets, in one workgroup and over
     ceil(T / 4) workgroups (threshold ranking, and the rounds for tokens with heavy
     ties) with integer router logits: ids, counts, offsets and the row metadata
-    bit-exact against the oracle, on two calls in a row (the second one finds the
-    hand-over word the first one cleared)."""
+    bit-exact against the oracle, on two calls in a row, each in a workspace of
+    random bytes."""
     cfg = PARITY_CONFIGS["decode_t100"].with_(T=T, E=E, k=k, H=128, I=64, zipf_s=None)
     s = shape_of(cfg)
     p = B.layer_plan(s, gate=False)
@@ -428,8 +430,13 @@ def test_layer_decode_routing_ties(T, E, k, wgs):
     inp.pop("bias", None)
     ref = oracle.route(oracle.router_scores(lg, None), k, E)
     rt, tr = oracle.permutation(ref["ids"], E)
+    # the workspace starts as random bytes each time: whatever the hand-over word holds
+    # counts as zero unless it carries the call's own tag
+    wsp = ws(s, B.MOE_CALL_LAYER)
+    gen_t = torch.Generator(device="cuda:0").manual_seed(T * 7 + k)
     for _ in range(2):
-        got = run_layer(cfg, inp)
+        wsp.copy_(torch.randint(0, 256, wsp.shape, generator=gen_t, device="cuda:0", dtype=torch.uint8))
+        got = run_layer(cfg, inp, workspace=wsp)
         np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
         assert np.max(np.abs(got["topk_w"] - ref["weights"])) <= 1e-6
         np.testing.assert_array_equal(got["counts"], ref["counts"])
