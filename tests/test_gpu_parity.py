@@ -646,10 +646,13 @@ def test_layer_under_graph_capture(name):
         np.testing.assert_array_equal(host(out), want)
 
 
-def test_concurrent_layers_on_two_streams():
-    """Calls are re-entrant across distinct workspaces: two different layers launched
-    concurrently on two streams (default priority) give the bits of serial runs."""
-    cfgs = [PARITY_CONFIGS["small_bf16_zipf"], PARITY_CONFIGS["small_bf16_decode"].with_(dispatch="mxfp8")]
+def test_concurrent_layers_on_separate_streams():
+    """Calls are re-entrant across distinct workspaces: different layers launched
+    concurrently on separate streams (default priority) give the bits of serial runs,
+    the decode routing over several workgroups (its hand-over word in each call's own
+    workspace) among them."""
+    cfgs = [PARITY_CONFIGS["small_bf16_zipf"], PARITY_CONFIGS["small_bf16_decode"].with_(dispatch="mxfp8"),
+            PARITY_CONFIGS["decode_many_experts"]]
     setups = []
     for cfg in cfgs:
         inp = gen.layer_inputs(cfg)
@@ -675,10 +678,11 @@ def test_concurrent_layers_on_two_streams():
             B.layer_forward(w, x, logits, out, B.MOE_F32, s, wsp, stream=stream)
         return out
 
-    serial = [host(run(i, None, 1)) for i in range(2)]
+    assert B.layer_plan(setups[2][1], gate=False)["route_workgroups"] > 1
+    serial = [host(run(i, None, 1)) for i in range(len(cfgs))]
     torch.cuda.synchronize()
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
-    outs = [run(0, s1, 20), run(1, s2, 20)]
+    streams = [torch.cuda.Stream() for _ in cfgs]
+    outs = [run(i, streams[i], 20) for i in range(len(cfgs))]
     torch.cuda.synchronize()
-    for i in range(2):
+    for i in range(len(cfgs)):
         np.testing.assert_array_equal(host(outs[i]), serial[i])
