@@ -18,9 +18,11 @@
  * --------------------------------
  * - Every tensor pointer is a DEVICE pointer owned by the caller, dense and
  *   row-major, 16-byte aligned.  The library allocates nothing and keeps no
- *   state between calls; all scratch comes from the caller's workspace `ws`
- *   of `ws_bytes` bytes (size it with moe_workspace_bytes; NULL allowed when
- *   that size is 0).
+ *   state between calls beyond a process-wide counter that tags each
+ *   decode-scale routing call (moe_layer_forward) so it never mistakes another
+ *   call's hand-over word for its own; all scratch comes from the caller's
+ *   workspace `ws` of `ws_bytes` bytes (size it with moe_workspace_bytes; NULL
+ *   allowed when that size is 0), and nothing in it has to start at zero.
  * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *   stream).  They never read device memory on the host and never
  *   synchronise: static grids, GPU-resident counts and offsets (same page,
