@@ -445,6 +445,37 @@ def test_layer_decode_routing_ties(T, E, k, wgs):
         np.testing.assert_array_equal(got["token_row"], tr)
 
 
+@pytest.mark.parametrize("T,H,E,k,I,dtype", [(1000, 256, 16, 2, 192, "bf16"),   # persistent prefill tiles
+                                              (600, 256, 4, 1, 2048, "bf16"),    # long-K down tiles
+                                              (100, 256, 300, 4, 128, "bf16"),   # decode, one routing workgroup
+                                              (128, 256, 896, 16, 128, "bf16"),  # decode, 32 routing workgroups
+                                              (97, 96, 6, 3, 80, "f32")])
+def test_layer_all_tokens_on_the_same_experts(T, H, E, k, I, dtype):
+    """Every token picks the same k experts (the hottest possible skew): those experts
+    hold T rows each, every other expert is empty.  Routing and the row metadata are
+    bit-exact and every output element is within the derived bound."""
+    cfg = PARITY_CONFIGS["decode_t100"].with_(T=T, H=H, E=E, k=k, I=I, dtype=dtype, zipf_s=None,
+                                              seed=T + E + k)
+    inp = gen.layer_inputs(cfg)
+    r = np.random.default_rng(T * 3 + E)
+    lg = r.standard_normal((T, E)).astype(np.float32)
+    hot = r.choice(E, size=k, replace=False)
+    lg[:, hot] = (10.0 + np.arange(k, dtype=np.float32))[None, :]   # same order for every token
+    inp["logits"] = lg
+    inp.pop("bias", None)
+    got = run_layer(cfg, inp)
+    bf = dtype == "bf16"
+    ref = oracle.layer_forward(inp, k=k, E=E, bf16=bf, capacity=0)
+    np.testing.assert_array_equal(got["topk_ids"], ref["ids"])
+    assert set(np.unique(ref["ids"])) == set(hot.tolist())
+    np.testing.assert_array_equal(got["counts"], ref["counts"])
+    np.testing.assert_array_equal(got["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(got["row_token"][:len(ref["row_token"])], ref["row_token"])
+    np.testing.assert_array_equal(got["token_row"], ref["token_row"])
+    check_layer_out(cfg, inp, ref, got["out"], np.ones(T, dtype=bool))
+    assert out_err_over_rms(got["out"], ref["out"], None) <= (2e-2 if bf else 1e-5)
+
+
 @pytest.mark.parametrize("name", ["small_bf16_zipf", "small_latent", "tiny_f32"])
 def test_layer_matches_separate_calls_and_is_deterministic(name):
     """Fusion is execution-only: routing, permutation and output bits equal the separate calls."""
