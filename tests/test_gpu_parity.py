@@ -98,6 +98,24 @@ def test_route_ties_at_threshold(E, k):
     _check_route(cfg, lg, None)
 
 
+def test_p95_skew_from_gpu_counts():
+    """The p95 of the max / mean expert-load skew over reseeded routing steps (the
+    figure the bench reports, taken from the GPU's counts) equals the oracle's, on a
+    layer whose router logits carry a Zipf bias."""
+    cfg = PARITY_CONFIGS["decode_many_experts"].with_(T=512, capacity=0)
+    bias = gen.zipf_bias(cfg)
+    gpu, ref = [], []
+    for step in range(8):
+        lg = gen.drawn_logits(cfg, step)
+        _, _, counts, _ = _route_gpu(cfg, lg, bias)
+        r = oracle.route(oracle.router_scores(lg, bias), cfg.k, cfg.E)
+        np.testing.assert_array_equal(counts, r["counts"])
+        gpu.append(oracle.load_skew(counts, cfg.T, cfg.k))
+        ref.append(oracle.load_skew(r["counts"], cfg.T, cfg.k))
+    assert oracle.p95_nearest_rank(gpu) == oracle.p95_nearest_rank(ref)
+    assert oracle.p95_nearest_rank(ref) > 2.0   # the bias makes the load uneven
+
+
 @pytest.mark.parametrize("E,k", [(300, 8), (500, 9), (1024, 64)])
 def test_route_many_tokens_wide(E, k):
     """More than 2048 tokens (over 128 ranking blocks, so every scan thread walks
